@@ -1,0 +1,143 @@
+/*
+ * canopy.h: C ABI of libcanopy, tree-structured speculative verification of one Gated
+ * DeltaNet (gated delta-rule linear attention) layer on AMD Instinct MI355X (gfx950).
+ *
+ * The operation (the canopy project page, projects.dotslasha.me/p/canopy.md, "Science
+ * background"): a draft tree of T tokens, numbered so that parents precede children, is
+ * verified through one layer whose per-head state S is d_k x d_v = 128 x 128. Running the gated
+ * delta rule (S~ = alpha S, u = beta (v - S~^T k), S = S~ + k u^T, o = S^T q) along every
+ * node's root path from the committed state S0 gives every node's output o_i and pseudo-value
+ * u_i. The library computes them without walking the tree: with l_i the log cumulative decay
+ * over path(i) and Gamma_ij = exp(l_i - l_j), it builds the ancestor-masked, decay-weighted
+ * matrices G (beta_i Gamma_ij k_i.k_j over strict ancestors) and C (Gamma_ij q_i.k_j over
+ * path(i)), solves the unit lower-triangular system (I + G) U = R with
+ * R_i = beta_i (v_i - exp(l_i) S0^T k_i), and reads out O = diag(exp l) Q S0 + C U
+ * ("The tree closed form"). Commit rebuilds only the accepted path's state,
+ * S_a = exp(l_a) S0 + sum_{j in path(a)} Gamma_aj k_j u_j^T ("What the commit kernel stores").
+ *
+ * Conventions for every call:
+ *  - All array pointers are HIP device memory, C-contiguous, owned and allocated by the
+ *    caller. The library keeps no pointer after a call returns and allocates nothing.
+ *  - Calls only enqueue work on `stream` (0 = the null stream) and return; they do not
+ *    synchronise. Inputs are read-only; outputs are fully overwritten.
+ *  - d_k = d_v = 128. 1 <= T <= 256. B >= 1, H >= 1. q, k and v all have H heads.
+ *  - Node order is the caller's: node i's outputs sit at index i. parent[b,0] must be -1 and
+ *    -1 <= parent[b,i] < i; further roots (parent -1) start from S0 too.
+ *  - The scale on q is 1 (callers that want 1/sqrt(d_k) pre-scale q).
+ *  - alpha must lie in (0, 1]; beta is any finite value (0 allowed).
+ *  - q, k, v, S0, U, S_new, O (serial baseline) and snapshots must be 16-byte aligned.
+ *  - Errors found on the host (null required pointer, misaligned array, bad size, dtype, solver
+ *    or waves) return a status and launch nothing. A failed launch returns CANOPY_ERR_HIP. A malformed tree or
+ *    path is found on the device without blocking: it is reported in tree_status/path_status
+ *    and that sequence's outputs are NaN.
+ */
+#ifndef CANOPY_H
+#define CANOPY_H
+
+#include <stddef.h>
+#include <stdint.h>
+#include <hip/hip_runtime_api.h>
+
+#ifdef __cplusplus
+extern "C" {
+#endif
+
+typedef enum {
+    CANOPY_OK = 0,
+    CANOPY_ERR_ARG = 1,         /* null required pointer or a size out of range */
+    CANOPY_ERR_UNSUPPORTED = 2, /* dtype, solver or waves value not supported */
+    CANOPY_ERR_HIP = 4          /* the HIP runtime reported a launch error */
+} canopy_status;
+
+typedef enum { CANOPY_FP32 = 0, CANOPY_BF16 = 1 } canopy_dtype;
+
+/* How the unit lower-triangular system (I + G) U = R is solved ("Design decisions / Two solve
+ * strategies"). Both work on 64-node blocks, with the couplings to earlier blocks applied as
+ * matrix-core products: FWDSUB solves each diagonal block by forward substitution in LDS
+ * (rows of equal in-block depth together); NEUMANN sums the finite series
+ * sum_{m=0..d} (-G_bb)^m of the diagonal block on the matrix cores, d being the block's depth
+ * (for T <= 64 this is the whole tree's Neumann series with one term per tree level). */
+typedef enum { CANOPY_SOLVE_AUTO = 0, CANOPY_SOLVE_FWDSUB = 1, CANOPY_SOLVE_NEUMANN = 2 } canopy_solver;
+
+/* Library version, major * 10000 + minor * 100 + patch. */
+int canopy_version(void);
+
+/* Text for a status code (static storage). */
+const char *canopy_status_string(canopy_status s);
+
+/*
+ * Tree preprocessing on the GPU ("The tree closed form"; "Design decisions / Tree order and
+ * tiling" for the T x T bitmask).
+ *   parent      [B,T] int32, in.
+ *   alpha       [B,T,H] fp32, in.
+ *   anc_mask    [B,T,ceil(T/32)] uint32, out, may be NULL: bit (j % 32) of word j / 32 of row
+ *               i is set iff j is in path(i) (strict ancestors and i itself).
+ *   depth       [B,T] int32, out, may be NULL: |A(i)|, the root 0.
+ *   ell         [B,T,H] fp32, out, may be NULL: l_i = log alpha_i + l_parent(i), a root's
+ *               parent counting 0, summed in fp64 and rounded once.
+ *   tree_status [B] int32, out, may be NULL: 0, or 1 + the first node i whose parent is not
+ *               in -1..i-1 (then mask and depth rows are 0 and ell is NaN).
+ */
+canopy_status canopy_tree_prep(const int32_t *parent, const float *alpha, int B, int H, int T,
+                               uint32_t *anc_mask, int32_t *depth, float *ell,
+                               int32_t *tree_status, hipStream_t stream);
+
+/*
+ * Verify a draft tree through one GDN layer: every node's output and pseudo-value in one pass
+ * (prep, S0 projections, masked Gram matrices, the triangular solve and the read-out fused).
+ *   q, k, v     [B,T,H,128], in_dtype (fp32, or bf16 as 16-bit patterns), in.
+ *   alpha, beta [B,T,H] fp32, in.
+ *   S0          [B,H,128(k),128(v)] fp32, in: the committed state per (sequence, head).
+ *   parent      [B,T] int32, in.
+ *   O, U        [B,T,H,128] fp32, out: outputs o_i and pseudo-values u_i.
+ *   ell         [B,T,H] fp32, out: as in canopy_tree_prep.
+ *   anc_mask, depth, tree_status: optional outputs (NULL to skip), as in canopy_tree_prep.
+ *   solver      FWDSUB, NEUMANN, or AUTO (FWDSUB).
+ *   waves       waves per workgroup, each owning 16 value columns (1, 2, 4 or 8), or 0 to let
+ *               the library choose from B, H and T.
+ */
+canopy_status canopy_tree_verify(const void *q, const void *k, const void *v,
+                                 const float *alpha, const float *beta, const float *S0,
+                                 const int32_t *parent, int B, int H, int T,
+                                 canopy_dtype in_dtype, float *O, float *U, float *ell,
+                                 uint32_t *anc_mask, int32_t *depth, int32_t *tree_status,
+                                 canopy_solver solver, int waves, hipStream_t stream);
+
+/*
+ * Commit the accepted path: S_new = exp(l_a) S0 + sum_{j in path} exp(l_a - l_j) k_j u_j^T
+ * with a the path's last node ("What the commit kernel stores"; "M5"). The decay ratios are
+ * suffix sums of log alpha along the path (fp64), so no cancellation of large l enters them.
+ *   S0          [B,H,128,128] fp32, in.
+ *   k           [B,T,H,128], in_dtype, in: the keys given to canopy_tree_verify.
+ *   U           [B,T,H,128] fp32, in: the pseudo-values canopy_tree_verify wrote.
+ *   alpha       [B,T,H] fp32, in.
+ *   parent      [B,T] int32, in: only the path's own links are checked.
+ *   path        [B,T] int32, in: node ids root first; entries past path_len are ignored.
+ *   path_len    [B] int32, in: m in 0..T (0 commits nothing: S_new = S0).
+ *   S_new       [B,H,128,128] fp32, out; may be the same memory as S0 (in place).
+ *   path_status [B] int32, out, may be NULL: 0 valid, -1 path_len out of range, else 1 + the
+ *               first position t whose node is out of range or is not a child of path[t-1]
+ *               (for t = 0: not a root). S_new of such a sequence is NaN.
+ */
+canopy_status canopy_commit(const float *S0, const void *k, canopy_dtype in_dtype,
+                            const float *U, const float *alpha, const int32_t *parent,
+                            const int32_t *path, const int32_t *path_len, int B, int H, int T,
+                            float *S_new, int32_t *path_status, hipStream_t stream);
+
+/*
+ * Serial fork baseline ("Design decisions / Serial baseline"): walk the nodes in order; each
+ * node starts from its parent's per-node state snapshot (S0 for a root), takes one step of the
+ * gated delta rule and writes its own snapshot, output and pseudo-value. Same inputs and
+ * outputs as canopy_tree_verify plus
+ *   snapshots   [B,T,H,128,128] fp32, out: every node's state.
+ */
+canopy_status canopy_serial_verify(const void *q, const void *k, const void *v,
+                                   const float *alpha, const float *beta, const float *S0,
+                                   const int32_t *parent, int B, int H, int T,
+                                   canopy_dtype in_dtype, float *O, float *U, float *snapshots,
+                                   int32_t *tree_status, hipStream_t stream);
+
+#ifdef __cplusplus
+}
+#endif
+#endif /* CANOPY_H */

@@ -1,0 +1,62 @@
+"""CPU checks of the boundary: the built library loads and exports every entry point that
+include/canopy.h declares (no compute is called without a GPU)."""
+from __future__ import annotations
+
+import ctypes
+import os
+import re
+
+ROOT = os.path.dirname(os.path.dirname(os.path.abspath(__file__)))
+HEADER = os.path.join(ROOT, "include", "canopy.h")
+LIB = os.path.join(ROOT, "tree_speculative_verification_amd", "libcanopy.so")
+
+
+def declared_functions():
+    text = open(HEADER).read()
+    text = re.sub(r"/\*.*?\*/", "", text, flags=re.S)
+    return sorted(set(re.findall(r"\b(canopy_[a-z_]+)\s*\(", text)))
+
+
+def test_header_declares_the_calls():
+    names = declared_functions()
+    for n in ("canopy_tree_verify", "canopy_commit", "canopy_serial_verify", "canopy_tree_prep",
+              "canopy_status_string", "canopy_version"):
+        assert n in names
+
+
+def test_library_exports_every_declared_symbol():
+    assert os.path.exists(LIB), "libcanopy.so is not built (run __graft_entry__.build())"
+    lib = ctypes.CDLL(LIB)
+    for n in declared_functions():
+        assert hasattr(lib, n), n
+    lib.canopy_version.restype = ctypes.c_int
+    assert lib.canopy_version() >= 100
+    lib.canopy_status_string.restype = ctypes.c_char_p
+    lib.canopy_status_string.argtypes = [ctypes.c_int]
+    assert lib.canopy_status_string(0) == b"ok"
+
+
+def test_host_checks_need_no_gpu():
+    """Argument errors are found on the host before any HIP call, so they work without a GPU."""
+    lib = ctypes.CDLL(LIB)
+    f = lib.canopy_tree_verify
+    f.restype = ctypes.c_int
+    nul = ctypes.c_void_p(0)
+    args = [nul] * 7 + [ctypes.c_int(1), ctypes.c_int(1), ctypes.c_int(4), ctypes.c_int(0)] + \
+        [nul] * 6 + [ctypes.c_int(0), ctypes.c_int(0), nul]
+    assert f(*args) == 1
+    g = lib.canopy_commit
+    g.restype = ctypes.c_int
+    assert g(*([nul, nul, ctypes.c_int(0), nul, nul, nul, nul, nul, ctypes.c_int(1),
+                ctypes.c_int(1), ctypes.c_int(4), nul, nul, nul])) == 1
+
+
+def test_product_path_does_not_touch_the_oracle():
+    """The package and its sources never name the oracle module."""
+    pkg = os.path.join(ROOT, "tree_speculative_verification_amd")
+    for dirpath, _, files in os.walk(pkg):
+        for f in files:
+            if f.endswith((".py", ".hip", ".hpp", ".h", ".cpp")):
+                src = open(os.path.join(dirpath, f)).read()
+                assert "import oracle" not in src and "from oracle" not in src, f
+                assert "liboracle" not in src, f

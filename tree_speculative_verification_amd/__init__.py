@@ -1,0 +1,196 @@
+"""Python binding of libcanopy: tree-structured verification of a Gated DeltaNet layer on
+MI355X. Argument marshalling only: every step runs in the HIP kernels behind the C ABI of
+``include/canopy.h``. PyTorch supplies device memory and the current stream.
+
+Functions take and return torch tensors on the GPU:
+  tree_prep(parent, alpha)                              -> (anc_mask, depth, ell, status)
+  tree_verify(q, k, v, alpha, beta, S0, parent, ...)    -> (O, U, ell) [+ mask, depth, status]
+  commit(S0, k, U, alpha, parent, path, path_len, ...)  -> (S_new, path_status)
+  serial_verify(q, k, v, alpha, beta, S0, parent)       -> (O, U, snapshots, status)
+q, k, v are torch.bfloat16 or torch.float32 [B,T,H,128]; alpha, beta fp32 [B,T,H];
+S0 fp32 [B,H,128,128]; parent int32 [B,T]; path int32 [B,T]; path_len int32 [B].
+
+There is no fallback: if the library is missing or fails to load, every call raises.
+"""
+from __future__ import annotations
+
+import ctypes
+import os
+
+import torch  # loaded first so that libcanopy binds to the HIP runtime torch uses
+
+__all__ = ["load", "lib_path", "tree_prep", "tree_verify", "commit", "serial_verify",
+           "CanopyError", "SOLVERS"]
+
+_HERE = os.path.dirname(os.path.abspath(__file__))
+_LIB_PATH = os.path.join(_HERE, "libcanopy.so")
+_lib = None
+
+SOLVERS = {"auto": 0, "fwdsub": 1, "neumann": 2}
+_FP32, _BF16 = 0, 1
+
+
+class CanopyError(RuntimeError):
+    pass
+
+
+def lib_path() -> str:
+    return _LIB_PATH
+
+
+def load():
+    """Load libcanopy.so (built in-tree by ``build.build()``); raise if it is absent."""
+    global _lib
+    if _lib is not None:
+        return _lib
+    if not os.path.exists(_LIB_PATH):
+        raise CanopyError(f"{_LIB_PATH} is missing: build it with "
+                          "`python -m tree_speculative_verification_amd.build`")
+    lib = ctypes.CDLL(_LIB_PATH)
+    P, i, u64 = ctypes.c_void_p, ctypes.c_int, ctypes.c_void_p
+    lib.canopy_version.restype = i
+    lib.canopy_status_string.argtypes = [i]
+    lib.canopy_status_string.restype = ctypes.c_char_p
+    lib.canopy_tree_prep.argtypes = [P, P, i, i, i, P, P, P, P, u64]
+    lib.canopy_tree_prep.restype = i
+    lib.canopy_tree_verify.argtypes = [P, P, P, P, P, P, P, i, i, i, i, P, P, P, P, P, P, i, i, u64]
+    lib.canopy_tree_verify.restype = i
+    lib.canopy_commit.argtypes = [P, P, i, P, P, P, P, P, i, i, i, P, P, u64]
+    lib.canopy_commit.restype = i
+    lib.canopy_serial_verify.argtypes = [P, P, P, P, P, P, P, i, i, i, i, P, P, P, P, u64]
+    lib.canopy_serial_verify.restype = i
+    _lib = lib
+    return lib
+
+
+def _check(st: int):
+    if st != 0:
+        msg = load().canopy_status_string(st).decode()
+        raise CanopyError(f"libcanopy status {st}: {msg}")
+
+
+def _ptr(t):
+    return None if t is None else ctypes.c_void_p(t.data_ptr())
+
+
+def _stream():
+    return ctypes.c_void_p(torch.cuda.current_stream().cuda_stream)
+
+
+def _req(t, name, dtype=None, shape=None):
+    if not isinstance(t, torch.Tensor):
+        raise TypeError(f"{name} must be a torch.Tensor")
+    if not t.is_cuda:
+        raise ValueError(f"{name} must be on the GPU")
+    if not t.is_contiguous():
+        raise ValueError(f"{name} must be contiguous")
+    if dtype is not None and t.dtype != dtype:
+        raise TypeError(f"{name} must be {dtype}, got {t.dtype}")
+    if shape is not None and tuple(t.shape) != tuple(shape):
+        raise ValueError(f"{name} has shape {tuple(t.shape)}, expected {tuple(shape)}")
+    return t
+
+
+def _in_dtype(q):
+    if q.dtype == torch.bfloat16:
+        return _BF16
+    if q.dtype == torch.float32:
+        return _FP32
+    raise TypeError(f"q, k, v must be bfloat16 or float32, got {q.dtype}")
+
+
+def tree_prep(parent, alpha):
+    """Ancestor bitmask [B,T,ceil(T/32)] (as int32 bit patterns), depth [B,T], ell [B,T,H] and
+    tree status [B], computed on the GPU."""
+    B, T = parent.shape
+    H = alpha.shape[2]
+    _req(parent, "parent", torch.int32, (B, T))
+    _req(alpha, "alpha", torch.float32, (B, T, H))
+    W = (T + 31) // 32
+    dev = parent.device
+    mask = torch.empty((B, T, W), dtype=torch.int32, device=dev)
+    depth = torch.empty((B, T), dtype=torch.int32, device=dev)
+    ell = torch.empty((B, T, H), dtype=torch.float32, device=dev)
+    status = torch.empty((B,), dtype=torch.int32, device=dev)
+    _check(load().canopy_tree_prep(_ptr(parent), _ptr(alpha), B, H, T, _ptr(mask), _ptr(depth),
+                                   _ptr(ell), _ptr(status), _stream()))
+    return mask, depth, ell, status
+
+
+def tree_verify(q, k, v, alpha, beta, S0, parent, solver="auto", waves=0, structure=False,
+                out=None):
+    """Every node's output O and pseudo-value U ([B,T,H,128] fp32) and ell ([B,T,H] fp32).
+    With ``structure=True`` also returns the ancestor bitmask, depth and tree status.
+    ``out`` may pass preallocated (O, U, ell)."""
+    B, T, H, d = q.shape
+    dt = _in_dtype(q)
+    for name, t in (("q", q), ("k", k), ("v", v)):
+        _req(t, name, q.dtype, (B, T, H, d))
+    _req(alpha, "alpha", torch.float32, (B, T, H))
+    _req(beta, "beta", torch.float32, (B, T, H))
+    _req(S0, "S0", torch.float32, (B, H, d, d))
+    _req(parent, "parent", torch.int32, (B, T))
+    dev = q.device
+    if out is None:
+        O = torch.empty((B, T, H, d), dtype=torch.float32, device=dev)
+        U = torch.empty((B, T, H, d), dtype=torch.float32, device=dev)
+        ell = torch.empty((B, T, H), dtype=torch.float32, device=dev)
+    else:
+        O, U, ell = out
+    mask = depth = status = None
+    if structure:
+        mask = torch.empty((B, T, (T + 31) // 32), dtype=torch.int32, device=dev)
+        depth = torch.empty((B, T), dtype=torch.int32, device=dev)
+        status = torch.empty((B,), dtype=torch.int32, device=dev)
+    _check(load().canopy_tree_verify(_ptr(q), _ptr(k), _ptr(v), _ptr(alpha), _ptr(beta),
+                                     _ptr(S0), _ptr(parent), B, H, T, dt, _ptr(O), _ptr(U),
+                                     _ptr(ell), _ptr(mask), _ptr(depth), _ptr(status),
+                                     SOLVERS[solver], int(waves), _stream()))
+    if structure:
+        return O, U, ell, mask, depth, status
+    return O, U, ell
+
+
+def commit(S0, k, U, alpha, parent, path, path_len, out=None):
+    """State after the accepted path: S_new [B,H,128,128] fp32 (``out`` may be S0 itself for
+    an in-place commit) and the path status [B]."""
+    B, T, H, d = k.shape
+    dt = _in_dtype(k)
+    _req(S0, "S0", torch.float32, (B, H, d, d))
+    _req(k, "k", None, (B, T, H, d))
+    _req(U, "U", torch.float32, (B, T, H, d))
+    _req(alpha, "alpha", torch.float32, (B, T, H))
+    _req(parent, "parent", torch.int32, (B, T))
+    _req(path, "path", torch.int32, (B, T))
+    _req(path_len, "path_len", torch.int32, (B,))
+    S_new = torch.empty_like(S0) if out is None else _req(out, "out", torch.float32, (B, H, d, d))
+    status = torch.empty((B,), dtype=torch.int32, device=k.device)
+    _check(load().canopy_commit(_ptr(S0), _ptr(k), dt, _ptr(U), _ptr(alpha), _ptr(parent),
+                                _ptr(path), _ptr(path_len), B, H, T, _ptr(S_new), _ptr(status),
+                                _stream()))
+    return S_new, status
+
+
+def serial_verify(q, k, v, alpha, beta, S0, parent, snapshots=None):
+    """The serial fork baseline: O, U [B,T,H,128], every node's state snapshot
+    [B,T,H,128,128] and the tree status [B]."""
+    B, T, H, d = q.shape
+    dt = _in_dtype(q)
+    for name, t in (("q", q), ("k", k), ("v", v)):
+        _req(t, name, q.dtype, (B, T, H, d))
+    _req(alpha, "alpha", torch.float32, (B, T, H))
+    _req(beta, "beta", torch.float32, (B, T, H))
+    _req(S0, "S0", torch.float32, (B, H, d, d))
+    _req(parent, "parent", torch.int32, (B, T))
+    dev = q.device
+    O = torch.empty((B, T, H, d), dtype=torch.float32, device=dev)
+    U = torch.empty((B, T, H, d), dtype=torch.float32, device=dev)
+    if snapshots is None:
+        snapshots = torch.empty((B, T, H, d, d), dtype=torch.float32, device=dev)
+    else:
+        _req(snapshots, "snapshots", torch.float32, (B, T, H, d, d))
+    status = torch.empty((B,), dtype=torch.int32, device=dev)
+    _check(load().canopy_serial_verify(_ptr(q), _ptr(k), _ptr(v), _ptr(alpha), _ptr(beta),
+                                       _ptr(S0), _ptr(parent), B, H, T, dt, _ptr(O), _ptr(U),
+                                       _ptr(snapshots), _ptr(status), _stream()))
+    return O, U, snapshots, status

@@ -1,0 +1,107 @@
+// The C ABI of libcanopy (declared in include/canopy.h): host-side argument checks, the launch
+// configuration, and nothing else. Every call only enqueues kernels on the caller's stream.
+#include "canopy_device.hpp"
+#include "canopy_kernels.hpp"
+
+using namespace canopy;
+
+namespace {
+
+bool sizes_ok(int B, int H, int T) { return B >= 1 && H >= 1 && T >= 1 && T <= 256; }
+
+canopy_status from_hip(hipError_t e) { return e == hipSuccess ? CANOPY_OK : CANOPY_ERR_HIP; }
+
+// Kernels move 16-byte vectors of these arrays; a misaligned view is rejected on the host.
+bool aligned16(const void *p) { return (reinterpret_cast<uintptr_t>(p) & 15u) == 0; }
+
+// Waves per workgroup (16 value columns each) for the verify kernel: the widest tile that still
+// gives about two workgroups per compute unit, so small batches spread the S0 reads over the
+// chip and large ones do not repeat the shared Gram work across value tiles.
+int pick_waves(int B, int H, int T) {
+    (void)T;
+    const long bh = static_cast<long>(B) * H;
+    const int cand[4] = {8, 4, 2, 1};
+    for (int c : cand)
+        if (bh * (D / (16 * c)) >= 512) return c;
+    return 1;
+}
+
+}  // namespace
+
+extern "C" {
+
+int canopy_version(void) { return 100; }
+
+const char *canopy_status_string(canopy_status s) {
+    switch (s) {
+        case CANOPY_OK: return "ok";
+        case CANOPY_ERR_ARG: return "invalid argument (null pointer or size out of range)";
+        case CANOPY_ERR_UNSUPPORTED: return "unsupported dtype, solver or waves value";
+        case CANOPY_ERR_HIP: return "HIP launch error";
+        default: return "unknown status";
+    }
+}
+
+canopy_status canopy_tree_prep(const int32_t *parent, const float *alpha, int B, int H, int T,
+                               uint32_t *anc_mask, int32_t *depth, float *ell,
+                               int32_t *tree_status, hipStream_t stream) {
+    if (!parent || !alpha || !sizes_ok(B, H, T)) return CANOPY_ERR_ARG;
+    PrepArgs a{parent, alpha, B, H, T, anc_mask, depth, ell, tree_status};
+    return from_hip(launch_prep(a, stream));
+}
+
+canopy_status canopy_tree_verify(const void *q, const void *k, const void *v,
+                                 const float *alpha, const float *beta, const float *S0,
+                                 const int32_t *parent, int B, int H, int T,
+                                 canopy_dtype in_dtype, float *O, float *U, float *ell,
+                                 uint32_t *anc_mask, int32_t *depth, int32_t *tree_status,
+                                 canopy_solver solver, int waves, hipStream_t stream) {
+    if (!q || !k || !v || !alpha || !beta || !S0 || !parent || !O || !U || !ell)
+        return CANOPY_ERR_ARG;
+    if (!sizes_ok(B, H, T)) return CANOPY_ERR_ARG;
+    if (!aligned16(q) || !aligned16(k) || !aligned16(v) || !aligned16(S0)) return CANOPY_ERR_ARG;
+    if (in_dtype != CANOPY_FP32 && in_dtype != CANOPY_BF16) return CANOPY_ERR_UNSUPPORTED;
+    if (solver != CANOPY_SOLVE_AUTO && solver != CANOPY_SOLVE_FWDSUB && solver != CANOPY_SOLVE_NEUMANN)
+        return CANOPY_ERR_UNSUPPORTED;
+    if (waves != 0 && waves != 1 && waves != 2 && waves != 4 && waves != 8) return CANOPY_ERR_UNSUPPORTED;
+    VerifyArgs a{};
+    a.q = q; a.k = k; a.v = v;
+    a.alpha = alpha; a.beta = beta; a.S0 = S0; a.parent = parent;
+    a.B = B; a.H = H; a.T = T;
+    a.bf16 = in_dtype == CANOPY_BF16;
+    a.solver = solver == CANOPY_SOLVE_NEUMANN ? CANOPY_SOLVE_NEUMANN : CANOPY_SOLVE_FWDSUB;
+    a.O = O; a.U = U; a.ell = ell;
+    a.anc_mask = anc_mask; a.depth = depth; a.tree_status = tree_status;
+    return from_hip(launch_verify(a, waves ? waves : pick_waves(B, H, T), stream));
+}
+
+canopy_status canopy_commit(const float *S0, const void *k, canopy_dtype in_dtype,
+                            const float *U, const float *alpha, const int32_t *parent,
+                            const int32_t *path, const int32_t *path_len, int B, int H, int T,
+                            float *S_new, int32_t *path_status, hipStream_t stream) {
+    if (!S0 || !k || !U || !alpha || !parent || !path || !path_len || !S_new) return CANOPY_ERR_ARG;
+    if (!sizes_ok(B, H, T)) return CANOPY_ERR_ARG;
+    if (!aligned16(S0) || !aligned16(U) || !aligned16(S_new)) return CANOPY_ERR_ARG;
+    if (in_dtype != CANOPY_FP32 && in_dtype != CANOPY_BF16) return CANOPY_ERR_UNSUPPORTED;
+    CommitArgs a{S0, k, in_dtype == CANOPY_BF16, U, alpha, parent, path, path_len,
+                 B, H, T, S_new, path_status};
+    return from_hip(launch_commit(a, stream));
+}
+
+canopy_status canopy_serial_verify(const void *q, const void *k, const void *v,
+                                   const float *alpha, const float *beta, const float *S0,
+                                   const int32_t *parent, int B, int H, int T,
+                                   canopy_dtype in_dtype, float *O, float *U, float *snapshots,
+                                   int32_t *tree_status, hipStream_t stream) {
+    if (!q || !k || !v || !alpha || !beta || !S0 || !parent || !O || !U || !snapshots)
+        return CANOPY_ERR_ARG;
+    if (!sizes_ok(B, H, T)) return CANOPY_ERR_ARG;
+    if (!aligned16(S0) || !aligned16(v) || !aligned16(O) || !aligned16(U) || !aligned16(snapshots))
+        return CANOPY_ERR_ARG;
+    if (in_dtype != CANOPY_FP32 && in_dtype != CANOPY_BF16) return CANOPY_ERR_UNSUPPORTED;
+    SerialArgs a{q, k, v, alpha, beta, S0, parent, B, H, T, in_dtype == CANOPY_BF16,
+                 O, U, snapshots, tree_status};
+    return from_hip(launch_serial(a, stream));
+}
+
+}  // extern "C"

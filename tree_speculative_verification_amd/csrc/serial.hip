@@ -1,0 +1,124 @@
+// Serial fork baseline ("Design decisions / Serial baseline" on the canopy project page): the
+// nodes are visited in order; each starts from its parent's per-node state snapshot (S0 for a
+// root), applies one step of the gated delta rule
+//   S~ = alpha S_p,  u = beta (v - S~^T k),  S = S~ + k u^T,  o = S^T q,
+// and writes its own snapshot, o and u. One wave per (sequence, head, 16 value columns); the
+// wave keeps its 128 x 16 state slice in registers (lane: 8 rows x 4 columns) and reloads it
+// from a snapshot only when a node's parent is not the node just processed.
+#include "canopy_device.hpp"
+#include "canopy_kernels.hpp"
+#include <limits.h>
+
+namespace canopy {
+
+template <bool BF>
+__global__ __launch_bounds__(64) void serial_kernel(SerialArgs a) {
+    constexpr int TILES = D / 16;
+    const int g = xcd_remap(blockIdx.x, gridDim.x);
+    const int tile = g % TILES;
+    const int bh = g / TILES;
+    const int H = a.H, T = a.T;
+    const int b = bh / H, h = bh % H;
+    const int lane = threadIdx.x;
+    const int cq = lane & 3, rg = lane >> 2;  // columns 4*cq.., rows rg + 16*m
+    const int col = tile * 16 + 4 * cq;
+    const int32_t *par = a.parent + static_cast<size_t>(b) * T;
+    const size_t rs = static_cast<size_t>(H) * D;
+    const size_t base = (static_cast<size_t>(b) * T * H + h) * D;
+    const size_t sbase = static_cast<size_t>(b) * T * H + h;
+    const size_t SS = static_cast<size_t>(D) * D;
+
+    int bad = INT_MAX;
+    for (int i = lane; i < T; i += 64) {
+        const int p = par[i];
+        if (p < -1 || p >= i) bad = min(bad, i + 1);
+    }
+#pragma unroll
+    for (int o = 32; o > 0; o >>= 1) bad = min(bad, __shfl_xor(bad, o, 64));
+    if (a.tree_status && tile == 0 && h == 0 && lane == 0) a.tree_status[b] = bad == INT_MAX ? 0 : bad;
+    if (bad != INT_MAX) {
+        const float qnan = __builtin_nanf("");
+        for (int i = rg; i < T; i += 16) {
+            reinterpret_cast<float4 *>(a.O + base + i * rs + col)[0] = make_float4(qnan, qnan, qnan, qnan);
+            reinterpret_cast<float4 *>(a.U + base + i * rs + col)[0] = make_float4(qnan, qnan, qnan, qnan);
+        }
+        return;
+    }
+
+    float4 S[8];
+    int cur = -2;  // node whose state the registers hold
+    for (int i = 0; i < T; ++i) {
+        const int p = par[i];
+        if (p != cur) {
+            const float *src = (p < 0) ? a.S0 + static_cast<size_t>(bh) * SS
+                                       : a.snap + ((static_cast<size_t>(b) * T + p) * H + h) * SS;
+            // The snapshot was written by this wave; order those stores before these loads.
+            __builtin_amdgcn_fence(__ATOMIC_SEQ_CST, "workgroup");
+#pragma unroll
+            for (int m = 0; m < 8; ++m) S[m] = reinterpret_cast<const float4 *>(src + (rg + 16 * m) * D + col)[0];
+        }
+        const size_t node = base + static_cast<size_t>(i) * rs;
+        const float al = a.alpha[sbase + static_cast<size_t>(i) * H];
+        const float be = a.beta[sbase + static_cast<size_t>(i) * H];
+        float kv[8], qv[8];
+#pragma unroll
+        for (int m = 0; m < 8; ++m) {
+            const size_t el = node + rg + 16 * m;
+            kv[m] = BF ? bf16_to_f32(static_cast<const uint16_t *>(a.k)[el]) : static_cast<const float *>(a.k)[el];
+            qv[m] = BF ? bf16_to_f32(static_cast<const uint16_t *>(a.q)[el]) : static_cast<const float *>(a.q)[el];
+        }
+        float4 part = make_float4(0.f, 0.f, 0.f, 0.f);
+#pragma unroll
+        for (int m = 0; m < 8; ++m) {
+            S[m].x *= al; S[m].y *= al; S[m].z *= al; S[m].w *= al;
+            part.x += S[m].x * kv[m]; part.y += S[m].y * kv[m];
+            part.z += S[m].z * kv[m]; part.w += S[m].w * kv[m];
+        }
+#pragma unroll
+        for (int o = 4; o < 64; o <<= 1) {
+            part.x += __shfl_xor(part.x, o, 64); part.y += __shfl_xor(part.y, o, 64);
+            part.z += __shfl_xor(part.z, o, 64); part.w += __shfl_xor(part.w, o, 64);
+        }
+        float4 vv;
+        if (BF) {
+            const uint16_t *vp = static_cast<const uint16_t *>(a.v) + node + col;
+            vv = make_float4(bf16_to_f32(vp[0]), bf16_to_f32(vp[1]), bf16_to_f32(vp[2]), bf16_to_f32(vp[3]));
+        } else {
+            vv = reinterpret_cast<const float4 *>(static_cast<const float *>(a.v) + node + col)[0];
+        }
+        const float4 u = make_float4(be * (vv.x - part.x), be * (vv.y - part.y),
+                                     be * (vv.z - part.z), be * (vv.w - part.w));
+        float4 o = make_float4(0.f, 0.f, 0.f, 0.f);
+#pragma unroll
+        for (int m = 0; m < 8; ++m) {
+            S[m].x += kv[m] * u.x; S[m].y += kv[m] * u.y;
+            S[m].z += kv[m] * u.z; S[m].w += kv[m] * u.w;
+            o.x += S[m].x * qv[m]; o.y += S[m].y * qv[m];
+            o.z += S[m].z * qv[m]; o.w += S[m].w * qv[m];
+        }
+#pragma unroll
+        for (int s = 4; s < 64; s <<= 1) {
+            o.x += __shfl_xor(o.x, s, 64); o.y += __shfl_xor(o.y, s, 64);
+            o.z += __shfl_xor(o.z, s, 64); o.w += __shfl_xor(o.w, s, 64);
+        }
+        float *dst = a.snap + ((static_cast<size_t>(b) * T + i) * H + h) * SS;
+#pragma unroll
+        for (int m = 0; m < 8; ++m) reinterpret_cast<float4 *>(dst + (rg + 16 * m) * D + col)[0] = S[m];
+        if (rg == 0) {
+            reinterpret_cast<float4 *>(a.O + node + col)[0] = o;
+            reinterpret_cast<float4 *>(a.U + node + col)[0] = u;
+        }
+        cur = i;
+    }
+}
+
+hipError_t launch_serial(const SerialArgs &a, hipStream_t stream) {
+    const dim3 grid(static_cast<unsigned>(a.B * a.H * (D / 16))), block(64);
+    if (a.bf16)
+        hipLaunchKernelGGL(serial_kernel<true>, grid, block, 0, stream, a);
+    else
+        hipLaunchKernelGGL(serial_kernel<false>, grid, block, 0, stream, a);
+    return hipGetLastError();
+}
+
+}  // namespace canopy
