@@ -5,7 +5,10 @@ A step is one pass of the hot path over one layer's synthetic batch: canopy_tree
 preprocessing, S0 projections, masked Gram matrices, triangular solve, read-out) followed by
 canopy_commit of a random root-to-leaf path. The serial fork baseline is timed beside it.
 Inputs are resident in HBM before the timed region; the timed region holds exactly --steps
-steps between two stream synchronisations, timed with HIP events on the launch stream.
+steps between two stream synchronisations, timed with HIP events on the launch stream. The
+steps are captured once into a HIP graph and the timed region is one replay of it (the kernels
+are short enough at B=1 that launching them one by one from Python would time the host);
+--eager launches them one by one instead.
 
 Prints one JSON line. The default workload is the 9B-shaped layer: B=1, H=32, d=128, T=16
 top-k tree (root, 3 children, 4 children each), bf16 q/k/v, fp32 state.
@@ -79,8 +82,37 @@ def to_device(inp):
     return out
 
 
-def time_loop(fn, iters, warmup):
-    """Average µs per call of fn() over `iters` back-to-back calls on the current stream."""
+def graph_of(fn, n):
+    """A HIP graph holding n back-to-back calls of fn (captured on torch's capture stream, which
+    is the stream the library launches on)."""
+    import torch
+    fn()  # warm the caching allocator and the code objects outside the capture
+    torch.cuda.synchronize()
+    g = torch.cuda.CUDAGraph()
+    with torch.cuda.graph(g):
+        for _ in range(n):
+            fn()
+    torch.cuda.synchronize()
+    return g
+
+
+def time_graph(g, n):
+    """Average µs per call of a graph of n calls: one replay between two events on the stream
+    the replay runs on, synchronised on both sides."""
+    import torch
+    g.replay()  # warm replay
+    torch.cuda.synchronize()
+    e0 = torch.cuda.Event(enable_timing=True)
+    e1 = torch.cuda.Event(enable_timing=True)
+    e0.record()
+    g.replay()
+    e1.record()
+    torch.cuda.synchronize()
+    return e0.elapsed_time(e1) * 1000.0 / n
+
+
+def time_eager(fn, iters, warmup):
+    """Average µs per call of fn() over `iters` back-to-back eager calls."""
     import torch
     for _ in range(warmup):
         fn()
@@ -124,11 +156,13 @@ def main(argv=None):
     ap.add_argument("--steps", type=int, default=200)
     ap.add_argument("--warmup", type=int, default=25)
     ap.add_argument("--workload", default="topk16_b1", choices=sorted(WORKLOADS))
-    ap.add_argument("--solver", default="auto", choices=["auto", "fwdsub", "neumann"])
+    ap.add_argument("--solver", default="auto", choices=["auto", "fwdsub", "neumann", "level"])
     ap.add_argument("--waves", type=int, default=0)
     ap.add_argument("--no-cpu", action="store_true", help="skip the oracle CPU baseline")
     ap.add_argument("--no-serial", action="store_true", help="skip the serial fork baseline")
     ap.add_argument("--cpu-budget", type=float, default=10.0)
+    ap.add_argument("--eager", action="store_true",
+                    help="launch every kernel from Python instead of replaying a HIP graph")
     args = ap.parse_args(argv)
 
     if args.gpus != 1 or int(os.environ.get("WORLD_SIZE", "1")) != 1:
@@ -162,23 +196,28 @@ def main(argv=None):
         verify()
         commit()
 
-    # Timed region: exactly `steps` steps, synchronised on both sides.
     for _ in range(args.warmup):
         step()
     torch.cuda.synchronize()
-    e0 = torch.cuda.Event(enable_timing=True)
-    e1 = torch.cuda.Event(enable_timing=True)
-    e0.record()
-    for _ in range(args.steps):
-        step()
-    e1.record()
-    torch.cuda.synchronize()
-    ms_total = e0.elapsed_time(e1)
-    us_step = ms_total * 1000.0 / args.steps
-
-    # Per-kernel averages (same stream, back-to-back launches of one kernel).
-    us_verify = time_loop(verify, args.steps, 5)
-    us_commit = time_loop(commit, args.steps, 5)
+    ref_O, ref_U, ref_S = O.clone(), U.clone(), S_new.clone()
+    if args.eager:
+        us_step = time_eager(step, args.steps, 0)
+        us_verify = time_eager(verify, args.steps, 5)
+        us_commit = time_eager(commit, args.steps, 5)
+    else:
+        # Timed region: one replay of a graph holding exactly `steps` steps.
+        g_step = graph_of(step, args.steps)
+        us_step = time_graph(g_step, args.steps)
+        # The replayed kernels must reproduce the eager results bit for bit.
+        if not (torch.equal(O, ref_O) and torch.equal(U, ref_U) and torch.equal(S_new, ref_S)):
+            raise RuntimeError("graph replay differs from the eager run")
+        del g_step
+        g_v = graph_of(verify, args.steps)
+        us_verify = time_graph(g_v, args.steps)
+        del g_v
+        g_c = graph_of(commit, args.steps)
+        us_commit = time_graph(g_c, args.steps)
+        del g_c
     us_serial = None
     if not args.no_serial:
         snaps = torch.empty((B, T, H, 128, 128), device="cuda")
@@ -186,7 +225,13 @@ def main(argv=None):
         def serial():
             tsv.serial_verify(d["q"], d["k"], d["v"], d["alpha"], d["beta"], d["S0"], d["parent"],
                               snapshots=snaps)
-        us_serial = time_loop(serial, max(10, args.steps // 4), 3)
+        n_ser = max(10, args.steps // 4)
+        if args.eager:
+            us_serial = time_eager(serial, n_ser, 3)
+        else:
+            g_s = graph_of(serial, n_ser)
+            us_serial = time_graph(g_s, n_ser)
+            del g_s
         del snaps
 
     vbytes = verify_bytes(B, H, T, dt)
@@ -206,7 +251,8 @@ def main(argv=None):
         "data": "synthetic",
         "config": {"workload": wl["desc"], "B": B, "H": H, "T": T, "dk": 128, "dv": 128,
                    "tree": wl["tree"], "solver": args.solver, "waves": args.waves,
-                   "step": "verify + commit of a random root-to-leaf path"},
+                   "step": "verify + commit of a random root-to-leaf path",
+                   "launch": "eager" if args.eager else "hip graph of all timed steps"},
         "nodes_per_s": round(B * T / (us_step * 1e-6), 1),
         "verify_us": round(us_verify, 3),
         "verify_nodes_per_s": round(B * T / (us_verify * 1e-6), 1),

@@ -52,12 +52,23 @@ typedef enum {
 typedef enum { CANOPY_FP32 = 0, CANOPY_BF16 = 1 } canopy_dtype;
 
 /* How the unit lower-triangular system (I + G) U = R is solved ("Design decisions / Two solve
- * strategies"). Both work on 64-node blocks, with the couplings to earlier blocks applied as
- * matrix-core products: FWDSUB solves each diagonal block by forward substitution in LDS
- * (rows of equal in-block depth together); NEUMANN sums the finite series
- * sum_{m=0..d} (-G_bb)^m of the diagonal block on the matrix cores, d being the block's depth
- * (for T <= 64 this is the whole tree's Neumann series with one term per tree level). */
-typedef enum { CANOPY_SOLVE_AUTO = 0, CANOPY_SOLVE_FWDSUB = 1, CANOPY_SOLVE_NEUMANN = 2 } canopy_solver;
+ * strategies"; "The tree closed form" for the Neumann series and the level-synchronous solve).
+ * All work on 64-node blocks staged in LDS, the couplings to earlier blocks applied as
+ * matrix-core products; they differ in how a diagonal block is solved:
+ *   FWDSUB   forward substitution over four 16-node sub-blocks: every 16 x 16 diagonal
+ *            sub-block is inverted by substitution and applied on the matrix cores, the
+ *            couplings between sub-blocks too. Its cost does not depend on the tree's depth.
+ *   NEUMANN  the finite series sum_{m=0..d} (-G_bb)^m, d the block's in-block depth, one
+ *            matrix-core product per term (for T <= 64: the whole tree's Neumann series with
+ *            one term per tree level).
+ *   LEVEL    row-by-row substitution with the rows of equal in-block depth solved together.
+ *   AUTO     LEVEL for blocks of in-block depth <= 3, FWDSUB otherwise. */
+typedef enum {
+    CANOPY_SOLVE_AUTO = 0,
+    CANOPY_SOLVE_FWDSUB = 1,
+    CANOPY_SOLVE_NEUMANN = 2,
+    CANOPY_SOLVE_LEVEL = 3
+} canopy_solver;
 
 /* Library version, major * 10000 + minor * 100 + patch. */
 int canopy_version(void);
@@ -92,9 +103,10 @@ canopy_status canopy_tree_prep(const int32_t *parent, const float *alpha, int B,
  *   O, U        [B,T,H,128] fp32, out: outputs o_i and pseudo-values u_i.
  *   ell         [B,T,H] fp32, out: as in canopy_tree_prep.
  *   anc_mask, depth, tree_status: optional outputs (NULL to skip), as in canopy_tree_prep.
- *   solver      FWDSUB, NEUMANN, or AUTO (FWDSUB).
+ *   solver      AUTO, FWDSUB, NEUMANN or LEVEL (see canopy_solver).
  *   waves       waves per workgroup, each owning 16 value columns (1, 2, 4 or 8), or 0 to let
- *               the library choose from B, H and T.
+ *               the library choose from B, H and T. fp32 inputs use at most 2 (a wider value
+ *               is taken as 2).
  */
 canopy_status canopy_tree_verify(const void *q, const void *k, const void *v,
                                  const float *alpha, const float *beta, const float *S0,

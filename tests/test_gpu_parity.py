@@ -57,7 +57,7 @@ def test_config_binary7_fp32(canopy):
     inp["path_len"][:] = 3
     d = to_device(inp)
     ref = run_oracle(inp, accept=[3])
-    for solver in ("fwdsub", "neumann"):
+    for solver in ("fwdsub", "neumann", "level", "auto"):
         for waves in (1, 2, 4, 8):
             _say("binary7 fp32", solver, "waves", waves)
             O, U, ell, mask, depth, st = _verify(canopy, d, solver=solver, waves=waves)
@@ -75,7 +75,7 @@ def test_config_binary7_fp32(canopy):
     assert_close_state("S_new vs path recurrence", Sn.cpu().numpy(), S_or, TOL["fp32"])
 
 
-@pytest.mark.parametrize("solver", ["fwdsub", "neumann"])
+@pytest.mark.parametrize("solver", ["fwdsub", "neumann", "level", "auto"])
 def test_config_topk16_bf16(canopy, solver):
     """The 1+3+12 top-k tree at the 9B layer's shape: B=1 H=32 T=16 bf16, commit of a random
     root-to-leaf path."""
@@ -111,7 +111,7 @@ def test_tile_edges(canopy, T, dtype):
     inp = synth.make_inputs(2, 2, T, tree=kind, tree_kw=kw, dtype=dtype, seed=100 + T)
     d = to_device(inp)
     ref = run_oracle(inp)
-    for solver, waves in (("fwdsub", 1), ("neumann", 2), ("fwdsub", 4), ("neumann", 8)):
+    for solver, waves in (("fwdsub", 1), ("neumann", 2), ("level", 4), ("auto", 8), ("fwdsub", 8)):
         _say("edge", T, dtype, kind, solver, waves)
         O, U, ell, mask, depth, st = _verify(canopy, d, solver=solver, waves=waves)
         assert_close_heads("O", O, ref["O"], TOL[dtype])
@@ -130,7 +130,7 @@ def test_config_skewed64_batch_sweep(canopy, B):
     bsel = sorted(set([0, B - 1, B // 2]))
     hsel = [0, 7, 31]
     ref = run_oracle(slice_inputs(inp, bsel, hsel))
-    for solver in ("fwdsub", "neumann"):
+    for solver in ("fwdsub", "neumann", "level", "auto"):
         _say("skewed64 B", B, solver)
         O, U, ell, mask, depth, st = _verify(canopy, d, solver=solver)
         assert_close_heads("O", O[bsel][:, :, hsel], ref["O"], TOL["bf16"])
@@ -156,7 +156,12 @@ def test_config_random256_b16(canopy):
     bsel, hsel = [0, 5, 15], [0, 13, 31]
     sub = slice_inputs(inp, bsel, hsel)
     ref = run_oracle(sub)
-    _say("random256 B16 verify")
+    for solver in ("fwdsub", "neumann", "level"):
+        _say("random256 B16 verify", solver)
+        O, U, ell, mask, depth, st = _verify(canopy, d, solver=solver)
+        assert_close_heads("O", O[bsel][:, :, hsel], ref["O"], TOL["bf16"])
+        assert_close_heads("U", U[bsel][:, :, hsel], ref["U"], TOL["bf16"])
+    _say("random256 B16 verify auto")
     O, U, ell, mask, depth, st = _verify(canopy, d)
     assert_close_heads("O", O[bsel][:, :, hsel], ref["O"], TOL["bf16"])
     assert_close_heads("U", U[bsel][:, :, hsel], ref["U"], TOL["bf16"])

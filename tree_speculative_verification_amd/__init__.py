@@ -26,7 +26,7 @@ _HERE = os.path.dirname(os.path.abspath(__file__))
 _LIB_PATH = os.path.join(_HERE, "libcanopy.so")
 _lib = None
 
-SOLVERS = {"auto": 0, "fwdsub": 1, "neumann": 2}
+SOLVERS = {"auto": 0, "fwdsub": 1, "neumann": 2, "level": 3}
 _FP32, _BF16 = 0, 1
 
 

@@ -14,17 +14,12 @@ canopy_status from_hip(hipError_t e) { return e == hipSuccess ? CANOPY_OK : CANO
 // Kernels move 16-byte vectors of these arrays; a misaligned view is rejected on the host.
 bool aligned16(const void *p) { return (reinterpret_cast<uintptr_t>(p) & 15u) == 0; }
 
-// Waves per workgroup (16 value columns each) for the verify kernel: the widest tile that still
-// gives about two workgroups per compute unit, so small batches spread the S0 reads over the
-// chip and large ones do not repeat the shared Gram work across value tiles.
-int pick_waves(int B, int H, int T) {
-    (void)T;
-    const long bh = static_cast<long>(B) * H;
-    const int cand[4] = {8, 4, 2, 1};
-    for (int c : cand)
-        if (bh * (D / (16 * c)) >= 512) return c;
-    return 1;
-}
+// Waves per workgroup (16 value columns each) for the verify kernel. One workgroup per
+// (sequence, head) with all 128 columns (8 waves) measured fastest on MI355X at every size of
+// the benchmark (B = 1..16, T = 16..256): the per-workgroup chain of dependent phases sets the
+// time, and narrower tiles repeat the shared Gram work without shortening that chain.
+// fp32 inputs stage twice the bytes per block and use 2 waves.
+int pick_waves(canopy_dtype dt) { return dt == CANOPY_BF16 ? 8 : 2; }
 
 }  // namespace
 
@@ -61,7 +56,8 @@ canopy_status canopy_tree_verify(const void *q, const void *k, const void *v,
     if (!sizes_ok(B, H, T)) return CANOPY_ERR_ARG;
     if (!aligned16(q) || !aligned16(k) || !aligned16(v) || !aligned16(S0)) return CANOPY_ERR_ARG;
     if (in_dtype != CANOPY_FP32 && in_dtype != CANOPY_BF16) return CANOPY_ERR_UNSUPPORTED;
-    if (solver != CANOPY_SOLVE_AUTO && solver != CANOPY_SOLVE_FWDSUB && solver != CANOPY_SOLVE_NEUMANN)
+    if (solver != CANOPY_SOLVE_AUTO && solver != CANOPY_SOLVE_FWDSUB &&
+        solver != CANOPY_SOLVE_NEUMANN && solver != CANOPY_SOLVE_LEVEL)
         return CANOPY_ERR_UNSUPPORTED;
     if (waves != 0 && waves != 1 && waves != 2 && waves != 4 && waves != 8) return CANOPY_ERR_UNSUPPORTED;
     VerifyArgs a{};
@@ -69,10 +65,10 @@ canopy_status canopy_tree_verify(const void *q, const void *k, const void *v,
     a.alpha = alpha; a.beta = beta; a.S0 = S0; a.parent = parent;
     a.B = B; a.H = H; a.T = T;
     a.bf16 = in_dtype == CANOPY_BF16;
-    a.solver = solver == CANOPY_SOLVE_NEUMANN ? CANOPY_SOLVE_NEUMANN : CANOPY_SOLVE_FWDSUB;
+    a.solver = solver;
     a.O = O; a.U = U; a.ell = ell;
     a.anc_mask = anc_mask; a.depth = depth; a.tree_status = tree_status;
-    return from_hip(launch_verify(a, waves ? waves : pick_waves(B, H, T), stream));
+    return from_hip(launch_verify(a, waves ? waves : pick_waves(in_dtype), stream));
 }
 
 canopy_status canopy_commit(const float *S0, const void *k, canopy_dtype in_dtype,

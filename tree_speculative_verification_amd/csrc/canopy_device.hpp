@@ -7,6 +7,9 @@ namespace canopy {
 
 typedef __attribute__((__vector_size__(8 * sizeof(__bf16)))) __bf16 bf16x8;
 typedef __attribute__((__vector_size__(4 * sizeof(float)))) float f32x4;
+// Plain 16-byte vector (HIP's uint4 is a struct with a union, which defeats scalar replacement
+// of register arrays).
+typedef unsigned int u32x4 __attribute__((ext_vector_type(4)));
 
 constexpr int D = 128;  // d_k = d_v
 
@@ -15,12 +18,13 @@ __device__ __forceinline__ float bf16_to_f32(uint16_t b) {
     return __uint_as_float(static_cast<uint32_t>(b) << 16);
 }
 
-// Makes this wave's earlier LDS writes visible to its later LDS reads across lanes. A wave's
-// LDS operations complete in order; this stops the compiler from moving accesses across it.
+// Makes this wave's earlier LDS writes visible to its later LDS reads across lanes: a wave's
+// LDS operations complete in order, so it is enough to drain the LDS counter and keep the
+// compiler from moving memory accesses across this point. Only LDS (not vector memory) is
+// waited for, so loads to registers stay in flight.
 __device__ __forceinline__ void wave_lds_sync() {
-    __builtin_amdgcn_fence(__ATOMIC_RELEASE, "wavefront");
+    asm volatile("s_waitcnt lgkmcnt(0)" ::: "memory");
     __builtin_amdgcn_wave_barrier();
-    __builtin_amdgcn_fence(__ATOMIC_ACQUIRE, "wavefront");
 }
 
 __device__ __forceinline__ int wave_max(int x) {
@@ -56,6 +60,9 @@ __device__ __forceinline__ f32x4 mfma_f32(float a, float b, f32x4 c) {
 // bf16 inputs are exact in one bf16 fragment; fp32 data (S0, G, C, U) used with bf16 inputs is
 // split into hi + lo bf16 parts (|x - hi - lo| <= 2^-16 |x|) and multiplied in up to three
 // passes (hi*hi + hi*lo + lo*hi). fp32 inputs use fp32 MFMA with exact fp32 products.
+//
+// Input rows (q, k: 128 values) staged in LDS use 16-byte chunks with the chunk index XORed
+// with (row % 16): the 16 rows a fragment read touches then fall in distinct banks.
 template <bool BF>
 struct Ops;
 
@@ -63,21 +70,23 @@ template <>
 struct Ops<true> {
     struct In { bf16x8 x; };            // exact input fragment
     struct Sp { bf16x8 hi, lo; };       // split fp32 fragment
-    static constexpr int in_bytes = 2;
+    static constexpr int ROWB = D * 2;  // bytes of one staged input row
+    static constexpr int ES = 2;        // bytes per input element
 
-    __device__ static __forceinline__ In load_in(const void *base, size_t elem, bool valid) {
-        In r;
-        if (valid) {
-            const uint4 raw = *reinterpret_cast<const uint4 *>(
-                static_cast<const uint16_t *>(base) + elem);
-            r.x = __builtin_bit_cast(bf16x8, raw);
-        } else {
-            r.x = __builtin_bit_cast(bf16x8, make_uint4(0, 0, 0, 0));
-        }
-        return r;
-    }
     __device__ static __forceinline__ float in_scalar(const void *base, size_t elem) {
         return bf16_to_f32(static_cast<const uint16_t *>(base)[elem]);
+    }
+    typedef uint16_t Raw;  // an input element as loaded, converted only where it is used
+    __device__ static __forceinline__ Raw load_raw(const void *base, size_t elem) {
+        return static_cast<const uint16_t *>(base)[elem];
+    }
+    __device__ static __forceinline__ float raw_f32(Raw r) { return bf16_to_f32(r); }
+    // Fragment of staged row `row`, reduction indices 8*g8 .. 8*g8+7.
+    __device__ static __forceinline__ In lds_frag(const uint8_t *buf, int row, int g8) {
+        In r;
+        r.x = __builtin_bit_cast(bf16x8, *reinterpret_cast<const uint4 *>(
+                                             buf + row * ROWB + ((g8 ^ (row & 15)) << 4)));
+        return r;
     }
     __device__ static __forceinline__ Sp split(const float (&v)[8]) {
         Sp s;
@@ -105,23 +114,25 @@ template <>
 struct Ops<false> {
     struct In { float x[8]; };
     typedef In Sp;
-    static constexpr int in_bytes = 4;
+    static constexpr int ROWB = D * 4;
+    static constexpr int ES = 4;
 
-    __device__ static __forceinline__ In load_in(const void *base, size_t elem, bool valid) {
-        In r;
-        if (valid) {
-            const float4 *p = reinterpret_cast<const float4 *>(static_cast<const float *>(base) + elem);
-            const float4 a = p[0], b = p[1];
-            r.x[0] = a.x; r.x[1] = a.y; r.x[2] = a.z; r.x[3] = a.w;
-            r.x[4] = b.x; r.x[5] = b.y; r.x[6] = b.z; r.x[7] = b.w;
-        } else {
-#pragma unroll
-            for (int e = 0; e < 8; ++e) r.x[e] = 0.f;
-        }
-        return r;
-    }
     __device__ static __forceinline__ float in_scalar(const void *base, size_t elem) {
         return static_cast<const float *>(base)[elem];
+    }
+    typedef float Raw;
+    __device__ static __forceinline__ Raw load_raw(const void *base, size_t elem) {
+        return static_cast<const float *>(base)[elem];
+    }
+    __device__ static __forceinline__ float raw_f32(Raw r) { return r; }
+    __device__ static __forceinline__ In lds_frag(const uint8_t *buf, int row, int g8) {
+        In r;
+        const uint8_t *p = buf + row * ROWB;
+        const float4 a = *reinterpret_cast<const float4 *>(p + (((2 * g8) ^ (row & 15)) << 4));
+        const float4 b = *reinterpret_cast<const float4 *>(p + (((2 * g8 + 1) ^ (row & 15)) << 4));
+        r.x[0] = a.x; r.x[1] = a.y; r.x[2] = a.z; r.x[3] = a.w;
+        r.x[4] = b.x; r.x[5] = b.y; r.x[6] = b.z; r.x[7] = b.w;
+        return r;
     }
     __device__ static __forceinline__ Sp split(const float (&v)[8]) {
         Sp s;
@@ -135,5 +146,93 @@ struct Ops<false> {
         return c;
     }
 };
+
+// One 64-row block of q or k (rows row0 .. row0+63 of one head; rows >= T repeat row T-1)
+// copied into the swizzled LDS layout through registers: issue() loads each thread's 16-byte
+// chunks (consecutive threads, consecutive chunks of a row), commit() stores them. The loads
+// stay in flight across other work until commit() needs them.
+template <bool BF, int NT>
+struct BlockCopy {
+    static constexpr int ROWB = Ops<BF>::ROWB;
+    static constexpr int ES = ROWB / D;        // bytes per element
+    static constexpr int CPR = ROWB / 16;      // chunks per row
+    static constexpr int PER = 64 * CPR / NT;  // chunks per thread
+    u32x4 r[PER];
+    __device__ __forceinline__ void issue(const void *g, size_t base, size_t rs, int row0, int T) {
+#pragma unroll
+        for (int m = 0; m < PER; ++m) {
+            const int idx = threadIdx.x + m * NT;
+            const int row = idx / CPR, ch = idx % CPR;
+            const int gr = min(row0 + row, T - 1);
+            r[m] = *reinterpret_cast<const u32x4 *>(static_cast<const uint8_t *>(g) +
+                                                    (base + static_cast<size_t>(gr) * rs) * ES + ch * 16);
+        }
+    }
+    __device__ __forceinline__ void commit(uint8_t *buf) const {
+#pragma unroll
+        for (int m = 0; m < PER; ++m) {
+            const int idx = threadIdx.x + m * NT;
+            const int row = idx / CPR, ch = idx % CPR;
+            *reinterpret_cast<u32x4 *>(buf + row * ROWB + ((ch ^ (row & 15)) << 4)) = r[m];
+        }
+    }
+};
+
+// One wave's 16 value columns of a 64-row block (rows >= T repeat row T-1), through registers
+// into a per-wave LDS buffer [64 rows][16 columns]: each 16-byte chunk holds 8 (bf16) or
+// 4 (fp32) columns of one row, so a row is 2 or 4 chunks.
+template <bool BF>
+struct VCopy {
+    static constexpr int ES = Ops<BF>::ES;
+    static constexpr int CPR = 16 * ES / 16;  // chunks per row
+    static constexpr int PER = 64 * CPR / 64; // chunks per lane
+    u32x4 r[PER];
+    __device__ __forceinline__ void issue(const void *g, size_t base, size_t rs, int col0, int row0,
+                                          int T, int lane) {
+#pragma unroll
+        for (int m = 0; m < PER; ++m) {
+            const int idx = lane + 64 * m;
+            const int row = idx / CPR, ch = idx % CPR;
+            const int gr = min(row0 + row, T - 1);
+            r[m] = *reinterpret_cast<const u32x4 *>(static_cast<const uint8_t *>(g) +
+                                                    (base + static_cast<size_t>(gr) * rs + col0) * ES + ch * 16);
+        }
+    }
+    __device__ __forceinline__ void commit(uint8_t *buf, int lane) const {
+#pragma unroll
+        for (int m = 0; m < PER; ++m) *reinterpret_cast<u32x4 *>(buf + (lane + 64 * m) * 16) = r[m];
+    }
+    __device__ static __forceinline__ float get(const uint8_t *buf, int row, int col) {
+        if constexpr (BF)
+            return bf16_to_f32(*reinterpret_cast<const uint16_t *>(buf + (row * 16 + col) * 2));
+        else
+            return *reinterpret_cast<const float *>(buf + (row * 16 + col) * 4);
+    }
+};
+
+// The same copy without holding the whole block in registers (for small workgroups):
+// eight chunks per thread at a time.
+template <bool BF, int NT>
+__device__ __forceinline__ void copy_block(uint8_t *buf, const void *g, size_t base, size_t rs,
+                                           int row0, int T) {
+    using BC = BlockCopy<BF, NT>;
+    for (int m0 = 0; m0 < BC::PER; m0 += 8) {
+        u32x4 r[8];
+#pragma unroll
+        for (int m = 0; m < 8; ++m) {
+            const int idx = threadIdx.x + (m0 + m) * NT;
+            const int row = idx / BC::CPR, ch = idx % BC::CPR;
+            const int gr = min(row0 + row, T - 1);
+            r[m] = *reinterpret_cast<const u32x4 *>(static_cast<const uint8_t *>(g) +
+                                                    (base + static_cast<size_t>(gr) * rs) * BC::ES + ch * 16);
+        }
+#pragma unroll
+        for (int m = 0; m < 8; ++m) {
+            const int idx = threadIdx.x + (m0 + m) * NT;
+            const int row = idx / BC::CPR, ch = idx % BC::CPR;
+            *reinterpret_cast<u32x4 *>(buf + row * BC::ROWB + ((ch ^ (row & 15)) << 4)) = r[m];
+        }
+    }
+}
 
 }  // namespace canopy

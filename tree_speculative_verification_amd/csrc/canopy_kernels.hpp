@@ -2,7 +2,7 @@
 #pragma once
 #include <hip/hip_runtime.h>
 #include <stdint.h>
-#include "../../include/canopy.h"
+#include "canopy.h"
 
 namespace canopy {
 
@@ -12,7 +12,7 @@ struct VerifyArgs {
     const int32_t *parent;
     int B, H, T;
     int bf16;    // 1: q, k, v are bf16 bit patterns; 0: fp32
-    int solver;  // CANOPY_SOLVE_FWDSUB or CANOPY_SOLVE_NEUMANN
+    int solver;  // a canopy_solver value
     float *O, *U, *ell;
     uint32_t *anc_mask;
     int32_t *depth, *tree_status;

@@ -18,14 +18,31 @@ struct PrepSmem {
     int bad;
 };
 
+// Per-thread inputs of the preprocessing: the parent and alpha of nodes tid, tid + NT, ...
+// Loading them first (before any bulk loads) keeps their latency off the critical path.
+template <int MAXT, int NT>
+struct PrepIn {
+    static constexpr int NPT = (MAXT + NT - 1) / NT;
+    int p[NPT];
+    float al[NPT];
+    __device__ __forceinline__ void load(const int32_t *parent_b, const float *alpha_h, int astride,
+                                         int T) {
+#pragma unroll
+        for (int t = 0; t < NPT; ++t) {
+            const int i = threadIdx.x + t * NT;
+            const int ic = min(i, T - 1);
+            p[t] = parent_b[ic];
+            al[t] = alpha_h[static_cast<size_t>(ic) * astride];
+        }
+    }
+};
+
 // All NT threads of the block call this. Returns 0 for a valid tree, else 1 + the first node
 // whose parent lies outside -1..i-1 (the block's result is then undefined apart from that).
-// alpha_h points at alpha[b, 0, h]; consecutive nodes are `astride` floats apart.
 template <int MAXT, int NT>
-__device__ int tree_prep_block(PrepSmem<MAXT> &s, const int32_t *parent_b, const float *alpha_h,
-                               int astride, int T) {
+__device__ int tree_prep_compute(PrepSmem<MAXT> &s, const PrepIn<MAXT, NT> &in, int T) {
     constexpr int MW = MAXT / 32;
-    constexpr int NPT = (MAXT + NT - 1) / NT;
+    constexpr int NPT = PrepIn<MAXT, NT>::NPT;
     const int tid = threadIdx.x;
     if (tid == 0) s.bad = INT_MAX;
     __syncthreads();
@@ -36,12 +53,12 @@ __device__ int tree_prep_block(PrepSmem<MAXT> &s, const int32_t *parent_b, const
             int p = -1;
             double l = 0.0;
             if (i < T) {
-                p = parent_b[i];
+                p = in.p[t];
                 if (p < -1 || p >= i) {
                     atomicMin(&s.bad, i + 1);
                     p = -1;
                 }
-                l = log(static_cast<double>(alpha_h[static_cast<size_t>(i) * astride]));
+                l = log(static_cast<double>(in.al[t]));
             }
             s.jump[i] = p;
             s.ell[i] = l;
@@ -90,6 +107,14 @@ __device__ int tree_prep_block(PrepSmem<MAXT> &s, const int32_t *parent_b, const
         if (!__syncthreads_or(more)) break;
     }
     return 0;
+}
+
+template <int MAXT, int NT>
+__device__ int tree_prep_block(PrepSmem<MAXT> &s, const int32_t *parent_b, const float *alpha_h,
+                               int astride, int T) {
+    PrepIn<MAXT, NT> in;
+    in.load(parent_b, alpha_h, astride, T);
+    return tree_prep_compute<MAXT, NT>(s, in, T);
 }
 
 // Popcount of a node's mask row, minus one: |A(i)|.

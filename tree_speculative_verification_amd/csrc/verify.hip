@@ -7,88 +7,199 @@
 //   a2       KS = K S0, QS = Q S0 on MFMA: R_i = beta_i (v_i - P_i KS_i), O_i = P_i QS_i
 //   a3       G_rc = -beta_i Gamma_ij k_i.k_j (strict ancestors), C_rc = Gamma_ij q_i.k_j
 //            (path) for 64 x 64 node blocks r >= c, MFMA K K^T and Q K^T, staged in LDS
-//   a4       blocked solve: RHS_r = R_r - sum_{c<r} G_rc U_c (MFMA), then the diagonal block
-//            by forward substitution (rows of equal in-block depth together) or by the finite
-//            Neumann series (one MFMA product per in-block level)
+//   a4       blocked solve: RHS_r = R_r - sum_{c<r} G_rc U_c (MFMA), then the diagonal block:
+//            FWDSUB  forward substitution over four 16-node sub-blocks, each 16 x 16 diagonal
+//                    sub-block inverted by substitution and applied on MFMA (depth-independent)
+//            LEVEL   row substitution, rows of equal in-block depth together (cheap when shallow)
+//            NEUMANN the finite Neumann series, one MFMA product per in-block level
+//            AUTO    LEVEL for blocks of in-block depth <= 3, else FWDSUB
 //   a5       O_r += sum_{c<=r} C_rc U_c (MFMA); O and U stored as fp32.
 // G is staged negated so that every coupling term accumulates with a plain MFMA.
+//
+// Data movement: each 64-node block of K and Q is copied once per workgroup from HBM into LDS
+// (16-byte loads to registers, then swizzled LDS stores), and every wave reads its MFMA
+// operands from there. The tree (parent, alpha, beta) is requested first, then block 0 of K
+// and Q, the wave's S0 columns and value rows, all before the tree preprocessing runs; the
+// next block's K, Q, V (and K_0) are requested before the current diagonal block is solved
+// and stored to LDS after it, and K_{c+1} is requested before the couplings to K_c.
 #include "canopy_prep.hpp"
 #include "canopy_kernels.hpp"
 
 namespace canopy {
 
-// Staging of one 64 x 64 block pair of -G and C, in the A-operand order of the MFMA.
+// Staging of one 64 x 64 block pair of -G and C in LDS, as MFMA A operands.
 template <bool BF>
 struct Stage;
 
+// bf16 hi/lo parts, rows of 8 x 16-byte chunks; chunk index XOR ((row / 2) % 8) so that the
+// 16 rows of a fragment read land in distinct banks.
 template <>
 struct Stage<true> {
-    static constexpr int LD = 72;  // bf16 elements per row (16 B aligned rows)
-    alignas(16) uint16_t gh[64][LD];
-    alignas(16) uint16_t gl[64][LD];
-    alignas(16) uint16_t ch[64][LD];
-    alignas(16) uint16_t cl[64][LD];
+    alignas(16) uint8_t gh[64 * 128];
+    alignas(16) uint8_t gl[64 * 128];
+    alignas(16) uint8_t ch[64 * 128];
+    alignas(16) uint8_t cl[64 * 128];
+    __device__ static __forceinline__ int off(int r, int c) {
+        return r * 128 + ((((c >> 3) ^ ((r >> 1) & 7))) << 4) + ((c & 7) << 1);
+    }
     __device__ __forceinline__ void store(int r, int c, float g, float cv) {
         const __bf16 g1 = static_cast<__bf16>(g), c1 = static_cast<__bf16>(cv);
         const __bf16 g2 = static_cast<__bf16>(g - static_cast<float>(g1));
         const __bf16 c2 = static_cast<__bf16>(cv - static_cast<float>(c1));
-        gh[r][c] = __builtin_bit_cast(uint16_t, g1);
-        gl[r][c] = __builtin_bit_cast(uint16_t, g2);
-        ch[r][c] = __builtin_bit_cast(uint16_t, c1);
-        cl[r][c] = __builtin_bit_cast(uint16_t, c2);
+        const int o = off(r, c);
+        *reinterpret_cast<__bf16 *>(gh + o) = g1;
+        *reinterpret_cast<__bf16 *>(gl + o) = g2;
+        *reinterpret_cast<__bf16 *>(ch + o) = c1;
+        *reinterpret_cast<__bf16 *>(cl + o) = c2;
     }
-    __device__ __forceinline__ Ops<true>::Sp frag(const uint16_t (*h)[LD], const uint16_t (*l)[LD],
-                                                 int r, int k0) const {
+    // G and C at row r, columns c0 .. c0+3 (c0 % 4 == 0): one 8-byte store per array.
+    __device__ __forceinline__ void store4(int r, int c0, const float (&g)[4], const float (&cv)[4]) {
+        uint16_t gh4[4], gl4[4], ch4[4], cl4[4];
+#pragma unroll
+        for (int e = 0; e < 4; ++e) {
+            const __bf16 g1 = static_cast<__bf16>(g[e]), c1 = static_cast<__bf16>(cv[e]);
+            gh4[e] = __builtin_bit_cast(uint16_t, g1);
+            gl4[e] = __builtin_bit_cast(uint16_t, static_cast<__bf16>(g[e] - static_cast<float>(g1)));
+            ch4[e] = __builtin_bit_cast(uint16_t, c1);
+            cl4[e] = __builtin_bit_cast(uint16_t, static_cast<__bf16>(cv[e] - static_cast<float>(c1)));
+        }
+        const int o = off(r, c0);
+        auto pack = [](const uint16_t (&x)[4]) {
+            return make_uint2(x[0] | (static_cast<uint32_t>(x[1]) << 16), x[2] | (static_cast<uint32_t>(x[3]) << 16));
+        };
+        *reinterpret_cast<uint2 *>(gh + o) = pack(gh4);
+        *reinterpret_cast<uint2 *>(gl + o) = pack(gl4);
+        *reinterpret_cast<uint2 *>(ch + o) = pack(ch4);
+        *reinterpret_cast<uint2 *>(cl + o) = pack(cl4);
+    }
+    // Zero the 16 x 16 tile at (r0, c0) of all four arrays: 128 chunks, two per lane.
+    __device__ __forceinline__ void zero_tile(int r0, int c0, int lane) {
+#pragma unroll
+        for (int a = 0; a < 2; ++a) {
+            const int idx = lane + 64 * a;
+            const int row = idx & 15, half = (idx >> 4) & 1, arr = idx >> 5;
+            uint8_t *base = arr == 0 ? gh : arr == 1 ? gl : arr == 2 ? ch : cl;
+            *reinterpret_cast<uint4 *>(base + off(r0 + row, c0 + 8 * half)) = make_uint4(0, 0, 0, 0);
+        }
+    }
+    // Overwrite G[r0 + i][c0 + lr] (i = 0..15) with x[i]: a column of a 16 x 16 tile.
+    __device__ __forceinline__ void put_col16(int r0, int c0, int lr, const float (&x)[16]) {
+#pragma unroll
+        for (int i = 0; i < 16; ++i) {
+            const __bf16 h1 = static_cast<__bf16>(x[i]);
+            const __bf16 l1 = static_cast<__bf16>(x[i] - static_cast<float>(h1));
+            const int o = off(r0 + i, c0 + lr);
+            *reinterpret_cast<__bf16 *>(gh + o) = h1;
+            *reinterpret_cast<__bf16 *>(gl + o) = l1;
+        }
+    }
+    __device__ __forceinline__ Ops<true>::Sp frag(const uint8_t *h, const uint8_t *l, int r, int k0) const {
+        const int o = off(r, k0);
         Ops<true>::Sp s;
-        s.hi = __builtin_bit_cast(bf16x8, *reinterpret_cast<const uint4 *>(&h[r][k0]));
-        s.lo = __builtin_bit_cast(bf16x8, *reinterpret_cast<const uint4 *>(&l[r][k0]));
+        s.hi = __builtin_bit_cast(bf16x8, *reinterpret_cast<const uint4 *>(h + o));
+        s.lo = __builtin_bit_cast(bf16x8, *reinterpret_cast<const uint4 *>(l + o));
         return s;
     }
     __device__ __forceinline__ Ops<true>::Sp fragG(int r, int k0) const { return frag(gh, gl, r, k0); }
     __device__ __forceinline__ Ops<true>::Sp fragC(int r, int k0) const { return frag(ch, cl, r, k0); }
     __device__ __forceinline__ float getG(int r, int c) const {
-        return bf16_to_f32(gh[r][c]) + bf16_to_f32(gl[r][c]);
+        const int o = off(r, c);
+        return static_cast<float>(*reinterpret_cast<const __bf16 *>(gh + o)) +
+               static_cast<float>(*reinterpret_cast<const __bf16 *>(gl + o));
+    }
+    // The 16 staged values G[r][c0 .. c0+15] (c0 a multiple of 16).
+    __device__ __forceinline__ void rowG16(int r, int c0, float (&out)[16]) const {
+#pragma unroll
+        for (int hh = 0; hh < 2; ++hh) {
+            const int o = off(r, c0 + 8 * hh);
+            const bf16x8 a = __builtin_bit_cast(bf16x8, *reinterpret_cast<const uint4 *>(gh + o));
+            const bf16x8 b = __builtin_bit_cast(bf16x8, *reinterpret_cast<const uint4 *>(gl + o));
+#pragma unroll
+            for (int e = 0; e < 8; ++e) out[8 * hh + e] = static_cast<float>(a[e]) + static_cast<float>(b[e]);
+        }
     }
 };
 
+// fp32, rows of 16 x 16-byte chunks, chunk index XOR (row % 16).
 template <>
 struct Stage<false> {
-    static constexpr int LD = 68;
-    alignas(16) float g[64][LD];
-    alignas(16) float c[64][LD];
-    __device__ __forceinline__ void store(int r, int cc, float gv, float cv) {
-        g[r][cc] = gv;
-        c[r][cc] = cv;
+    alignas(16) uint8_t g[64 * 256];
+    alignas(16) uint8_t c[64 * 256];
+    __device__ static __forceinline__ int off(int r, int cc) {
+        return r * 256 + (((cc >> 2) ^ (r & 15)) << 4) + ((cc & 3) << 2);
     }
-    __device__ __forceinline__ Ops<false>::Sp frag(const float (*m)[LD], int r, int k0) const {
+    __device__ __forceinline__ void store(int r, int cc, float gv, float cv) {
+        const int o = off(r, cc);
+        *reinterpret_cast<float *>(g + o) = gv;
+        *reinterpret_cast<float *>(c + o) = cv;
+    }
+    __device__ __forceinline__ void store4(int r, int c0, const float (&gv)[4], const float (&cv)[4]) {
+        const int o = off(r, c0);
+        *reinterpret_cast<float4 *>(g + o) = make_float4(gv[0], gv[1], gv[2], gv[3]);
+        *reinterpret_cast<float4 *>(c + o) = make_float4(cv[0], cv[1], cv[2], cv[3]);
+    }
+    __device__ __forceinline__ void zero_tile(int r0, int c0, int lane) {
+#pragma unroll
+        for (int a = 0; a < 2; ++a) {
+            const int idx = lane + 64 * a;
+            const int row = idx & 15, q = (idx >> 4) & 3, arr = idx >> 6;
+            uint8_t *base = arr == 0 ? g : c;
+            *reinterpret_cast<uint4 *>(base + off(r0 + row, c0 + 4 * q)) = make_uint4(0, 0, 0, 0);
+        }
+    }
+    __device__ __forceinline__ void put_col16(int r0, int c0, int lr, const float (&x)[16]) {
+#pragma unroll
+        for (int i = 0; i < 16; ++i) *reinterpret_cast<float *>(g + off(r0 + i, c0 + lr)) = x[i];
+    }
+    __device__ __forceinline__ Ops<false>::Sp frag(const uint8_t *m, int r, int k0) const {
         Ops<false>::Sp s;
-        const float4 a = *reinterpret_cast<const float4 *>(&m[r][k0]);
-        const float4 b = *reinterpret_cast<const float4 *>(&m[r][k0 + 4]);
-        s.x[0] = a.x; s.x[1] = a.y; s.x[2] = a.z; s.x[3] = a.w;
-        s.x[4] = b.x; s.x[5] = b.y; s.x[6] = b.z; s.x[7] = b.w;
+        const float4 x = *reinterpret_cast<const float4 *>(m + off(r, k0));
+        const float4 y = *reinterpret_cast<const float4 *>(m + off(r, k0 + 4));
+        s.x[0] = x.x; s.x[1] = x.y; s.x[2] = x.z; s.x[3] = x.w;
+        s.x[4] = y.x; s.x[5] = y.y; s.x[6] = y.z; s.x[7] = y.w;
         return s;
     }
     __device__ __forceinline__ Ops<false>::Sp fragG(int r, int k0) const { return frag(g, r, k0); }
     __device__ __forceinline__ Ops<false>::Sp fragC(int r, int k0) const { return frag(c, r, k0); }
-    __device__ __forceinline__ float getG(int r, int cc) const { return g[r][cc]; }
+    __device__ __forceinline__ float getG(int r, int cc) const {
+        return *reinterpret_cast<const float *>(g + off(r, cc));
+    }
+    __device__ __forceinline__ void rowG16(int r, int c0, float (&out)[16]) const {
+#pragma unroll
+        for (int q = 0; q < 4; ++q) {
+            const float4 x = *reinterpret_cast<const float4 *>(g + off(r, c0 + 4 * q));
+            out[4 * q] = x.x; out[4 * q + 1] = x.y; out[4 * q + 2] = x.z; out[4 * q + 3] = x.w;
+        }
+    }
 };
 
 constexpr int XS = 17;  // row stride (floats) of the per-wave 64 x 16 solve buffer
+// AUTO solves a diagonal block whose in-block depth is at most this by level-scheduled row
+// substitution (a few dependent steps), deeper blocks by the 16-node sub-block substitution.
+constexpr int kLevelMaxDepth = 3;
 
 template <int NW, bool BF, int NB>
 __global__ __launch_bounds__(NW * 64) void verify_kernel(VerifyArgs a) {
     using Op = Ops<BF>;
     using In = typename Op::In;
     using Sp = typename Op::Sp;
+    using Raw = typename Op::Raw;
     constexpr int MAXT = 64 * NB;
     constexpr int NT = NW * 64;
     constexpr int TILES = D / (16 * NW);
+    constexpr int BLK = 64 * Op::ROWB;  // bytes of one staged 64-row block of K or Q
+    using BC = BlockCopy<BF, NT>;
+    constexpr bool kPF = BC::PER <= 4;  // prefetch blocks through registers (wide workgroups)
 
     __shared__ PrepSmem<MAXT> ps;
     __shared__ float s_beta[MAXT], s_P[MAXT];
     __shared__ Stage<BF> st;
     __shared__ float s_x[NW][64][XS];
     __shared__ int s_list[NW][64];
+    __shared__ __attribute__((aligned(16))) uint8_t s_v[NW][64 * 16 * Op::ES];  // V rows x 16 columns
+    __shared__ __attribute__((aligned(16))) uint8_t s_ka[BLK];
+    __shared__ __attribute__((aligned(16))) uint8_t s_qa[BLK];
+    __shared__ __attribute__((aligned(16))) uint8_t s_kb[NB > 1 ? BLK : 16];
 
     const int g = xcd_remap(blockIdx.x, gridDim.x);
     const int tile = g % TILES;
@@ -103,8 +214,30 @@ __global__ __launch_bounds__(NW * 64) void verify_kernel(VerifyArgs a) {
     const size_t sbase = (static_cast<size_t>(b) * T * H + h);     // (b, node 0, h) scalars
     float(*X)[XS] = s_x[wave];
 
-    const int bad = tree_prep_block<MAXT, NT>(ps, a.parent + static_cast<size_t>(b) * T,
-                                              a.alpha + sbase, H, T);
+    // ---- loads, latency-critical first: the tree, then block 0 of K and Q, S0, V
+    PrepIn<MAXT, NT> pin;
+    pin.load(a.parent + static_cast<size_t>(b) * T, a.alpha + sbase, H, T);
+    float bet[PrepIn<MAXT, NT>::NPT];
+#pragma unroll
+    for (int t = 0; t < PrepIn<MAXT, NT>::NPT; ++t)
+        bet[t] = a.beta[sbase + static_cast<size_t>(min(tid + t * NT, T - 1)) * H];
+    BC pk, pq, p0;
+    if constexpr (kPF) {
+        pk.issue(a.k, base, rs, 0, T);
+        pq.issue(a.q, base, rs, 0, T);
+    }
+    float s0v[4][8];
+    {
+        const float *S0p = a.S0 + static_cast<size_t>(bh) * D * D + col0 + lr;
+#pragma unroll
+        for (int ks = 0; ks < 4; ++ks)
+#pragma unroll
+            for (int e = 0; e < 8; ++e) s0v[ks][e] = S0p[(32 * ks + 8 * lg + e) * D];
+    }
+    VCopy<BF> pv;  // this wave's 16 value columns of a 64-row block
+    pv.issue(a.v, base, rs, col0, 0, T, lane);
+
+    const int bad = tree_prep_compute<MAXT, NT>(ps, pin, T);
     if (bad) {
         const float qnan = __builtin_nanf("");
         for (int i = lg; i < T; i += 4) {
@@ -124,15 +257,18 @@ __global__ __launch_bounds__(NW * 64) void verify_kernel(VerifyArgs a) {
         return;
     }
 
-    for (int i = tid; i < MAXT; i += NT) {
-        float be = 0.f, P = 0.f;
-        if (i < T) {
-            be = a.beta[sbase + static_cast<size_t>(i) * H];
-            P = static_cast<float>(exp(ps.ell[i]));
-            if (tile == 0) a.ell[sbase + static_cast<size_t>(i) * H] = static_cast<float>(ps.ell[i]);
+#pragma unroll
+    for (int t = 0; t < PrepIn<MAXT, NT>::NPT; ++t) {
+        const int i = tid + t * NT;
+        if (i < MAXT) {
+            float P = 0.f;
+            if (i < T) {
+                P = static_cast<float>(exp(ps.ell[i]));
+                if (tile == 0) a.ell[sbase + static_cast<size_t>(i) * H] = static_cast<float>(ps.ell[i]);
+            }
+            s_beta[i] = (i < T) ? bet[t] : 0.f;
+            s_P[i] = P;
         }
-        s_beta[i] = be;
-        s_P[i] = P;
     }
     if (tile == 0 && h == 0) {
         const int W = (T + 31) >> 5;
@@ -144,19 +280,18 @@ __global__ __launch_bounds__(NW * 64) void verify_kernel(VerifyArgs a) {
                     a.anc_mask[(static_cast<size_t>(b) * T + i) * W + w] = ps.mask[i][w];
         }
     }
-
+    if constexpr (kPF) {
+        pk.commit(s_ka);
+        pq.commit(s_qa);
+    } else {
+        copy_block<BF, NT>(s_ka, a.k, base, rs, 0, T);
+        copy_block<BF, NT>(s_qa, a.q, base, rs, 0, T);
+    }
+    pv.commit(s_v[wave], lane);
     // S0 columns of this wave as B operands of K S0 and Q S0 (reduction index = key row).
     Sp s0f[4];
-    {
-        const float *S0p = a.S0 + static_cast<size_t>(bh) * D * D + col0 + lr;
 #pragma unroll
-        for (int ks = 0; ks < 4; ++ks) {
-            float v[8];
-#pragma unroll
-            for (int e = 0; e < 8; ++e) v[e] = S0p[(32 * ks + 8 * lg + e) * D];
-            s0f[ks] = Op::split(v);
-        }
-    }
+    for (int ks = 0; ks < 4; ++ks) s0f[ks] = Op::split(s0v[ks]);
     __syncthreads();
 
     Sp uf[NB][2];  // U of every solved block, as B operands (reduction index = node)
@@ -172,13 +307,10 @@ __global__ __launch_bounds__(NW * 64) void verify_kernel(VerifyArgs a) {
             const int i0 = 64 * r + 16 * ti;
             f32x4 ak = {0.f, 0.f, 0.f, 0.f}, aq = {0.f, 0.f, 0.f, 0.f};
             if (i0 < T) {
-                const int row = i0 + lr;
-                const bool ok = row < T;
-                const size_t el = base + static_cast<size_t>(ok ? row : 0) * rs + 8 * lg;
 #pragma unroll
                 for (int ks = 0; ks < 4; ++ks) {
-                    const In kf = Op::load_in(a.k, el + 32 * ks, ok);
-                    const In qf = Op::load_in(a.q, el + 32 * ks, ok);
+                    const In kf = Op::lds_frag(s_ka, 16 * ti + lr, 4 * ks + lg);
+                    const In qf = Op::lds_frag(s_qa, 16 * ti + lr, 4 * ks + lg);
                     ak = Op::mma(kf, s0f[ks], ak);
                     aq = Op::mma(qf, s0f[ks], aq);
                 }
@@ -188,8 +320,7 @@ __global__ __launch_bounds__(NW * 64) void verify_kernel(VerifyArgs a) {
                 const int i = i0 + 4 * lg + e;
                 float rv = 0.f, ov = 0.f;
                 if (i < T) {
-                    const float vv = Op::in_scalar(a.v, base + static_cast<size_t>(i) * rs + col0 + lr);
-                    rv = s_beta[i] * (vv - s_P[i] * ak[e]);
+                    rv = s_beta[i] * (VCopy<BF>::get(s_v[wave], 16 * ti + 4 * lg + e, lr) - s_P[i] * ak[e]);
                     ov = s_P[i] * aq[e];
                 }
                 rhs[ti][e] = rv;
@@ -199,43 +330,54 @@ __global__ __launch_bounds__(NW * 64) void verify_kernel(VerifyArgs a) {
 
 #pragma unroll
         for (int c = 0; c <= r; ++c) {
-            // ---- a3: masked, decay-weighted Gram block pair (r, c), shared by all waves
-            __syncthreads();
+            // ---- a3: masked, decay-weighted Gram block pair (r, c), shared by all waves. The
+            // MFMA takes K_c as A and K_r / Q_r as B, so each lane ends with 4 consecutive
+            // columns j of one row i: one mask word, one row's scalars, 8-byte stores.
+            const uint8_t *kc = (c < r) ? s_kb : s_ka;
+#pragma unroll 1
             for (int p = wave; p < 16; p += NW) {
                 const int ti = p >> 2, tj = p & 3;
                 const int i0 = 64 * r + 16 * ti, j0 = 64 * c + 16 * tj;
                 const bool need = (i0 < T) && (j0 < T) && (c < r || tj <= ti);
+                if (!need) {
+                    st.zero_tile(16 * ti, 16 * tj, lane);
+                    continue;
+                }
                 f32x4 kk = {0.f, 0.f, 0.f, 0.f}, qk = {0.f, 0.f, 0.f, 0.f};
-                if (need) {
-                    const int ra = i0 + lr, rb = j0 + lr;
-                    const bool oka = ra < T, okb = rb < T;
-                    const size_t ea = base + static_cast<size_t>(oka ? ra : 0) * rs + 8 * lg;
-                    const size_t eb = base + static_cast<size_t>(okb ? rb : 0) * rs + 8 * lg;
 #pragma unroll
-                    for (int ks = 0; ks < 4; ++ks) {
-                        const In ka = Op::load_in(a.k, ea + 32 * ks, oka);
-                        const In qa = Op::load_in(a.q, ea + 32 * ks, oka);
-                        const In kb = Op::load_in(a.k, eb + 32 * ks, okb);
-                        kk = Op::mma(ka, kb, kk);
-                        qk = Op::mma(qa, kb, qk);
+                for (int ks = 0; ks < 4; ++ks) {
+                    const In kb = Op::lds_frag(kc, 16 * tj + lr, 4 * ks + lg);
+                    const In ka = Op::lds_frag(s_ka, 16 * ti + lr, 4 * ks + lg);
+                    const In qa = Op::lds_frag(s_qa, 16 * ti + lr, 4 * ks + lg);
+                    kk = Op::mma(kb, ka, kk);
+                    qk = Op::mma(kb, qa, qk);
+                }
+                const int i = i0 + lr;
+                const int jb = j0 + 4 * lg;  // first of this lane's 4 columns
+                const uint32_t bits = (ps.mask[i][jb >> 5] >> (jb & 31)) & 0xFu;
+                float gv[4] = {0.f, 0.f, 0.f, 0.f}, cv[4] = {0.f, 0.f, 0.f, 0.f};
+                if (bits) {
+                    const double li = ps.ell[i];
+                    const float bi = s_beta[i];
+#pragma unroll
+                    for (int e = 0; e < 4; ++e) {
+                        if ((bits >> e) & 1u) {
+                            const float gam = expf(static_cast<float>(li - ps.ell[jb + e]));
+                            cv[e] = gam * qk[e];
+                            if (i != jb + e) gv[e] = -bi * gam * kk[e];
+                        }
                     }
                 }
-#pragma unroll
-                for (int e = 0; e < 4; ++e) {
-                    const int il = 16 * ti + 4 * lg + e, jl = 16 * tj + lr;
-                    const int i = 64 * r + il, j = 64 * c + jl;
-                    float gv = 0.f, cv = 0.f;
-                    if (need && i < T && j < T && ((ps.mask[i][j >> 5] >> (j & 31)) & 1u)) {
-                        const float gam = expf(static_cast<float>(ps.ell[i] - ps.ell[j]));
-                        cv = gam * qk[e];
-                        if (i != j) gv = -s_beta[i] * gam * kk[e];
-                    }
-                    st.store(il, jl, gv, cv);
-                }
+                st.store4(16 * ti + lr, 16 * tj + 4 * lg, gv, cv);
             }
             __syncthreads();
 
             if (c < r) {
+                // K_c is no longer needed: request K_{c+1} for the next pair of this block.
+                const bool more = c + 1 < r;
+                if constexpr (kPF) {
+                    if (more) p0.issue(a.k, base, rs, 64 * (c + 1), T);
+                }
                 // ---- a4/a5: couplings to the solved block c
 #pragma unroll
                 for (int ti = 0; ti < 4; ++ti) {
@@ -247,7 +389,21 @@ __global__ __launch_bounds__(NW * 64) void verify_kernel(VerifyArgs a) {
                         oacc[ti] = Op::mma(cf, uf[c][ks], oacc[ti]);
                     }
                 }
+                if (more) {
+                    if constexpr (kPF) p0.commit(s_kb);
+                    else copy_block<BF, NT>(s_kb, a.k, base, rs, 64 * (c + 1), T);
+                }
             } else {
+                // Block r's K and Q are no longer needed: request the next block's K, Q, V and K_0.
+                const bool next = r + 1 < nb;
+                if (next) {
+                    if constexpr (kPF) {
+                        pk.issue(a.k, base, rs, 64 * (r + 1), T);
+                        pq.issue(a.q, base, rs, 64 * (r + 1), T);
+                        if (NB > 1) p0.issue(a.k, base, rs, 0, T);
+                    }
+                    pv.issue(a.v, base, rs, col0, 64 * (r + 1), T, lane);
+                }
                 // ---- a4: the diagonal block, per wave on its 16 columns
                 const int ib = 64 * r + lane;
                 uint64_t bm = 0;
@@ -255,6 +411,31 @@ __global__ __launch_bounds__(NW * 64) void verify_kernel(VerifyArgs a) {
                     bm = (static_cast<uint64_t>(ps.mask[ib][2 * r + 1]) << 32) | ps.mask[ib][2 * r];
                 const int ld = (ib < T) ? __popcll(bm) - 1 : -1;
                 const int maxld = wave_max(ld);
+                const bool use_level = a.solver == CANOPY_SOLVE_LEVEL ||
+                                       (a.solver == CANOPY_SOLVE_AUTO && maxld <= kLevelMaxDepth);
+                const bool use_fwd = !use_level && a.solver != CANOPY_SOLVE_NEUMANN;
+                if (use_fwd) {
+                    // Each 16 x 16 unit lower-triangular diagonal sub-block I + G_pp is
+                    // inverted once per workgroup, column by column (wave 0; lane: sub-block
+                    // lg, column lr), by forward substitution on e_c. The stage holds -G, so
+                    // x_i = [i == c] + sum_{j<i} st_ij x_j. The inverse replaces G_pp in the
+                    // stage, which the sub-block substitution below no longer needs.
+                    if (wave == 0) {
+                        float x[16];
+#pragma unroll
+                        for (int i = 0; i < 16; ++i) {
+                            float row[16];
+                            st.rowG16(16 * lg + i, 16 * lg, row);
+                            float acc = (i == lr) ? 1.f : 0.f;
+#pragma unroll
+                            for (int j = 0; j < i; ++j) acc += row[j] * x[j];
+                            x[i] = acc;
+                        }
+                        wave_lds_sync();
+                        st.put_col16(16 * lg, 16 * lg, lr, x);
+                    }
+                    __syncthreads();
+                }
                 if (a.solver == CANOPY_SOLVE_NEUMANN) {
                     f32x4 z[4];
 #pragma unroll
@@ -289,7 +470,7 @@ __global__ __launch_bounds__(NW * 64) void verify_kernel(VerifyArgs a) {
 #pragma unroll
                         for (int e = 0; e < 4; ++e) X[16 * ti + 4 * lg + e][lr] = rhs[ti][e];
                     wave_lds_sync();
-                } else {
+                } else if (use_level) {
 #pragma unroll
                     for (int ti = 0; ti < 4; ++ti)
 #pragma unroll
@@ -318,6 +499,51 @@ __global__ __launch_bounds__(NW * 64) void verify_kernel(VerifyArgs a) {
                         }
                         wave_lds_sync();
                     }
+                } else {
+                    // Blocked forward substitution inside the block: four 16-node sub-blocks;
+                    // the inverses of the diagonal sub-blocks are in the stage (see above).
+#pragma unroll
+                    for (int ti = 0; ti < 4; ++ti)
+#pragma unroll
+                        for (int e = 0; e < 4; ++e) X[16 * ti + 4 * lg + e][lr] = rhs[ti][e];
+                    wave_lds_sync();
+                    // (2) U_p = (I + G_pp)^-1 (RHS_p - sum_{q<p} G_pq U_q), p = 0..3 (MFMA).
+#pragma unroll
+                    for (int p = 0; p < 4; ++p) {
+                        if (64 * r + 16 * p >= T) break;
+                        f32x4 acc = rhs[p];
+#pragma unroll
+                        for (int ks = 0; ks < 2; ++ks) {
+                            if (32 * ks < 16 * p) {
+                                Sp gf = st.fragG(16 * p + lr, 32 * ks + 8 * lg);
+                                if (32 * ks + 8 * lg >= 16 * p) {
+                                    const float z8[8] = {0.f, 0.f, 0.f, 0.f, 0.f, 0.f, 0.f, 0.f};
+                                    gf = Op::split(z8);
+                                }
+                                float v[8];
+#pragma unroll
+                                for (int e = 0; e < 8; ++e) v[e] = X[32 * ks + 8 * lg + e][lr];
+                                acc = Op::mma(gf, Op::split(v), acc);
+                            }
+                        }
+#pragma unroll
+                        for (int e = 0; e < 4; ++e) X[16 * p + 4 * lg + e][lr] = acc[e];
+                        wave_lds_sync();
+                        float v[8];
+#pragma unroll
+                        for (int e = 0; e < 8; ++e) v[e] = (lg < 2) ? X[16 * p + 8 * lg + e][lr] : 0.f;
+                        Sp dfr = st.fragG(16 * p + lr, 16 * p + 8 * (lg & 1));
+                        if (lg >= 2) {
+                            const float z8[8] = {0.f, 0.f, 0.f, 0.f, 0.f, 0.f, 0.f, 0.f};
+                            dfr = Op::split(z8);
+                        }
+                        f32x4 u = {0.f, 0.f, 0.f, 0.f};
+                        u = Op::mma(dfr, Op::split(v), u);
+                        wave_lds_sync();
+#pragma unroll
+                        for (int e = 0; e < 4; ++e) X[16 * p + 4 * lg + e][lr] = u[e];
+                        wave_lds_sync();
+                    }
                 }
 #pragma unroll
                 for (int ks = 0; ks < 2; ++ks) {
@@ -331,23 +557,37 @@ __global__ __launch_bounds__(NW * 64) void verify_kernel(VerifyArgs a) {
 #pragma unroll
                     for (int ks = 0; ks < 2; ++ks)
                         oacc[ti] = Op::mma(st.fragC(16 * ti + lr, 32 * ks + 8 * lg), uf[r][ks], oacc[ti]);
-            }
-        }
 
-        // ---- a6: outputs of block r
+                // ---- a6: outputs of block r
 #pragma unroll
-        for (int m = 0; m < 16; ++m) {
-            const int rl = lg + 4 * m;
-            const int i = 64 * r + rl;
-            if (i < T) a.U[base + static_cast<size_t>(i) * rs + col0 + lr] = X[rl][lr];
-        }
+                for (int m = 0; m < 16; ++m) {
+                    const int rl = lg + 4 * m;
+                    const int i = 64 * r + rl;
+                    if (i < T) a.U[base + static_cast<size_t>(i) * rs + col0 + lr] = X[rl][lr];
+                }
 #pragma unroll
-        for (int ti = 0; ti < 4; ++ti)
+                for (int ti = 0; ti < 4; ++ti)
 #pragma unroll
-            for (int e = 0; e < 4; ++e) {
-                const int i = 64 * r + 16 * ti + 4 * lg + e;
-                if (i < T) a.O[base + static_cast<size_t>(i) * rs + col0 + lr] = oacc[ti][e];
+                    for (int e = 0; e < 4; ++e) {
+                        const int i = 64 * r + 16 * ti + 4 * lg + e;
+                        if (i < T) a.O[base + static_cast<size_t>(i) * rs + col0 + lr] = oacc[ti][e];
+                    }
+                if (next) {
+                    pv.commit(s_v[wave], lane);
+                    if constexpr (kPF) {
+                        pk.commit(s_ka);
+                        pq.commit(s_qa);
+                        if (NB > 1) p0.commit(s_kb);
+                    } else {
+                        copy_block<BF, NT>(s_ka, a.k, base, rs, 64 * (r + 1), T);
+                        copy_block<BF, NT>(s_qa, a.q, base, rs, 64 * (r + 1), T);
+                        if (NB > 1) copy_block<BF, NT>(s_kb, a.k, base, rs, 0, T);
+                    }
+                }
             }
+            // The stage is free and the next operands are in LDS for every wave.
+            __syncthreads();
+        }
     }
 }
 
@@ -370,18 +610,18 @@ static hipError_t launch_nw(const VerifyArgs &a, hipStream_t stream) {
     }
 }
 
-template <bool BF>
-static hipError_t launch_bf(const VerifyArgs &a, int waves, hipStream_t stream) {
-    switch (waves) {
-        case 1: return launch_nw<1, BF>(a, stream);
-        case 2: return launch_nw<2, BF>(a, stream);
-        case 4: return launch_nw<4, BF>(a, stream);
-        default: return launch_nw<8, BF>(a, stream);
-    }
-}
-
 hipError_t launch_verify(const VerifyArgs &a, int waves, hipStream_t stream) {
-    return a.bf16 ? launch_bf<true>(a, waves, stream) : launch_bf<false>(a, waves, stream);
+    if (a.bf16) {
+        switch (waves) {
+            case 1: return launch_nw<1, true>(a, stream);
+            case 2: return launch_nw<2, true>(a, stream);
+            case 4: return launch_nw<4, true>(a, stream);
+            default: return launch_nw<8, true>(a, stream);
+        }
+    }
+    // fp32 inputs stage twice the bytes per block: at most 2 waves fit the LDS budget.
+    if (waves == 1) return launch_nw<1, false>(a, stream);
+    return launch_nw<2, false>(a, stream);
 }
 
 }  // namespace canopy
