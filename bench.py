@@ -150,6 +150,133 @@ def cpu_baseline(inp, budget_s=10.0):
                 kind="oracle", sample=f"{len(times)} full layers of this workload, median")
 
 
+def crossover_cells():
+    """Depth x width level trees: root, then levels of W nodes (the last one partial);
+    W = 1 is a chain; shapes that coincide (stars) are kept once; depth 1..64."""
+    import synth
+    seen, cells = set(), []
+    for W in (1, 2, 4, 8, 16):
+        for T in (3, 8, 16, 32, 64, 128, 256):
+            par = synth.level_tree(T, W)
+            D = int(synth.tree_depths(par).max())
+            if not 1 <= D <= 64:
+                continue
+            key = tuple(par.tolist())
+            if key in seen:
+                continue
+            seen.add(key)
+            cells.append((W, T, D))
+    return cells
+
+
+def run_crossover(args):
+    """24 stacked GDN layers, rounds of verify + commit that chain each layer's committed
+    state, parallel (tree verify + commit) against the serial fork baseline (serial verify +
+    snapshot commit), for every depth x width cell and batch size. One round (24 layers) is
+    captured as a HIP graph; the accepted path of every round is copied in before its replay."""
+    import numpy as np
+    import torch
+    import synth
+    import tree_speculative_verification_amd as tsv
+    tsv.load()
+    L, H = 24, 32
+    out = open(args.out, "a") if args.out else None
+    gen = torch.Generator(device="cuda")
+    for B in args.batches:
+        for (W, T, D) in crossover_cells():
+            if args.max_t and T > args.max_t:
+                continue
+            gen.manual_seed(1000 * B + T * 17 + W)
+            par_np = synth.level_tree(T, W)
+            parent = torch.from_numpy(np.broadcast_to(par_np, (B, T)).copy()).cuda()
+            q, k, v, al, be, S0 = [], [], [], [], [], []
+            for _ in range(L):
+                xq = torch.randn(B, T, H, 128, device="cuda", generator=gen)
+                xk = torch.randn(B, T, H, 128, device="cuda", generator=gen)
+                q.append((xq / xq.norm(dim=-1, keepdim=True)).to(torch.bfloat16))
+                k.append((xk / xk.norm(dim=-1, keepdim=True)).to(torch.bfloat16))
+                v.append(torch.randn(B, T, H, 128, device="cuda", generator=gen).to(torch.bfloat16))
+                be.append(torch.sigmoid(torch.randn(B, T, H, device="cuda", generator=gen)))
+                al.append(torch.exp(-torch.nn.functional.softplus(torch.randn(B, T, H, device="cuda", generator=gen))))
+                S0.append(0.1 * torch.randn(B, H, 128, 128, device="cuda", generator=gen))
+            rng = np.random.default_rng(B * 7919 + T * 31 + W)
+            R = args.rounds
+            paths = np.full((R, B, T), -1, np.int32)
+            plens = np.zeros((R, B), np.int32)
+            for r in range(R):
+                for b in range(B):
+                    pth = synth.random_leaf_path(par_np, rng)
+                    paths[r, b, :len(pth)] = pth
+                    plens[r, b] = len(pth)
+            paths_d = torch.from_numpy(paths).cuda()
+            plens_d = torch.from_numpy(plens).cuda()
+            path_cur = torch.empty((B, T), dtype=torch.int32, device="cuda")
+            plen_cur = torch.empty((B,), dtype=torch.int32, device="cuda")
+            O = torch.empty((B, T, H, 128), device="cuda")
+            U = torch.empty_like(O)
+            ell = torch.empty((B, T, H), device="cuda")
+            S_par = [s.clone() for s in S0]
+            S_ser = [s.clone() for s in S0]
+            snaps = torch.empty((B, T, H, 128, 128), device="cuda")
+
+            def round_parallel():
+                for l in range(L):
+                    tsv.tree_verify(q[l], k[l], v[l], al[l], be[l], S_par[l], parent, out=(O, U, ell))
+                    tsv.commit(S_par[l], k[l], U, al[l], parent, path_cur, plen_cur, out=S_par[l])
+
+            def round_serial():
+                for l in range(L):
+                    tsv.serial_verify(q[l], k[l], v[l], al[l], be[l], S_ser[l], parent, snapshots=snaps)
+                    tsv.serial_commit(snaps, S_ser[l], parent, path_cur, plen_cur, out=S_ser[l])
+
+            def timed(fn, r0, rounds):
+                """Rounds r0 .. r0+rounds-1 of the chain (each with its own accepted path)."""
+                path_cur.copy_(paths_d[r0]); plen_cur.copy_(plens_d[r0])
+                g = torch.cuda.CUDAGraph()
+                torch.cuda.synchronize()
+                with torch.cuda.graph(g):
+                    fn()
+                torch.cuda.synchronize()
+                e0 = torch.cuda.Event(enable_timing=True)
+                e1 = torch.cuda.Event(enable_timing=True)
+                e0.record()
+                for r in range(r0, r0 + rounds):
+                    path_cur.copy_(paths_d[r]); plen_cur.copy_(plens_d[r])
+                    g.replay()
+                e1.record()
+                torch.cuda.synchronize()
+                del g
+                return e0.elapsed_time(e1) * 1000.0 / rounds
+
+            # Both sides start from the same states and commit the same path in round r. The
+            # serial side times its first round alone, to size its run to the time budget.
+            us_par = timed(round_parallel, 0, R)
+            us_ser_probe = timed(round_serial, 0, 1)
+            R_ser = int(max(0, min(R - 1, args.serial_budget * 1e6 / max(us_ser_probe, 1.0))))
+            us_ser = timed(round_serial, 1, R_ser) if R_ser >= 1 else us_ser_probe
+            rounds_ser = 1 + R_ser
+            err = None
+            if rounds_ser == R:
+                num = max(float((a - b).abs().max()) / max(float(b.abs().max()), 1e-30) for a, b in zip(S_par, S_ser))
+                err = num
+            rec = {"W": W, "T": T, "depth": D, "B": B, "H": H, "layers": L,
+                   "rounds_parallel": R, "rounds_serial": rounds_ser,
+                   "us_per_round_parallel": round(us_par, 2), "us_per_round_serial": round(us_ser, 2),
+                   "us_per_layer_parallel": round(us_par / L, 3), "us_per_layer_serial": round(us_ser / L, 3),
+                   "speedup_parallel_over_serial": round(us_ser / us_par, 3),
+                   "final_state_rel_err_parallel_vs_serial": err}
+            line = json.dumps(rec)
+            print(line, flush=True)
+            if out:
+                out.write(line + "\n")
+                out.flush()
+            del q, k, v, al, be, S0, S_par, S_ser, snaps, O, U
+            torch.cuda.empty_cache()
+    if out:
+        out.close()
+    return 0
+
+
 def main(argv=None):
     ap = argparse.ArgumentParser(description=__doc__, formatter_class=argparse.RawDescriptionHelpFormatter)
     ap.add_argument("--gpus", type=int, default=1)
@@ -163,6 +290,17 @@ def main(argv=None):
     ap.add_argument("--cpu-budget", type=float, default=10.0)
     ap.add_argument("--eager", action="store_true",
                     help="launch every kernel from Python instead of replaying a HIP graph")
+    ap.add_argument("--crossover", action="store_true",
+                    help="run the depth x width crossover over 24 layers instead of one workload")
+    ap.add_argument("--rounds", type=int, default=100, help="crossover: rounds per cell")
+    ap.add_argument("--batches", type=int, nargs="+", default=[1, 4, 16], help="crossover: batch sizes")
+    ap.add_argument("--max-t", type=int, default=0, help="crossover: skip trees larger than this")
+    ap.add_argument("--serial-budget", type=float, default=2.0,
+                    help="crossover: seconds of serial rounds per cell (at most --rounds)")
+    ap.add_argument("--out", default="", help="crossover: append JSON lines to this file")
+    ap.add_argument("--copy-probe", type=int, default=0, metavar="BYTES",
+                    help="also run one plain device-to-device copy of this many bytes (a known "
+                         "traffic reference for hardware counters)")
     args = ap.parse_args(argv)
 
     if args.gpus != 1 or int(os.environ.get("WORLD_SIZE", "1")) != 1:
@@ -170,6 +308,8 @@ def main(argv=None):
               "head) with no exchange, and this build runs on a single MI355X. Use --gpus 1.",
               file=sys.stderr)
         return 2
+    if args.crossover:
+        return run_crossover(args)
 
     import numpy as np
     import torch
@@ -233,6 +373,14 @@ def main(argv=None):
             us_serial = time_graph(g_s, n_ser)
             del g_s
         del snaps
+
+    if args.copy_probe:
+        src = torch.empty(args.copy_probe // 4, dtype=torch.float32, device="cuda").fill_(1.0)
+        dst = torch.empty_like(src)
+        torch.cuda.synchronize()
+        dst.copy_(src)
+        torch.cuda.synchronize()
+        del src, dst
 
     vbytes = verify_bytes(B, H, T, dt)
     achieved = vbytes / (us_verify * 1e-6) / 1e9

@@ -62,7 +62,10 @@ typedef enum { CANOPY_FP32 = 0, CANOPY_BF16 = 1 } canopy_dtype;
  *            matrix-core product per term (for T <= 64: the whole tree's Neumann series with
  *            one term per tree level).
  *   LEVEL    row-by-row substitution with the rows of equal in-block depth solved together.
- *   AUTO     LEVEL for blocks of in-block depth <= 3, FWDSUB otherwise. */
+ *   AUTO     LEVEL for blocks of in-block depth <= 3, FWDSUB otherwise.
+ * Trees of at most 16 nodes fit one matrix-core tile: there AUTO and NEUMANN run a single-wave
+ * kernel that keeps everything in registers and sums the Neumann series (one term per tree
+ * level); FWDSUB and LEVEL run the blocked kernel. */
 typedef enum {
     CANOPY_SOLVE_AUTO = 0,
     CANOPY_SOLVE_FWDSUB = 1,
@@ -148,6 +151,18 @@ canopy_status canopy_serial_verify(const void *q, const void *k, const void *v,
                                    const int32_t *parent, int B, int H, int T,
                                    canopy_dtype in_dtype, float *O, float *U, float *snapshots,
                                    int32_t *tree_status, hipStream_t stream);
+
+/*
+ * Commit for the serial baseline: the accepted path's last node's snapshot (written by
+ * canopy_serial_verify) becomes the new state (S0 itself for an empty path). Path checks and
+ * path_status as in canopy_commit.
+ *   snapshots   [B,T,H,128,128] fp32, in.
+ *   S0          [B,H,128,128] fp32, in.
+ *   S_new       [B,H,128,128] fp32, out; may be the same memory as S0.
+ */
+canopy_status canopy_serial_commit(const float *snapshots, const float *S0, const int32_t *parent,
+                                   const int32_t *path, const int32_t *path_len, int B, int H, int T,
+                                   float *S_new, int32_t *path_status, hipStream_t stream);
 
 #ifdef __cplusplus
 }

@@ -195,6 +195,29 @@ def test_serial_snapshots_match_oracle_states(canopy):
         assert_close_state("snapshots", x, y, TOL[dtype])
 
 
+def test_serial_commit(canopy):
+    """The serial baseline's commit copies the accepted node's snapshot: it equals the oracle's
+    path recurrence; an empty path keeps S0; bad paths give their status and NaN."""
+    import torch
+    inp = synth.make_inputs(3, 2, 30, tree="skewed", dtype="bf16", seed=450)
+    inp["path_len"][1] = 0
+    d = to_device(inp)
+    _say("serial verify + commit")
+    O, U, snap, st = canopy.serial_verify(d["q"], d["k"], d["v"], d["alpha"], d["beta"], d["S0"], d["parent"])
+    Sn, pst = canopy.serial_commit(snap, d["S0"], d["parent"], d["path"], d["path_len"])
+    torch.cuda.synchronize()
+    S_or, st_or = oracle_commit(inp)
+    assert pst.cpu().numpy().tolist() == st_or.tolist() == [0, 0, 0]
+    assert torch.equal(Sn[1], d["S0"][1])
+    assert_close_state("serial S_new", Sn.cpu().numpy(), S_or, TOL["bf16"])
+    bad = d["path"].clone()
+    bad[0, 1] = 30  # a node id out of range at position 1
+    Sn2, pst2 = canopy.serial_commit(snap, d["S0"], d["parent"], bad, d["path_len"])
+    torch.cuda.synchronize()
+    assert pst2.cpu().numpy().tolist()[0] == 2
+    assert torch.isnan(Sn2[0]).all()
+
+
 def test_prep_entry_point(canopy):
     import torch
     for T in (1, 5, 33, 100, 256):
@@ -244,6 +267,32 @@ def test_invalid_tree_and_path_reported(canopy):
     Sn = Sn.cpu().numpy()
     assert np.isnan(Sn[1:]).all()
     assert_close_state("S_new", Sn[:1], S_or[:1], TOL["fp32"])
+
+
+@pytest.mark.parametrize("kind,T", [("chain", 200), ("chain", 33), ("skewed", 128), ("random", 256)])
+def test_commit_long_paths(canopy, kind, T):
+    """Paths of every length up to T (chains commit all T nodes): the path is staged 32 nodes at
+    a time, so lengths around and above 32 cover every chunk edge."""
+    import torch
+    for dtype in ("bf16", "fp32"):
+        inp = synth.make_inputs(4, 2, T, tree=kind, dtype=dtype, seed=900 + T)
+        rng = np.random.default_rng(T)
+        for b in range(4):  # accepted node anywhere on the tree, not only leaves
+            a_node = int(rng.integers(0, T)) if b else T - 1
+            pth = synth.root_path(inp["parent"][b], a_node)
+            inp["path"][b] = -1
+            inp["path"][b, :len(pth)] = pth
+            inp["path_len"][b] = len(pth)
+        d = to_device(inp)
+        _say("commit long paths", kind, T, dtype, inp["path_len"].tolist())
+        _, U, _ = canopy.tree_verify(d["q"], d["k"], d["v"], d["alpha"], d["beta"], d["S0"], d["parent"])
+        Sn, pst = canopy.commit(d["S0"], d["k"], U, d["alpha"], d["parent"], d["path"], d["path_len"])
+        Sn2, _ = canopy.commit(d["S0"], d["k"], U, d["alpha"], d["parent"], d["path"], d["path_len"])
+        torch.cuda.synchronize()
+        assert torch.equal(Sn, Sn2)
+        S_or, st_or = oracle_commit(inp)
+        assert pst.cpu().numpy().tolist() == st_or.tolist() == [0, 0, 0, 0]
+        assert_close_state("S_new", Sn.cpu().numpy(), S_or, TOL[dtype])
 
 
 def test_commit_empty_path_and_in_place(canopy):

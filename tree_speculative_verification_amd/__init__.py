@@ -7,6 +7,7 @@ Functions take and return torch tensors on the GPU:
   tree_verify(q, k, v, alpha, beta, S0, parent, ...)    -> (O, U, ell) [+ mask, depth, status]
   commit(S0, k, U, alpha, parent, path, path_len, ...)  -> (S_new, path_status)
   serial_verify(q, k, v, alpha, beta, S0, parent)       -> (O, U, snapshots, status)
+  serial_commit(snapshots, S0, parent, path, path_len)  -> (S_new, path_status)
 q, k, v are torch.bfloat16 or torch.float32 [B,T,H,128]; alpha, beta fp32 [B,T,H];
 S0 fp32 [B,H,128,128]; parent int32 [B,T]; path int32 [B,T]; path_len int32 [B].
 
@@ -20,7 +21,7 @@ import os
 import torch  # loaded first so that libcanopy binds to the HIP runtime torch uses
 
 __all__ = ["load", "lib_path", "tree_prep", "tree_verify", "commit", "serial_verify",
-           "CanopyError", "SOLVERS"]
+           "serial_commit", "CanopyError", "SOLVERS"]
 
 _HERE = os.path.dirname(os.path.abspath(__file__))
 _LIB_PATH = os.path.join(_HERE, "libcanopy.so")
@@ -59,6 +60,8 @@ def load():
     lib.canopy_commit.restype = i
     lib.canopy_serial_verify.argtypes = [P, P, P, P, P, P, P, i, i, i, i, P, P, P, P, u64]
     lib.canopy_serial_verify.restype = i
+    lib.canopy_serial_commit.argtypes = [P, P, P, P, P, i, i, i, P, P, u64]
+    lib.canopy_serial_commit.restype = i
     _lib = lib
     return lib
 
@@ -194,3 +197,20 @@ def serial_verify(q, k, v, alpha, beta, S0, parent, snapshots=None):
                                        _ptr(S0), _ptr(parent), B, H, T, dt, _ptr(O), _ptr(U),
                                        _ptr(snapshots), _ptr(status), _stream()))
     return O, U, snapshots, status
+
+
+def serial_commit(snapshots, S0, parent, path, path_len, out=None):
+    """Serial baseline commit: the snapshot of each sequence's accepted node becomes S_new
+    (``out`` may be S0 for an in-place commit); returns (S_new, path_status)."""
+    B, T, H, d, _ = snapshots.shape
+    _req(snapshots, "snapshots", torch.float32, (B, T, H, d, d))
+    _req(S0, "S0", torch.float32, (B, H, d, d))
+    _req(parent, "parent", torch.int32, (B, T))
+    _req(path, "path", torch.int32, (B, T))
+    _req(path_len, "path_len", torch.int32, (B,))
+    S_new = torch.empty_like(S0) if out is None else _req(out, "out", torch.float32, (B, H, d, d))
+    status = torch.empty((B,), dtype=torch.int32, device=S0.device)
+    _check(load().canopy_serial_commit(_ptr(snapshots), _ptr(S0), _ptr(parent), _ptr(path),
+                                       _ptr(path_len), B, H, T, _ptr(S_new), _ptr(status),
+                                       _stream()))
+    return S_new, status

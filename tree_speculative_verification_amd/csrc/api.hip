@@ -68,6 +68,10 @@ canopy_status canopy_tree_verify(const void *q, const void *k, const void *v,
     a.solver = solver;
     a.O = O; a.U = U; a.ell = ell;
     a.anc_mask = anc_mask; a.depth = depth; a.tree_status = tree_status;
+    // Trees of at most 16 nodes fit one MFMA tile: AUTO and NEUMANN run the single-wave
+    // register kernel (Neumann series in registers); FWDSUB and LEVEL keep the blocked kernel.
+    if (T <= 16 && (solver == CANOPY_SOLVE_AUTO || solver == CANOPY_SOLVE_NEUMANN))
+        return from_hip(launch_verify_small(a, stream));
     return from_hip(launch_verify(a, waves ? waves : pick_waves(in_dtype), stream));
 }
 
@@ -98,6 +102,16 @@ canopy_status canopy_serial_verify(const void *q, const void *k, const void *v,
     SerialArgs a{q, k, v, alpha, beta, S0, parent, B, H, T, in_dtype == CANOPY_BF16,
                  O, U, snapshots, tree_status};
     return from_hip(launch_serial(a, stream));
+}
+
+canopy_status canopy_serial_commit(const float *snapshots, const float *S0, const int32_t *parent,
+                                   const int32_t *path, const int32_t *path_len, int B, int H, int T,
+                                   float *S_new, int32_t *path_status, hipStream_t stream) {
+    if (!snapshots || !S0 || !parent || !path || !path_len || !S_new) return CANOPY_ERR_ARG;
+    if (!sizes_ok(B, H, T)) return CANOPY_ERR_ARG;
+    if (!aligned16(snapshots) || !aligned16(S0) || !aligned16(S_new)) return CANOPY_ERR_ARG;
+    SerialCommitArgs a{snapshots, S0, parent, path, path_len, B, H, T, S_new, path_status};
+    return from_hip(launch_serial_commit(a, stream));
 }
 
 }  // extern "C"

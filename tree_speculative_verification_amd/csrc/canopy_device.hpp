@@ -76,6 +76,15 @@ struct Ops<true> {
     __device__ static __forceinline__ float in_scalar(const void *base, size_t elem) {
         return bf16_to_f32(static_cast<const uint16_t *>(base)[elem]);
     }
+    // Fragment straight from global memory: 8 consecutive elements at `elem` (16-byte aligned).
+    template <class F>
+    __device__ static __forceinline__ F load_frag(const void *base, size_t elem, bool valid) {
+        F r;
+        u32x4 raw = {0u, 0u, 0u, 0u};
+        if (valid) raw = *reinterpret_cast<const u32x4 *>(static_cast<const uint16_t *>(base) + elem);
+        r.x = __builtin_bit_cast(bf16x8, raw);
+        return r;
+    }
     typedef uint16_t Raw;  // an input element as loaded, converted only where it is used
     __device__ static __forceinline__ Raw load_raw(const void *base, size_t elem) {
         return static_cast<const uint16_t *>(base)[elem];
@@ -119,6 +128,19 @@ struct Ops<false> {
 
     __device__ static __forceinline__ float in_scalar(const void *base, size_t elem) {
         return static_cast<const float *>(base)[elem];
+    }
+    template <class F>
+    __device__ static __forceinline__ F load_frag(const void *base, size_t elem, bool valid) {
+        F r;
+#pragma unroll
+        for (int e = 0; e < 8; ++e) r.x[e] = 0.f;
+        if (valid) {
+            const float4 *p = reinterpret_cast<const float4 *>(static_cast<const float *>(base) + elem);
+            const float4 x = p[0], y = p[1];
+            r.x[0] = x.x; r.x[1] = x.y; r.x[2] = x.z; r.x[3] = x.w;
+            r.x[4] = y.x; r.x[5] = y.y; r.x[6] = y.z; r.x[7] = y.w;
+        }
+        return r;
     }
     typedef float Raw;
     __device__ static __forceinline__ Raw load_raw(const void *base, size_t elem) {
@@ -209,6 +231,54 @@ struct VCopy {
             return *reinterpret_cast<const float *>(buf + (row * 16 + col) * 4);
     }
 };
+
+// 16 bytes per lane from global memory straight into LDS (global_load_lds_dwordx4): lane l's
+// data lands at lds_base + 16 * l; lds_base must be the same for the whole wave.
+__device__ __forceinline__ void dma16(const void *gsrc, void *lds_base) {
+    __builtin_amdgcn_global_load_lds(
+        (const void __attribute__((address_space(1))) *)gsrc,
+        (void __attribute__((address_space(3))) *)lds_base, 16, 0, 0);
+}
+
+// The same block copy with LDS-bound loads: no registers are held while the data is in flight.
+// Wave w issues the 1-KB pieces w, w + NW, ...; a piece is 1024 / ROWB rows, and lane l fetches
+// the global chunk that the swizzle places at piece offset 16 * l.
+template <bool BF, int NT>
+__device__ __forceinline__ void dma_block(uint8_t *buf, const void *g, size_t base, size_t rs,
+                                          int row0, int T) {
+    using BC = BlockCopy<BF, NT>;
+    constexpr int PIECES = 64 * BC::ROWB / 1024;
+    constexpr int RPP = 1024 / BC::ROWB;  // rows per piece
+    const int wave = threadIdx.x >> 6, lane = threadIdx.x & 63;
+    for (int s = wave; s < PIECES; s += NT / 64) {
+        const int row = RPP * s + lane / BC::CPR;
+        const int ch = (lane % BC::CPR) ^ (row & 15);
+        const int gr = min(row0 + row, T - 1);
+        dma16(static_cast<const uint8_t *>(g) + (base + static_cast<size_t>(gr) * rs) * BC::ES + ch * 16,
+              buf + s * 1024);
+    }
+}
+
+// One wave's 16 value columns of a 64-row block with LDS-bound loads, in the VCopy layout
+// [row][16 columns]: a 1-KB piece holds 1024 / (16 * ES) rows.
+template <bool BF>
+__device__ __forceinline__ void dma_v(uint8_t *buf, const void *g, size_t base, size_t rs, int col0,
+                                      int row0, int T, int lane) {
+    constexpr int ES = Ops<BF>::ES;
+    constexpr int LPR = 16 * ES / 16;          // lanes (16-byte chunks) per row
+    constexpr int PIECES = 64 * 16 * ES / 1024;
+#pragma unroll
+    for (int s = 0; s < PIECES; ++s) {
+        const int row = s * (64 / LPR) + lane / LPR;
+        const int ch = lane % LPR;
+        const int gr = min(row0 + row, T - 1);
+        dma16(static_cast<const uint8_t *>(g) + (base + static_cast<size_t>(gr) * rs + col0) * ES + ch * 16,
+              buf + s * 1024);
+    }
+}
+
+// Wait until this wave's LDS-bound loads (and other vector memory operations) have completed.
+__device__ __forceinline__ void wait_vmem() { asm volatile("s_waitcnt vmcnt(0)" ::: "memory"); }
 
 // The same copy without holding the whole block in registers (for small workgroups):
 // eight chunks per thread at a time.

@@ -49,9 +49,19 @@ struct SerialArgs {
     int32_t *tree_status;
 };
 
+struct SerialCommitArgs {
+    const float *snap, *S0;
+    const int32_t *parent, *path, *path_len;
+    int B, H, T;
+    float *S_new;
+    int32_t *path_status;
+};
+
 hipError_t launch_verify(const VerifyArgs &a, int waves, hipStream_t stream);
+hipError_t launch_verify_small(const VerifyArgs &a, hipStream_t stream);
 hipError_t launch_prep(const PrepArgs &a, hipStream_t stream);
 hipError_t launch_commit(const CommitArgs &a, hipStream_t stream);
 hipError_t launch_serial(const SerialArgs &a, hipStream_t stream);
+hipError_t launch_serial_commit(const SerialCommitArgs &a, hipStream_t stream);
 
 }  // namespace canopy

@@ -3,8 +3,10 @@
 //   w_t = exp(sum_{s > t} log alpha_{path[s]}) = Gamma_{a, path[t]},  P_a = exp(sum_s log alpha).
 // One workgroup per (sequence, head, 32 state rows); 256 threads, each owning four float4s of
 // the 32 x 128 row chunk, so loads and stores of S are fully coalesced. The decay weights are
-// suffix sums of log alpha along the path in fp64: the ratio of two nearby nodes is formed
-// directly and never as the difference of two large cumulative logs.
+// suffix sums of log alpha along the path in fp64 (wave shuffles, then the wave totals): the
+// ratio of two nearby nodes is a short sum, never the difference of two large cumulative
+// logs. S0, the path and the first 32 path nodes' U rows and keys are requested before the
+// sums are finished, so the path check, the sums and the loads overlap.
 #include "canopy_device.hpp"
 #include "canopy_kernels.hpp"
 #include <limits.h>
@@ -16,10 +18,11 @@ constexpr int CCH = 32;    // path nodes staged per pass
 
 template <bool BF>
 __global__ __launch_bounds__(256) void commit_kernel(CommitArgs a) {
-    __shared__ double s_la[256];
     __shared__ int s_path[256];
-    __shared__ int s_bad;
+    __shared__ double s_wsum[4];
     __shared__ float s_w[256];
+    __shared__ float s_pa;
+    __shared__ int s_bad;
     __shared__ float4 s_u[CCH][D / 4];
     __shared__ float s_kw[CCH][CROWS];
 
@@ -28,74 +31,107 @@ __global__ __launch_bounds__(256) void commit_kernel(CommitArgs a) {
     const int bh = g / (D / CROWS);
     const int H = a.H, T = a.T;
     const int b = bh / H, h = bh % H;
-    const int tid = threadIdx.x;
-    const int m = a.path_len[b];
+    const int tid = threadIdx.x, lane = tid & 63, wave = tid >> 6;
     const int32_t *pb = a.path + static_cast<size_t>(b) * T;
     const int32_t *par = a.parent + static_cast<size_t>(b) * T;
+    const int row0 = chunk * CROWS;
+    const int c4 = tid & 31;    // float4 column
+    const int rsub = tid >> 5;  // rows rsub + 8 * mm
+    const size_t rs = static_cast<size_t>(H) * D;
+    const size_t base = (static_cast<size_t>(b) * T * H + h) * D;
 
-    if (tid == 0) s_bad = (m < 0 || m > T) ? -1 : INT_MAX;
+    // ---- requests that need nothing else: the path length, this thread's path entry (and the
+    // one before it), and this thread's part of S0
+    const int m = a.path_len[b];
+    const int nd = tid < T ? pb[tid] : -1;
+    const int prev = (tid > 0 && tid < T) ? pb[tid - 1] : -1;
+    const float *S0 = a.S0 + static_cast<size_t>(bh) * D * D;
+    float4 s0[4];
+#pragma unroll
+    for (int mm = 0; mm < 4; ++mm) s0[mm] = reinterpret_cast<const float4 *>(S0 + (row0 + rsub + 8 * mm) * D)[c4];
+
+    // ---- path check (positions t < m) and log alpha of the path's nodes
+    const bool lenok = m >= 0 && m <= T;
+    const bool inpath = lenok && tid < m;
+    bool ok = true;
+    double la = 0.0;
+    if (inpath) {
+        ok = nd >= 0 && nd < T;
+        if (ok) ok = par[nd] == (tid == 0 ? -1 : prev);
+        if (ok) la = log(static_cast<double>(a.alpha[(static_cast<size_t>(b) * T + nd) * H + h]));
+    }
+    if (tid == 0) s_bad = lenok ? INT_MAX : -1;
+    s_path[tid] = (inpath && ok) ? nd : 0;
+    // suffix sums of log alpha within the wave: v_t = sum_{s >= t, same wave} la_s
+    double v = la;
+#pragma unroll
+    for (int off = 1; off < 64; off <<= 1) {
+        const double t = __shfl_down(v, off, 64);
+        if (lane + off < 64) v += t;
+    }
+    if (lane == 0) s_wsum[wave] = v;
     __syncthreads();
-    if (s_bad == INT_MAX) {
-        for (int t = tid; t < m; t += 256) {
-            const int n = pb[t];
-            const bool ok = n >= 0 && n < T && par[n] == (t == 0 ? -1 : pb[t - 1]);
-            if (!ok) {
-                atomicMin(&s_bad, t + 1);
-            } else {
-                s_path[t] = n;
-                s_la[t] = log(static_cast<double>(a.alpha[(static_cast<size_t>(b) * T + n) * H + h]));
-            }
+    if (inpath && !ok) atomicMin(&s_bad, tid + 1);
+    // ---- request the first 32 path nodes' U rows and k values (they only need s_path)
+    const int nt0 = lenok ? min(CCH, m) : 0;
+    // CCH x (D/4) float4s of U and CCH x CROWS keys: four of each per thread.
+    float4 ureg[4];
+    float kreg[4];
+#pragma unroll
+    for (int q = 0; q < 4; ++q) {
+        const int x = tid + 256 * q, t = x / (D / 4), cc = x % (D / 4);
+        ureg[q] = t < nt0 ? reinterpret_cast<const float4 *>(a.U + base + s_path[t] * rs)[cc]
+                          : make_float4(0.f, 0.f, 0.f, 0.f);
+        const int tk = x / CROWS, rr = x % CROWS;
+        kreg[q] = 0.f;
+        if (tk < nt0) {
+            const size_t el = base + s_path[tk] * rs + row0 + rr;
+            kreg[q] = BF ? bf16_to_f32(static_cast<const uint16_t *>(a.k)[el]) : static_cast<const float *>(a.k)[el];
         }
     }
+    // ---- finish the suffix sums across waves: S_t = sum_{s >= t} log alpha_s;
+    // w_t = exp(S_t - log alpha_t) = Gamma_{a, path[t]}, P_a = exp(S_0)
+    for (int w2 = wave + 1; w2 < 4; ++w2) v += s_wsum[w2];
+    if (inpath) s_w[tid] = static_cast<float>(exp(v - la));
+    if (tid == 0) s_pa = static_cast<float>(exp(m > 0 && lenok ? v : 0.0));
     __syncthreads();
     const int st = (s_bad == INT_MAX) ? 0 : s_bad;
     if (a.path_status && h == 0 && chunk == 0 && tid == 0) a.path_status[b] = st;
-
-    const int row0 = chunk * CROWS;
-    const int c4 = tid & 31;   // float4 column
-    const int rsub = tid >> 5; // rows rsub + 8 * mm
     float *Sn = a.S_new + static_cast<size_t>(bh) * D * D;
     if (st != 0) {
         const float qnan = __builtin_nanf("");
 #pragma unroll
         for (int mm = 0; mm < 4; ++mm)
-            reinterpret_cast<float4 *>(Sn + (row0 + rsub + 8 * mm) * D)[c4] =
-                make_float4(qnan, qnan, qnan, qnan);
+            reinterpret_cast<float4 *>(Sn + (row0 + rsub + 8 * mm) * D)[c4] = make_float4(qnan, qnan, qnan, qnan);
         return;
     }
-
-    // Inclusive suffix sums of log alpha along the path (Hillis-Steele, m <= 256).
-    for (int off = 1; off < 256; off <<= 1) {
-        const double add = (tid < m && tid + off < m) ? s_la[tid + off] : 0.0;
-        __syncthreads();
-        if (tid < m) s_la[tid] += add;
-        __syncthreads();
-    }
-    if (tid < m) s_w[tid] = static_cast<float>(exp(tid + 1 < m ? s_la[tid + 1] : 0.0));
-    const float Pa = static_cast<float>(exp(m > 0 ? s_la[0] : 0.0));
-    __syncthreads();
-
-    const float *S0 = a.S0 + static_cast<size_t>(bh) * D * D;
+    const float Pa = s_pa;
     float4 acc[4];
 #pragma unroll
-    for (int mm = 0; mm < 4; ++mm) {
-        const float4 s = reinterpret_cast<const float4 *>(S0 + (row0 + rsub + 8 * mm) * D)[c4];
-        acc[mm] = make_float4(Pa * s.x, Pa * s.y, Pa * s.z, Pa * s.w);
-    }
-    const size_t rs = static_cast<size_t>(H) * D;
-    const size_t base = (static_cast<size_t>(b) * T * H + h) * D;
+    for (int mm = 0; mm < 4; ++mm)
+        acc[mm] = make_float4(Pa * s0[mm].x, Pa * s0[mm].y, Pa * s0[mm].z, Pa * s0[mm].w);
     for (int t0 = 0; t0 < m; t0 += CCH) {
         const int nt = min(CCH, m - t0);
-        for (int x = tid; x < nt * (D / 4); x += 256) {
-            const int t = x / (D / 4), cc = x % (D / 4);
-            s_u[t][cc] = reinterpret_cast<const float4 *>(a.U + base + s_path[t0 + t] * rs)[cc];
+        if (t0 > 0) {  // later chunks (paths longer than 32 nodes)
+#pragma unroll
+            for (int q = 0; q < 4; ++q) {
+                const int x = tid + 256 * q, t = x / (D / 4), cc = x % (D / 4);
+                ureg[q] = t < nt ? reinterpret_cast<const float4 *>(a.U + base + s_path[t0 + t] * rs)[cc]
+                                 : make_float4(0.f, 0.f, 0.f, 0.f);
+                const int tk = x / CROWS, rr = x % CROWS;
+                kreg[q] = 0.f;
+                if (tk < nt) {
+                    const size_t el = base + s_path[t0 + tk] * rs + row0 + rr;
+                    kreg[q] = BF ? bf16_to_f32(static_cast<const uint16_t *>(a.k)[el]) : static_cast<const float *>(a.k)[el];
+                }
+            }
         }
-        for (int x = tid; x < nt * CROWS; x += 256) {
-            const int t = x / CROWS, rr = x % CROWS;
-            const size_t el = base + s_path[t0 + t] * rs + row0 + rr;
-            const float kv = BF ? bf16_to_f32(static_cast<const uint16_t *>(a.k)[el])
-                                : static_cast<const float *>(a.k)[el];
-            s_kw[t][rr] = s_w[t0 + t] * kv;
+#pragma unroll
+        for (int q = 0; q < 4; ++q) {
+            const int x = tid + 256 * q;
+            s_u[x / (D / 4)][x % (D / 4)] = ureg[q];
+            const int tk = x / CROWS, rr = x % CROWS;
+            s_kw[tk][rr] = tk < nt ? s_w[t0 + tk] * kreg[q] : 0.f;
         }
         __syncthreads();
         for (int t = 0; t < nt; ++t) {

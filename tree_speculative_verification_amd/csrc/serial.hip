@@ -112,6 +112,50 @@ __global__ __launch_bounds__(64) void serial_kernel(SerialArgs a) {
     }
 }
 
+// Commit for the serial baseline: the accepted node's snapshot becomes the new state. One
+// workgroup per (sequence, head, 32 state rows), float4 copies; path checks as canopy_commit.
+__global__ __launch_bounds__(256) void serial_commit_kernel(SerialCommitArgs a) {
+    __shared__ int s_bad;
+    const int g = xcd_remap(blockIdx.x, gridDim.x);
+    const int chunk = g % 4, bh = g / 4;
+    const int H = a.H, T = a.T;
+    const int b = bh / H, h = bh % H;
+    const int tid = threadIdx.x;
+    const int m = a.path_len[b];
+    const int32_t *pb = a.path + static_cast<size_t>(b) * T;
+    const int32_t *par = a.parent + static_cast<size_t>(b) * T;
+    if (tid == 0) s_bad = (m < 0 || m > T) ? -1 : INT_MAX;
+    __syncthreads();
+    if (s_bad == INT_MAX)
+        for (int t = tid; t < m; t += 256) {
+            const int n = pb[t];
+            if (!(n >= 0 && n < T && par[n] == (t == 0 ? -1 : pb[t - 1]))) atomicMin(&s_bad, t + 1);
+        }
+    __syncthreads();
+    const int st = (s_bad == INT_MAX) ? 0 : s_bad;
+    if (a.path_status && h == 0 && chunk == 0 && tid == 0) a.path_status[b] = st;
+    const size_t SS = static_cast<size_t>(D) * D;
+    float4 *dst = reinterpret_cast<float4 *>(a.S_new + bh * SS + chunk * 32 * D);
+    if (st != 0) {
+        const float qnan = __builtin_nanf("");
+#pragma unroll
+        for (int k = 0; k < 4; ++k) dst[tid + 256 * k] = make_float4(qnan, qnan, qnan, qnan);
+        return;
+    }
+    // Valid path: its last node is in 0..T-1 (or the path is empty).
+    const float *state = (m == 0) ? a.S0 + bh * SS
+                                  : a.snap + ((static_cast<size_t>(b) * T + pb[m - 1]) * H + h) * SS;
+    const float4 *src = reinterpret_cast<const float4 *>(state + chunk * 32 * D);
+#pragma unroll
+    for (int k = 0; k < 4; ++k) dst[tid + 256 * k] = src[tid + 256 * k];
+}
+
+hipError_t launch_serial_commit(const SerialCommitArgs &a, hipStream_t stream) {
+    const dim3 grid(static_cast<unsigned>(a.B * a.H * 4)), block(256);
+    hipLaunchKernelGGL(serial_commit_kernel, grid, block, 0, stream, a);
+    return hipGetLastError();
+}
+
 hipError_t launch_serial(const SerialArgs &a, hipStream_t stream) {
     const dim3 grid(static_cast<unsigned>(a.B * a.H * (D / 16))), block(64);
     if (a.bf16)

@@ -16,12 +16,13 @@
 //   a5       O_r += sum_{c<=r} C_rc U_c (MFMA); O and U stored as fp32.
 // G is staged negated so that every coupling term accumulates with a plain MFMA.
 //
-// Data movement: each 64-node block of K and Q is copied once per workgroup from HBM into LDS
-// (16-byte loads to registers, then swizzled LDS stores), and every wave reads its MFMA
-// operands from there. The tree (parent, alpha, beta) is requested first, then block 0 of K
-// and Q, the wave's S0 columns and value rows, all before the tree preprocessing runs; the
-// next block's K, Q, V (and K_0) are requested before the current diagonal block is solved
-// and stored to LDS after it, and K_{c+1} is requested before the couplings to K_c.
+// Data movement: each 64-node block of K and Q is copied once per workgroup from HBM into a
+// swizzled LDS layout, and every wave reads its MFMA operands from there. The tree (parent,
+// alpha, beta) is requested first, then block 0 of K and Q (through registers), the wave's S0
+// columns and value rows, all before the tree preprocessing runs. The next block's K, Q
+// (and K_0) are requested with LDS-bound loads before the current diagonal block is solved,
+// and K_{c+1} before the couplings to K_c; each wave waits for its own requests before the
+// barrier that ends the pair.
 #include "canopy_prep.hpp"
 #include "canopy_kernels.hpp"
 
@@ -173,7 +174,7 @@ struct Stage<false> {
     }
 };
 
-constexpr int XS = 17;  // row stride (floats) of the per-wave 64 x 16 solve buffer
+constexpr int XS = 68;  // column stride (floats) of the per-wave 64-row x 16-column solve buffer (column-major)
 // AUTO solves a diagonal block whose in-block depth is at most this by level-scheduled row
 // substitution (a few dependent steps), deeper blocks by the 16-node sub-block substitution.
 constexpr int kLevelMaxDepth = 3;
@@ -194,7 +195,7 @@ __global__ __launch_bounds__(NW * 64) void verify_kernel(VerifyArgs a) {
     __shared__ PrepSmem<MAXT> ps;
     __shared__ float s_beta[MAXT], s_P[MAXT];
     __shared__ Stage<BF> st;
-    __shared__ float s_x[NW][64][XS];
+    __shared__ __attribute__((aligned(16))) float s_x[NW][16][XS];
     __shared__ int s_list[NW][64];
     __shared__ __attribute__((aligned(16))) uint8_t s_v[NW][64 * 16 * Op::ES];  // V rows x 16 columns
     __shared__ __attribute__((aligned(16))) uint8_t s_ka[BLK];
@@ -212,7 +213,7 @@ __global__ __launch_bounds__(NW * 64) void verify_kernel(VerifyArgs a) {
     const size_t rs = static_cast<size_t>(H) * D;                  // node stride (elements)
     const size_t base = (static_cast<size_t>(b) * T * H + h) * D;  // (b, node 0, h, col 0)
     const size_t sbase = (static_cast<size_t>(b) * T * H + h);     // (b, node 0, h) scalars
-    float(*X)[XS] = s_x[wave];
+    float(*Xc)[XS] = s_x[wave];  // Xc[column][row]
 
     // ---- loads, latency-critical first: the tree, then block 0 of K and Q, S0, V
     PrepIn<MAXT, NT> pin;
@@ -221,7 +222,7 @@ __global__ __launch_bounds__(NW * 64) void verify_kernel(VerifyArgs a) {
 #pragma unroll
     for (int t = 0; t < PrepIn<MAXT, NT>::NPT; ++t)
         bet[t] = a.beta[sbase + static_cast<size_t>(min(tid + t * NT, T - 1)) * H];
-    BC pk, pq, p0;
+    BC pk, pq;
     if constexpr (kPF) {
         pk.issue(a.k, base, rs, 0, T);
         pq.issue(a.q, base, rs, 0, T);
@@ -375,9 +376,7 @@ __global__ __launch_bounds__(NW * 64) void verify_kernel(VerifyArgs a) {
             if (c < r) {
                 // K_c is no longer needed: request K_{c+1} for the next pair of this block.
                 const bool more = c + 1 < r;
-                if constexpr (kPF) {
-                    if (more) p0.issue(a.k, base, rs, 64 * (c + 1), T);
-                }
+                if (more) dma_block<BF, NT>(s_kb, a.k, base, rs, 64 * (c + 1), T);
                 // ---- a4/a5: couplings to the solved block c
 #pragma unroll
                 for (int ti = 0; ti < 4; ++ti) {
@@ -389,21 +388,9 @@ __global__ __launch_bounds__(NW * 64) void verify_kernel(VerifyArgs a) {
                         oacc[ti] = Op::mma(cf, uf[c][ks], oacc[ti]);
                     }
                 }
-                if (more) {
-                    if constexpr (kPF) p0.commit(s_kb);
-                    else copy_block<BF, NT>(s_kb, a.k, base, rs, 64 * (c + 1), T);
-                }
+                if (more) wait_vmem();
             } else {
-                // Block r's K and Q are no longer needed: request the next block's K, Q, V and K_0.
                 const bool next = r + 1 < nb;
-                if (next) {
-                    if constexpr (kPF) {
-                        pk.issue(a.k, base, rs, 64 * (r + 1), T);
-                        pq.issue(a.q, base, rs, 64 * (r + 1), T);
-                        if (NB > 1) p0.issue(a.k, base, rs, 0, T);
-                    }
-                    pv.issue(a.v, base, rs, col0, 64 * (r + 1), T, lane);
-                }
                 // ---- a4: the diagonal block, per wave on its 16 columns
                 const int ib = 64 * r + lane;
                 uint64_t bm = 0;
@@ -444,14 +431,14 @@ __global__ __launch_bounds__(NW * 64) void verify_kernel(VerifyArgs a) {
 #pragma unroll
                         for (int ti = 0; ti < 4; ++ti)
 #pragma unroll
-                            for (int e = 0; e < 4; ++e) X[16 * ti + 4 * lg + e][lr] = z[ti][e];
+                            for (int e = 0; e < 4; ++e) Xc[lr][16 * ti + 4 * lg + e] = z[ti][e];
                         wave_lds_sync();
                         Sp zf[2];
 #pragma unroll
                         for (int ks = 0; ks < 2; ++ks) {
                             float v[8];
 #pragma unroll
-                            for (int e = 0; e < 8; ++e) v[e] = X[32 * ks + 8 * lg + e][lr];
+                            for (int e = 0; e < 8; ++e) v[e] = Xc[lr][32 * ks + 8 * lg + e];
                             zf[ks] = Op::split(v);
                         }
                         wave_lds_sync();
@@ -468,13 +455,13 @@ __global__ __launch_bounds__(NW * 64) void verify_kernel(VerifyArgs a) {
 #pragma unroll
                     for (int ti = 0; ti < 4; ++ti)
 #pragma unroll
-                        for (int e = 0; e < 4; ++e) X[16 * ti + 4 * lg + e][lr] = rhs[ti][e];
+                        for (int e = 0; e < 4; ++e) Xc[lr][16 * ti + 4 * lg + e] = rhs[ti][e];
                     wave_lds_sync();
                 } else if (use_level) {
 #pragma unroll
                     for (int ti = 0; ti < 4; ++ti)
 #pragma unroll
-                        for (int e = 0; e < 4; ++e) X[16 * ti + 4 * lg + e][lr] = rhs[ti][e];
+                        for (int e = 0; e < 4; ++e) Xc[lr][16 * ti + 4 * lg + e] = rhs[ti][e];
                     wave_lds_sync();
                     for (int L = 1; L <= maxld; ++L) {
                         const uint64_t nodes = __ballot(ld == L);
@@ -488,13 +475,13 @@ __global__ __launch_bounds__(NW * 64) void verify_kernel(VerifyArgs a) {
                                 const int ni = 64 * r + n;
                                 uint64_t am = ((static_cast<uint64_t>(ps.mask[ni][2 * r + 1]) << 32) |
                                                ps.mask[ni][2 * r]) & ~(1ull << n);
-                                float acc = X[n][lr];
+                                float acc = Xc[lr][n];
                                 while (am) {
                                     const int j = __ffsll(static_cast<unsigned long long>(am)) - 1;
                                     am &= am - 1ull;
-                                    acc += st.getG(n, j) * X[j][lr];
+                                    acc += st.getG(n, j) * Xc[lr][j];
                                 }
-                                X[n][lr] = acc;
+                                Xc[lr][n] = acc;
                             }
                         }
                         wave_lds_sync();
@@ -505,7 +492,7 @@ __global__ __launch_bounds__(NW * 64) void verify_kernel(VerifyArgs a) {
 #pragma unroll
                     for (int ti = 0; ti < 4; ++ti)
 #pragma unroll
-                        for (int e = 0; e < 4; ++e) X[16 * ti + 4 * lg + e][lr] = rhs[ti][e];
+                        for (int e = 0; e < 4; ++e) Xc[lr][16 * ti + 4 * lg + e] = rhs[ti][e];
                     wave_lds_sync();
                     // (2) U_p = (I + G_pp)^-1 (RHS_p - sum_{q<p} G_pq U_q), p = 0..3 (MFMA).
 #pragma unroll
@@ -522,16 +509,16 @@ __global__ __launch_bounds__(NW * 64) void verify_kernel(VerifyArgs a) {
                                 }
                                 float v[8];
 #pragma unroll
-                                for (int e = 0; e < 8; ++e) v[e] = X[32 * ks + 8 * lg + e][lr];
+                                for (int e = 0; e < 8; ++e) v[e] = Xc[lr][32 * ks + 8 * lg + e];
                                 acc = Op::mma(gf, Op::split(v), acc);
                             }
                         }
 #pragma unroll
-                        for (int e = 0; e < 4; ++e) X[16 * p + 4 * lg + e][lr] = acc[e];
+                        for (int e = 0; e < 4; ++e) Xc[lr][16 * p + 4 * lg + e] = acc[e];
                         wave_lds_sync();
                         float v[8];
 #pragma unroll
-                        for (int e = 0; e < 8; ++e) v[e] = (lg < 2) ? X[16 * p + 8 * lg + e][lr] : 0.f;
+                        for (int e = 0; e < 8; ++e) v[e] = (lg < 2) ? Xc[lr][16 * p + 8 * lg + e] : 0.f;
                         Sp dfr = st.fragG(16 * p + lr, 16 * p + 8 * (lg & 1));
                         if (lg >= 2) {
                             const float z8[8] = {0.f, 0.f, 0.f, 0.f, 0.f, 0.f, 0.f, 0.f};
@@ -541,15 +528,24 @@ __global__ __launch_bounds__(NW * 64) void verify_kernel(VerifyArgs a) {
                         u = Op::mma(dfr, Op::split(v), u);
                         wave_lds_sync();
 #pragma unroll
-                        for (int e = 0; e < 4; ++e) X[16 * p + 4 * lg + e][lr] = u[e];
+                        for (int e = 0; e < 4; ++e) Xc[lr][16 * p + 4 * lg + e] = u[e];
                         wave_lds_sync();
                     }
+                }
+                // Block r's K, Q and V are no longer needed and this wave writes no more LDS in
+                // this pair: request the next block's K, Q, V and K_0 now, to land during the
+                // read-out and the stores.
+                if (next) {
+                    dma_block<BF, NT>(s_ka, a.k, base, rs, 64 * (r + 1), T);
+                    dma_block<BF, NT>(s_qa, a.q, base, rs, 64 * (r + 1), T);
+                    if (NB > 1) dma_block<BF, NT>(s_kb, a.k, base, rs, 0, T);
+                    dma_v<BF>(s_v[wave], a.v, base, rs, col0, 64 * (r + 1), T, lane);
                 }
 #pragma unroll
                 for (int ks = 0; ks < 2; ++ks) {
                     float v[8];
 #pragma unroll
-                    for (int e = 0; e < 8; ++e) v[e] = X[32 * ks + 8 * lg + e][lr];
+                    for (int e = 0; e < 8; ++e) v[e] = Xc[lr][32 * ks + 8 * lg + e];
                     uf[r][ks] = Op::split(v);
                 }
 #pragma unroll
@@ -563,7 +559,7 @@ __global__ __launch_bounds__(NW * 64) void verify_kernel(VerifyArgs a) {
                 for (int m = 0; m < 16; ++m) {
                     const int rl = lg + 4 * m;
                     const int i = 64 * r + rl;
-                    if (i < T) a.U[base + static_cast<size_t>(i) * rs + col0 + lr] = X[rl][lr];
+                    if (i < T) a.U[base + static_cast<size_t>(i) * rs + col0 + lr] = Xc[lr][rl];
                 }
 #pragma unroll
                 for (int ti = 0; ti < 4; ++ti)
@@ -572,18 +568,7 @@ __global__ __launch_bounds__(NW * 64) void verify_kernel(VerifyArgs a) {
                         const int i = 64 * r + 16 * ti + 4 * lg + e;
                         if (i < T) a.O[base + static_cast<size_t>(i) * rs + col0 + lr] = oacc[ti][e];
                     }
-                if (next) {
-                    pv.commit(s_v[wave], lane);
-                    if constexpr (kPF) {
-                        pk.commit(s_ka);
-                        pq.commit(s_qa);
-                        if (NB > 1) p0.commit(s_kb);
-                    } else {
-                        copy_block<BF, NT>(s_ka, a.k, base, rs, 64 * (r + 1), T);
-                        copy_block<BF, NT>(s_qa, a.q, base, rs, 64 * (r + 1), T);
-                        if (NB > 1) copy_block<BF, NT>(s_kb, a.k, base, rs, 0, T);
-                    }
-                }
+                if (next) wait_vmem();
             }
             // The stage is free and the next operands are in LDS for every wave.
             __syncthreads();
