@@ -108,8 +108,9 @@ canopy_status canopy_tree_prep(const int32_t *parent, const float *alpha, int B,
  *   anc_mask, depth, tree_status: optional outputs (NULL to skip), as in canopy_tree_prep.
  *   solver      AUTO, FWDSUB, NEUMANN or LEVEL (see canopy_solver).
  *   waves       waves per workgroup, each owning 16 value columns (1, 2, 4 or 8), or 0 to let
- *               the library choose from B, H and T. fp32 inputs use at most 2 (a wider value
- *               is taken as 2).
+ *               the library choose from B, H and T. In the blocked kernel fp32 inputs use at
+ *               most 2 (a wider value is taken as 2); the kernel for trees of at most 16 nodes
+ *               takes any of the four.
  */
 canopy_status canopy_tree_verify(const void *q, const void *k, const void *v,
                                  const float *alpha, const float *beta, const float *S0,

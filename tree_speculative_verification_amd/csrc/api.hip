@@ -71,7 +71,7 @@ canopy_status canopy_tree_verify(const void *q, const void *k, const void *v,
     // Trees of at most 16 nodes fit one MFMA tile: AUTO and NEUMANN run the single-wave
     // register kernel (Neumann series in registers); FWDSUB and LEVEL keep the blocked kernel.
     if (T <= 16 && (solver == CANOPY_SOLVE_AUTO || solver == CANOPY_SOLVE_NEUMANN))
-        return from_hip(launch_verify_small(a, stream));
+        return from_hip(launch_verify_small(a, waves, stream));
     return from_hip(launch_verify(a, waves ? waves : pick_waves(in_dtype), stream));
 }
 

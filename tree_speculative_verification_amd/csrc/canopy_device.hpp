@@ -56,6 +56,16 @@ __device__ __forceinline__ f32x4 mfma_f32(float a, float b, f32x4 c) {
     return __builtin_amdgcn_mfma_f32_16x16x4f32(a, b, c, 0, 0, 0);
 }
 
+// v_mfma_f32_16x16x16_bf16 (and four v_mfma_f32_16x16x4_f32): a 16-long reduction in which
+// lane l supplies row (l % 16) of A and column (l % 16) of B at reduction indices
+// 4*(l/16) .. 4*(l/16)+3. That is the lane placement of the 16x16 result tile itself (rows
+// 4*(l/16) .. +3 of column l % 16), so a result tile whose rows index the next reduction feeds
+// that product as its B operand without moving data between lanes.
+typedef __attribute__((__vector_size__(4 * sizeof(short)))) short i16x4;
+__device__ __forceinline__ f32x4 mfma_bf16_k16(i16x4 a, i16x4 b, f32x4 c) {
+    return __builtin_amdgcn_mfma_f32_16x16x16bf16_1k(a, b, c, 0, 0, 0);
+}
+
 // Operand fragments: 8 consecutive reduction-index values of one row (A) or column (B).
 // bf16 inputs are exact in one bf16 fragment; fp32 data (S0, G, C, U) used with bf16 inputs is
 // split into hi + lo bf16 parts (|x - hi - lo| <= 2^-16 |x|) and multiplied in up to three
@@ -117,6 +127,23 @@ struct Ops<true> {
         c = mfma_bf16(a.hi, b.lo, c);
         return mfma_bf16(a.lo, b.hi, c);
     }
+    // 16-long reductions on fp32 data (4 values per lane, split like Sp).
+    struct Sp4 { i16x4 hi, lo; };
+    __device__ static __forceinline__ Sp4 split4(const float (&v)[4]) {
+        Sp4 s;
+#pragma unroll
+        for (int e = 0; e < 4; ++e) {
+            const __bf16 h = static_cast<__bf16>(v[e]);
+            s.hi[e] = __builtin_bit_cast(short, h);
+            s.lo[e] = __builtin_bit_cast(short, static_cast<__bf16>(v[e] - static_cast<float>(h)));
+        }
+        return s;
+    }
+    __device__ static __forceinline__ f32x4 mma16(Sp4 a, Sp4 b, f32x4 c) {
+        c = mfma_bf16_k16(a.hi, b.hi, c);
+        c = mfma_bf16_k16(a.hi, b.lo, c);
+        return mfma_bf16_k16(a.lo, b.hi, c);
+    }
 };
 
 template <>
@@ -165,6 +192,19 @@ struct Ops<false> {
     __device__ static __forceinline__ f32x4 mma(In a, In b, f32x4 c) {
 #pragma unroll
         for (int e = 0; e < 8; ++e) c = mfma_f32(a.x[e], b.x[e], c);
+        return c;
+    }
+    struct Sp4 { float x[4]; };
+    __device__ static __forceinline__ Sp4 split4(const float (&v)[4]) {
+        Sp4 s;
+#pragma unroll
+        for (int e = 0; e < 4; ++e) s.x[e] = v[e];
+        return s;
+    }
+    // Instruction e pairs value e of every lane: row r of A at index 4g+e with row 4g+e of B.
+    __device__ static __forceinline__ f32x4 mma16(Sp4 a, Sp4 b, f32x4 c) {
+#pragma unroll
+        for (int e = 0; e < 4; ++e) c = mfma_f32(a.x[e], b.x[e], c);
         return c;
     }
 };

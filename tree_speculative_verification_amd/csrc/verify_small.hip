@@ -3,68 +3,58 @@
 // general kernel (the canopy project page, "The tree closed form"), specialised to a single
 // 16-node tile:
 //   prep   pointer jumping over lanes (lane i = node i) with shuffles: ancestor mask, depth,
-//          l_i = sum of log alpha over path(i) (fp64)
+//          l_i = sum of log alpha over path(i) (fp64 sums)
 //   a2     KS = K S0, QS = Q S0 (MFMA, K and Q fragments loaded straight from global memory)
 //   a3     K K^T and K Q^T (MFMA with K as the A operand, so lane (g, r) holds row r, columns
 //          4g..4g+3), masked and decay-weighted into -G (strict ancestors) and C (path)
 //   a4     U = sum_{m=0..d} (-G)^m R, the finite Neumann series with one term per tree level
-//          (d = the tree's depth < 16), one MFMA product per term
+//          (d = the tree's depth < 16), one 16-long MFMA product per term
 //   a5     O = diag(P) QS + C U (MFMA)
-// Operand layout changes between the MFMA result order (lane (g, r): rows 4g..4g+3 of column
-// r) and the operand order (lane (g, r): row or column r at reduction indices 8g..8g+7, g < 2)
-// use lane shuffles.
+// The Gram tiles come out with row r, columns 4g..4g+3 in lane (g, r), and the node-by-column
+// tiles (R, the series terms, U) with rows 4g..4g+3 of column r in lane (g, r): exactly the A
+// and B placements of a 16-long MFMA reduction, so the series and the read-out move no data
+// between lanes. A workgroup holds NWV waves, each on its own 16 value columns of one head.
 #include "canopy_device.hpp"
 #include "canopy_kernels.hpp"
 #include <limits.h>
 
 namespace canopy {
 
-// Values of 4 consecutive rows (result order) or 4 consecutive columns (row order) per lane,
-// regrouped into 8 consecutive reduction indices for lanes g = 0, 1 (zero for g = 2, 3):
-// lane (g, r) gathers from lanes (2g, r) and (2g + 1, r).
-__device__ __forceinline__ void regroup8(const float (&x)[4], int lane, float (&v)[8]) {
-    const int r = lane & 15, g = lane >> 4;
-    const int src0 = ((2 * g) & 3) * 16 + r, src1 = ((2 * g + 1) & 3) * 16 + r;
-#pragma unroll
-    for (int e = 0; e < 4; ++e) {
-        const float a = __shfl(x[e], src0, 64);
-        const float b = __shfl(x[e], src1, 64);
-        v[e] = g < 2 ? a : 0.f;
-        v[4 + e] = g < 2 ? b : 0.f;
-    }
-}
-
-template <bool BF>
-__global__ __launch_bounds__(64) void verify_small_kernel(VerifyArgs a) {
+template <bool BF, int NWV>
+__global__ __launch_bounds__(64 * NWV) void verify_small_kernel(VerifyArgs a) {
     using Op = Ops<BF>;
     using In = typename Op::In;
     using Sp = typename Op::Sp;
     constexpr int TILES = D / 16;
+    constexpr int GROUPS = TILES / NWV;  // workgroups per head
     const int gid = xcd_remap(blockIdx.x, gridDim.x);
-    const int tile = gid % TILES;
-    const int bh = gid / TILES;
+    const int tile = (gid % GROUPS) * NWV + static_cast<int>(threadIdx.x >> 6);
+    const int bh = gid / GROUPS;
     const int H = a.H, T = a.T;
     const int b = bh / H, h = bh % H;
-    const int lane = threadIdx.x, lr = lane & 15, lg = lane >> 4;
+    const int lane = threadIdx.x & 63, lr = lane & 15, lg = lane >> 4;
     const int col0 = tile * 16;
     const size_t rs = static_cast<size_t>(H) * D;
     const size_t base = (static_cast<size_t>(b) * T * H + h) * D;
     const size_t sbase = static_cast<size_t>(b) * T * H + h;
+    const bool writer = tile == 0;  // this head's wave for the per-node outputs
 
-    // ---- every load up front: the tree and gates (lane = node), K and Q fragments
-    // (row lr), S0 fragments (column col0 + lr), V (result order)
+    // ---- every load up front, unconditional (rows and nodes past T read row or node T-1 and
+    // are masked later), so that they all issue before the first one is waited for: the tree
+    // and gates (lane = node), K and Q fragments (row lr), S0 fragments (column col0 + lr), V
+    // (result order)
     const int node = lane;
     const bool real = node < T;
-    int par = real ? a.parent[static_cast<size_t>(b) * T + node] : -1;
-    const float alpha = real ? a.alpha[sbase + static_cast<size_t>(node) * H] : 1.f;
-    const float beta = real ? a.beta[sbase + static_cast<size_t>(node) * H] : 0.f;
-    const bool rowok = lr < T;
-    const size_t erow = base + static_cast<size_t>(rowok ? lr : 0) * rs + 8 * lg;
+    const int nodec = min(node, T - 1);
+    const int par_in = a.parent[static_cast<size_t>(b) * T + nodec];
+    const float alpha_in = a.alpha[sbase + static_cast<size_t>(nodec) * H];
+    const float beta_in = a.beta[sbase + static_cast<size_t>(nodec) * H];
+    const size_t erow = base + static_cast<size_t>(min(lr, T - 1)) * rs + 8 * lg;
     In kf[4], qf[4];
 #pragma unroll
     for (int ks = 0; ks < 4; ++ks) {
-        kf[ks] = Op::template load_frag<In>(a.k, erow + 32 * ks, rowok);
-        qf[ks] = Op::template load_frag<In>(a.q, erow + 32 * ks, rowok);
+        kf[ks] = Op::template load_frag<In>(a.k, erow + 32 * ks, true);
+        qf[ks] = Op::template load_frag<In>(a.q, erow + 32 * ks, true);
     }
     float s0v[4][8];
     {
@@ -79,47 +69,42 @@ __global__ __launch_bounds__(64) void verify_small_kernel(VerifyArgs a) {
     for (int e = 0; e < 4; ++e)
         vraw[e] = Op::load_raw(a.v, base + static_cast<size_t>(min(4 * lg + e, T - 1)) * rs + col0 + lr);
 
-    // ---- prep: validation, then pointer jumping across lanes
-    const bool badn = real && (par < -1 || par >= node);
+    // ---- prep: validation, then pointer jumping across lanes. A malformed tree is computed
+    // through like a forest (bad parents read as -1) and replaced by NaN at the stores, so that
+    // no branch separates the loads from their uses.
+    const bool badn = real && (par_in < -1 || par_in >= node);
     const unsigned long long badm = __ballot(badn);
     const int bad = badm ? (__ffsll(static_cast<unsigned long long>(badm))) : 0;  // 1 + first bad node
-    if (bad) {
-        const float qnan = __builtin_nanf("");
-        for (int i = lg; i < T; i += 4) {
-            a.O[base + static_cast<size_t>(i) * rs + col0 + lr] = qnan;
-            a.U[base + static_cast<size_t>(i) * rs + col0 + lr] = qnan;
-        }
-        if (tile == 0 && real) a.ell[sbase + static_cast<size_t>(node) * H] = qnan;
-        if (tile == 0 && h == 0) {
-            if (a.tree_status && lane == 0) a.tree_status[b] = bad;
-            if (real && a.depth) a.depth[static_cast<size_t>(b) * T + node] = 0;
-            if (real && a.anc_mask) a.anc_mask[static_cast<size_t>(b) * T + node] = 0u;
-        }
-        return;
-    }
+    const float beta = real ? beta_in : 0.f;
+    // log alpha in fp32 (its error is relative to each term, so it stays relative to any
+    // difference l_i - l_j of path sums); the sums themselves in fp64.
     uint32_t mask = real ? (1u << node) : 0u;
-    double ell = real ? log(static_cast<double>(alpha)) : 0.0;
-    int jmp = real ? par : -1;
-#pragma unroll
-    for (int round = 0; round < 4; ++round) {  // 2^4 = 16 > any depth here
+    double ell = real ? static_cast<double>(logf(alpha_in)) : 0.0;
+    int jmp = (real && !badn) ? par_in : -1;
+    // After round r every node's jump pointer is 2^(r+1) levels up; depth < 16 ends it in 4.
+    for (int round = 0; round < 4 && __any(jmp >= 0); ++round) {
         const int src = jmp >= 0 ? jmp : lane;
         const uint32_t pm = __shfl(mask, src, 64);
         const double pl = __shfl(ell, src, 64);
         const int pj = __shfl(jmp, src, 64);
-        if (jmp >= 0) {
-            mask |= pm;
-            ell += pl;
-            jmp = pj;
-        }
+        const bool up = jmp >= 0;
+        mask = up ? (mask | pm) : mask;
+        ell = up ? ell + pl : ell;
+        jmp = up ? pj : jmp;
     }
-    const float P = real ? static_cast<float>(exp(ell)) : 0.f;
+    const float ellf = static_cast<float>(ell);
+    const float P = real ? expf(ellf) : 0.f;
     const int depth = real ? __popc(mask) - 1 : -1;
-    const int dmax = wave_max(depth);
-    if (tile == 0 && real) a.ell[sbase + static_cast<size_t>(node) * H] = static_cast<float>(ell);
-    if (tile == 0 && h == 0) {
-        if (a.tree_status && lane == 0) a.tree_status[b] = 0;
-        if (real && a.depth) a.depth[static_cast<size_t>(b) * T + node] = depth;
-        if (real && a.anc_mask) a.anc_mask[static_cast<size_t>(b) * T + node] = mask;
+    // Tree depth by ballots on its 4 bits (depth < 16).
+    int dmax = 0;
+#pragma unroll
+    for (int bit = 3; bit >= 0; --bit)
+        if (__any(depth >= (dmax | (1 << bit)))) dmax |= 1 << bit;
+    if (writer && real) a.ell[sbase + static_cast<size_t>(node) * H] = bad ? __builtin_nanf("") : ellf;
+    if (writer && h == 0) {
+        if (a.tree_status && lane == 0) a.tree_status[b] = bad;
+        if (real && a.depth) a.depth[static_cast<size_t>(b) * T + node] = bad ? 0 : depth;
+        if (real && a.anc_mask) a.anc_mask[static_cast<size_t>(b) * T + node] = bad ? 0u : mask;
     }
 
     // ---- a2: projections; result order: lane (lg, lr) holds rows 4lg+e of column lr
@@ -132,13 +117,15 @@ __global__ __launch_bounds__(64) void verify_small_kernel(VerifyArgs a) {
         ak = Op::mma(kf[ks], s0f[ks], ak);
         aq = Op::mma(qf[ks], s0f[ks], aq);
     }
-    float rhs[4], o0[4];
+    float rhs[4];
+    f32x4 o0;
 #pragma unroll
     for (int e = 0; e < 4; ++e) {
         const int i = 4 * lg + e;
         const float bi = __shfl(beta, i, 64), Pi = __shfl(P, i, 64);
-        rhs[e] = i < T ? bi * (Op::raw_f32(vraw[e]) - Pi * ak[e]) : 0.f;
-        o0[e] = i < T ? Pi * aq[e] : 0.f;
+        const float r = bi * (Op::raw_f32(vraw[e]) - Pi * ak[e]), o = Pi * aq[e];
+        rhs[e] = i < T ? r : 0.f;
+        o0[e] = i < T ? o : 0.f;
     }
 
     // ---- a3: Gram tile with K as the A operand: lane (lg, lr) holds row i = lr, columns
@@ -160,31 +147,23 @@ __global__ __launch_bounds__(64) void verify_small_kernel(VerifyArgs a) {
         for (int e = 0; e < 4; ++e) {
             const int j = 4 * lg + e;
             const double lj = __shfl(ell, j, 64);
-            float gv = 0.f, cv = 0.f;
-            if ((mi >> j) & 1u) {
-                const float gam = expf(static_cast<float>(li - lj));
-                cv = gam * qk[e];
-                if (i != j) gv = -bi * gam * kk[e];
-            }
-            gneg[e] = gv;
-            cm[e] = cv;
+            // Off the path the exponent may overflow; the selects drop those entries.
+            const float gam = expf(static_cast<float>(li - lj));
+            const bool onpath = (mi >> j) & 1u;
+            cm[e] = onpath ? gam * qk[e] : 0.f;
+            gneg[e] = (onpath && i != j) ? -bi * gam * kk[e] : 0.f;
         }
     }
-    float gv8[8], cv8[8];
-    regroup8(gneg, lane, gv8);  // A operand: row lr, reduction index = column j
-    regroup8(cm, lane, cv8);
-    const Sp gf = Op::split(gv8);
-    const Sp cf = Op::split(cv8);
+    const typename Op::Sp4 gf = Op::split4(gneg);
+    const typename Op::Sp4 cf = Op::split4(cm);
 
-    // ---- a4: U = sum_{m=0..dmax} (-G)^m R; Z in result order, regrouped as a B operand
+    // ---- a4: U = sum_{m=0..dmax} (-G)^m R; each term in result order is the next B operand
     float u[4], z[4];
 #pragma unroll
     for (int e = 0; e < 4; ++e) u[e] = z[e] = rhs[e];
     for (int m = 1; m <= dmax; ++m) {
-        float zv[8];
-        regroup8(z, lane, zv);
         f32x4 nz = {0.f, 0.f, 0.f, 0.f};
-        nz = Op::mma(gf, Op::split(zv), nz);
+        nz = Op::mma16(gf, Op::split4(z), nz);
 #pragma unroll
         for (int e = 0; e < 4; ++e) {
             z[e] = nz[e];
@@ -192,28 +171,46 @@ __global__ __launch_bounds__(64) void verify_small_kernel(VerifyArgs a) {
         }
     }
     // ---- a5: O = diag(P) QS + C U
-    float uv[8];
-    regroup8(u, lane, uv);
-    f32x4 oc = {o0[0], o0[1], o0[2], o0[3]};
-    oc = Op::mma(cf, Op::split(uv), oc);
+    const f32x4 oc = Op::mma16(cf, Op::split4(u), o0);
 
-    // ---- a6: outputs
+    // ---- a6: outputs (NaN for a malformed tree)
+    const float qnan = __builtin_nanf("");
 #pragma unroll
     for (int e = 0; e < 4; ++e) {
         const int i = 4 * lg + e;
         if (i < T) {
-            a.U[base + static_cast<size_t>(i) * rs + col0 + lr] = u[e];
-            a.O[base + static_cast<size_t>(i) * rs + col0 + lr] = oc[e];
+            a.U[base + static_cast<size_t>(i) * rs + col0 + lr] = bad ? qnan : u[e];
+            a.O[base + static_cast<size_t>(i) * rs + col0 + lr] = bad ? qnan : oc[e];
         }
     }
 }
 
-hipError_t launch_verify_small(const VerifyArgs &a, hipStream_t stream) {
-    const dim3 grid(static_cast<unsigned>(a.B * a.H * (D / 16))), block(64);
+template <bool BF>
+static void launch_small_nwv(const VerifyArgs &a, int nwv, hipStream_t stream) {
+    const unsigned heads = static_cast<unsigned>(a.B * a.H);
+    switch (nwv) {
+        case 1:
+            hipLaunchKernelGGL((verify_small_kernel<BF, 1>), dim3(heads * 8), dim3(64), 0, stream, a);
+            break;
+        case 2:
+            hipLaunchKernelGGL((verify_small_kernel<BF, 2>), dim3(heads * 4), dim3(128), 0, stream, a);
+            break;
+        case 4:
+            hipLaunchKernelGGL((verify_small_kernel<BF, 4>), dim3(heads * 2), dim3(256), 0, stream, a);
+            break;
+        default:
+            hipLaunchKernelGGL((verify_small_kernel<BF, 8>), dim3(heads), dim3(512), 0, stream, a);
+            break;
+    }
+}
+
+// waves: waves per workgroup (1, 2, 4 or 8; 0 picks the default).
+hipError_t launch_verify_small(const VerifyArgs &a, int waves, hipStream_t stream) {
+    const int nwv = waves == 0 ? 1 : waves;
     if (a.bf16)
-        hipLaunchKernelGGL(verify_small_kernel<true>, grid, block, 0, stream, a);
+        launch_small_nwv<true>(a, nwv, stream);
     else
-        hipLaunchKernelGGL(verify_small_kernel<false>, grid, block, 0, stream, a);
+        launch_small_nwv<false>(a, nwv, stream);
     return hipGetLastError();
 }
 
