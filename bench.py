@@ -16,6 +16,8 @@ top-k tree (root, 3 children, 4 children each), bf16 q/k/v, fp32 state.
 from __future__ import annotations
 
 import argparse
+import csv
+import hashlib
 import json
 import os
 import sys
@@ -28,6 +30,10 @@ if ROOT not in sys.path:
 METRIC = "µs per GDN layer tree-verify (+nodes/s) at B=1/16, T=16-256; % HBM/MFMA peak"
 HBM_PEAK_GBS = 8000.0         # MI355X HBM3E
 BF16_PEAK_TFLOPS = 2500.0     # MI355X dense bf16 MFMA
+# HBM bytes per launch measured with rocprofv3 --pmc (FETCH_SIZE, WRITE_SIZE), keyed by the
+# digest of the kernel sources they were taken on; ignored once the sources have changed.
+TRAFFIC_FILE = os.path.join(ROOT, "profiles", "hbm_traffic.json")
+KERNEL_SOURCE_DIR = os.path.join(ROOT, "tree_speculative_verification_amd", "csrc")
 
 WORKLOADS = {
     "binary7_fp32": dict(B=1, H=2, T=7, tree="binary7", dtype="fp32", seed=0,
@@ -57,6 +63,97 @@ def commit_bytes(B, H, m_total):
     """S0 read and S_new written per (sequence, head), plus k (bf16) and U rows and alpha of
     the path nodes (m_total path nodes summed over sequences), plus the path arrays."""
     return B * H * 2 * 128 * 128 * 4 + m_total * H * (128 * 2 + 128 * 4 + 4) + m_total * 8
+
+
+def verify_flops(B, H, T):
+    """Algorithmic matrix flops of one verify launch, counting the Gram, solve and read-out
+    matrices as dense lower triangles (a tree's ancestor pattern is sparser): per (sequence,
+    head) the projections K S0 and Q S0 (4 T d^2), the strict and inclusive Gram triangles
+    (2 d T^2 together), the triangular solve and the C U read-out (2 d T^2 together)."""
+    d = 128
+    return B * H * (4 * T * d * d + 4 * d * T * T)
+
+
+def verify_kernel_name(T, solver):
+    """The kernel canopy_tree_verify launches for this size and solver."""
+    return "verify_small_kernel" if T <= 16 and solver in ("auto", "neumann") else "verify_kernel"
+
+
+def kernel_digest():
+    """Digest of the device code (every HIP source and header but the host-side C ABI file):
+    identifies the kernels a profile was taken on."""
+    h = hashlib.sha256()
+    for f in sorted(os.listdir(KERNEL_SOURCE_DIR)):
+        if f.endswith((".hip", ".hpp")) and f != "api.hip":
+            h.update(f.encode())
+            with open(os.path.join(KERNEL_SOURCE_DIR, f), "rb") as fh:
+                h.update(fh.read())
+    return h.hexdigest()[:16]
+
+
+def measured_traffic(workload, solver, waves):
+    """HBM bytes per verify launch from the committed counter summary, or None if there is
+    none for this configuration or the kernels have changed since it was taken."""
+    try:
+        with open(TRAFFIC_FILE) as fh:
+            data = json.load(fh)
+    except (OSError, ValueError):
+        return None
+    if data.get("kernel_digest") != kernel_digest():
+        return None
+    ent = data.get("workloads", {}).get(f"{workload}:{solver}:{waves}")
+    return None if ent is None else ent["verify"]["hbm_bytes_per_launch"]
+
+
+def pmc_summary(run_dir, out_path):
+    """Turn rocprofv3 --pmc runs of bench.py (one per counter and workload, each with
+    --copy-probe) into the per-launch HBM traffic summary. FETCH_SIZE and WRITE_SIZE (KiB per
+    dispatch) are scaled by what the same counter reads for the probe's plain copy of known
+    size."""
+    def per_kernel(path):
+        acc = {}
+        with open(path) as fh:
+            for r in csv.DictReader(fh):
+                acc.setdefault(r["Kernel_Name"], []).append(float(r["Counter_Value"]))
+        return acc
+
+    out = {"kernel_digest": None, "workloads": {}, "note": (
+        "HBM bytes per launch = FETCH_SIZE KiB x 1024 x fetch_scale + WRITE_SIZE KiB x 1024 x "
+        "write_scale, each scale = probe copy bytes / what the counter reads for that copy")}
+    for name in sorted(os.listdir(run_dir)):
+        if not name.startswith("pmc_FETCH_SIZE_") or not os.path.isdir(os.path.join(run_dir, name)):
+            continue
+        tag = name[len("pmc_FETCH_SIZE_"):]
+        fdir, wdir = os.path.join(run_dir, name), os.path.join(run_dir, "pmc_WRITE_SIZE_" + tag)
+        with open(fdir + ".log") as fh:
+            line = next(l for l in fh if l.startswith("{"))
+        rec = json.loads(line)
+        probe = rec["config"]["copy_probe_bytes"]
+        if out["kernel_digest"] is None:
+            out["kernel_digest"] = rec["kernel_digest"]
+        elif out["kernel_digest"] != rec["kernel_digest"]:
+            raise RuntimeError(f"{tag}: counters taken on different kernel sources")
+        f = per_kernel(os.path.join(fdir, "run_counter_collection.csv"))
+        w = per_kernel(os.path.join(wdir, "run_counter_collection.csv"))
+        fscale = probe / 1024.0 / max(f["__amd_rocclr_copyBuffer"])
+        wscale = probe / 1024.0 / max(w["__amd_rocclr_copyBuffer"])
+        ent = {"config": rec["config"], "fetch_scale": round(fscale, 4), "write_scale": round(wscale, 4)}
+        for kname, role in ((rec["roofline"]["kernel"], "verify"), ("commit_kernel", "commit")):
+            kf = [k for k in f if f"canopy::{kname}<" in k]
+            if len(kf) != 1:
+                raise RuntimeError(f"{tag}: expected one {kname} in the counters, found {kf}")
+            fk = sum(f[kf[0]]) / len(f[kf[0]])
+            wk = sum(w[kf[0]]) / len(w[kf[0]])
+            ent[role] = {"kernel": kf[0], "fetch_kib": round(fk, 1), "write_kib": round(wk, 1),
+                         "hbm_bytes_per_launch": int(round(fk * 1024 * fscale + wk * 1024 * wscale))}
+        ent["verify"]["algorithmic_bytes"] = rec["roofline"]["algorithmic_bytes"]
+        key = f"{rec['config']['workload_key']}:{rec['config']['solver']}:{rec['config']['waves']}"
+        out["workloads"][key] = ent
+    with open(out_path, "w") as fh:
+        json.dump(out, fh, indent=1, sort_keys=True)
+        fh.write("\n")
+    print(json.dumps(out, indent=1, sort_keys=True))
+    return 0
 
 
 def build_inputs(wl):
@@ -301,7 +398,12 @@ def main(argv=None):
     ap.add_argument("--copy-probe", type=int, default=0, metavar="BYTES",
                     help="also run one plain device-to-device copy of this many bytes (a known "
                          "traffic reference for hardware counters)")
+    ap.add_argument("--pmc-summary", default="", metavar="DIR",
+                    help="summarise rocprofv3 --pmc runs found in DIR into the HBM traffic file "
+                         "(no GPU work)")
     args = ap.parse_args(argv)
+    if args.pmc_summary:
+        return pmc_summary(args.pmc_summary, args.out or TRAFFIC_FILE)
 
     if args.gpus != 1 or int(os.environ.get("WORLD_SIZE", "1")) != 1:
         print("bench.py measures one GPU only: the verify and commit kernels shard by (sequence, "
@@ -384,6 +486,8 @@ def main(argv=None):
 
     vbytes = verify_bytes(B, H, T, dt)
     achieved = vbytes / (us_verify * 1e-6) / 1e9
+    vflops = verify_flops(B, H, T)
+    tflops = vflops / (us_verify * 1e-6) / 1e12
     out = {
         "metric": METRIC,
         "value": round(us_step, 3),
@@ -397,18 +501,25 @@ def main(argv=None):
         "vs_baseline": None,
         "dtype": "bf16" if dt == "bf16" else "fp32",
         "data": "synthetic",
-        "config": {"workload": wl["desc"], "B": B, "H": H, "T": T, "dk": 128, "dv": 128,
-                   "tree": wl["tree"], "solver": args.solver, "waves": args.waves,
-                   "step": "verify + commit of a random root-to-leaf path",
-                   "launch": "eager" if args.eager else "hip graph of all timed steps"},
+        "config": {"workload": wl["desc"], "workload_key": args.workload, "B": B, "H": H, "T": T,
+                   "dk": 128, "dv": 128, "tree": wl["tree"], "solver": args.solver,
+                   "waves": args.waves, "step": "verify + commit of a random root-to-leaf path",
+                   "launch": "eager" if args.eager else "hip graph of all timed steps",
+                   "copy_probe_bytes": args.copy_probe},
         "nodes_per_s": round(B * T / (us_step * 1e-6), 1),
         "verify_us": round(us_verify, 3),
         "verify_nodes_per_s": round(B * T / (us_verify * 1e-6), 1),
         "commit_us": round(us_commit, 3),
         "serial_verify_us": None if us_serial is None else round(us_serial, 3),
-        "roofline": {"bound": "hbm", "kernel": "verify_kernel", "achieved": round(achieved, 2),
-                     "peak": HBM_PEAK_GBS, "unit": "GB/s", "frac": round(achieved / HBM_PEAK_GBS, 5),
-                     "traffic": None, "algorithmic_bytes": vbytes},
+        "roofline": {"bound": "hbm", "kernel": verify_kernel_name(T, args.solver),
+                     "achieved": round(achieved, 2), "peak": HBM_PEAK_GBS, "unit": "GB/s",
+                     "frac": round(achieved / HBM_PEAK_GBS, 5),
+                     "traffic": measured_traffic(args.workload, args.solver, args.waves),
+                     "algorithmic_bytes": vbytes},
+        "mfma": {"flops_per_launch": vflops, "achieved_tflops": round(tflops, 2),
+                 "peak_tflops": BF16_PEAK_TFLOPS, "frac": round(tflops / BF16_PEAK_TFLOPS, 5),
+                 "note": "algorithmic dense-triangle flops of the verify launch"},
+        "kernel_digest": kernel_digest(),
     }
     if not args.no_cpu:
         out["cpu_baseline"] = cpu_baseline(inp, args.cpu_budget)

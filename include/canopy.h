@@ -20,7 +20,8 @@
  *    caller. The library keeps no pointer after a call returns and allocates nothing.
  *  - Calls only enqueue work on `stream` (0 = the null stream) and return; they do not
  *    synchronise. Inputs are read-only; outputs are fully overwritten.
- *  - d_k = d_v = 128. 1 <= T <= 256. B >= 1, H >= 1. q, k and v all have H heads.
+ *  - d_k = d_v = 128. 1 <= T <= 256. B >= 1, H >= 1, B * H * 256 <= INT_MAX. q, k and v all
+ *    have H heads.
  *  - Node order is the caller's: node i's outputs sit at index i. parent[b,0] must be -1 and
  *    -1 <= parent[b,i] < i; further roots (parent -1) start from S0 too.
  *  - The scale on q is 1 (callers that want 1/sqrt(d_k) pre-scale q).

@@ -7,7 +7,12 @@ using namespace canopy;
 
 namespace {
 
-bool sizes_ok(int B, int H, int T) { return B >= 1 && H >= 1 && T >= 1 && T <= 256; }
+// Grids have up to B*H*8 workgroups and index arithmetic on (b, h) pairs is 32-bit: keep
+// B*H*256 within int range.
+bool sizes_ok(int B, int H, int T) {
+    return B >= 1 && H >= 1 && T >= 1 && T <= 256 &&
+           static_cast<long long>(B) * H * 256 <= 2147483647LL;
+}
 
 canopy_status from_hip(hipError_t e) { return e == hipSuccess ? CANOPY_OK : CANOPY_ERR_HIP; }
 
