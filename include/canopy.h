@@ -53,20 +53,21 @@ typedef enum {
 typedef enum { CANOPY_FP32 = 0, CANOPY_BF16 = 1 } canopy_dtype;
 
 /* How the unit lower-triangular system (I + G) U = R is solved ("Design decisions / Two solve
- * strategies"; "The tree closed form" for the Neumann series and the level-synchronous solve).
- * All work on 64-node blocks staged in LDS, the couplings to earlier blocks applied as
- * matrix-core products; they differ in how a diagonal block is solved:
- *   FWDSUB   forward substitution over four 16-node sub-blocks: every 16 x 16 diagonal
- *            sub-block is inverted by substitution and applied on the matrix cores, the
- *            couplings between sub-blocks too. Its cost does not depend on the tree's depth.
- *   NEUMANN  the finite series sum_{m=0..d} (-G_bb)^m, d the block's in-block depth, one
- *            matrix-core product per term (for T <= 64: the whole tree's Neumann series with
- *            one term per tree level).
- *   LEVEL    row-by-row substitution with the rows of equal in-block depth solved together.
- *   AUTO     LEVEL for blocks of in-block depth <= 3, FWDSUB otherwise.
- * Trees of at most 16 nodes fit one matrix-core tile: there AUTO and NEUMANN run a single-wave
- * kernel that keeps everything in registers and sums the Neumann series (one term per tree
- * level); FWDSUB and LEVEL run the blocked kernel. */
+ * strategies"; "The tree closed form" for the Neumann series, its squaring form and the
+ * level-synchronous solve). Three kernels serve the sizes:
+ *  - T <= 16 (AUTO, NEUMANN): one wave per 16 value columns, all in registers; the Neumann
+ *    series with one term per tree level.
+ *  - 17 <= T <= 64 (AUTO, FWDSUB, NEUMANN): one wave per 16-node sub-block. FWDSUB and AUTO
+ *    substitute forward over the sub-blocks, each 16 x 16 diagonal inverse formed as the
+ *    squaring product (I + N)(I + N^2)(I + N^4)(I + N^8), N = -G_pp, truncated at the
+ *    sub-block's depth; NEUMANN sums the whole tree's series, one term per tree level.
+ *  - Otherwise, and for LEVEL: 64-node blocks staged in LDS, the couplings to earlier blocks
+ *    applied as matrix-core products; a diagonal block is solved by
+ *      FWDSUB   forward substitution over four 16-node sub-blocks, each 16 x 16 diagonal
+ *               sub-block inverted by substitution and applied on the matrix cores;
+ *      NEUMANN  the finite series sum_{m=0..d} (-G_bb)^m, d the block's in-block depth;
+ *      LEVEL    row-by-row substitution with the rows of equal in-block depth together;
+ *      AUTO     LEVEL for blocks of in-block depth <= 3, FWDSUB otherwise. */
 typedef enum {
     CANOPY_SOLVE_AUTO = 0,
     CANOPY_SOLVE_FWDSUB = 1,
@@ -108,10 +109,11 @@ canopy_status canopy_tree_prep(const int32_t *parent, const float *alpha, int B,
  *   ell         [B,T,H] fp32, out: as in canopy_tree_prep.
  *   anc_mask, depth, tree_status: optional outputs (NULL to skip), as in canopy_tree_prep.
  *   solver      AUTO, FWDSUB, NEUMANN or LEVEL (see canopy_solver).
- *   waves       waves per workgroup, each owning 16 value columns (1, 2, 4 or 8), or 0 to let
- *               the library choose from B, H and T. In the blocked kernel fp32 inputs use at
- *               most 2 (a wider value is taken as 2); the kernel for trees of at most 16 nodes
- *               takes any of the four.
+ *   waves       workgroup width, 1, 2, 4 or 8, or 0 to let the library choose from B, H and T.
+ *               T <= 16 (AUTO, NEUMANN): waves per workgroup, each owning 16 value columns.
+ *               17 <= T <= 64 (AUTO, FWDSUB, NEUMANN): 16-column tiles per workgroup, whose
+ *               waves each own 16 nodes (8 is taken as 4). Otherwise (the blocked kernel):
+ *               waves per workgroup, each owning 16 value columns; fp32 inputs use at most 2.
  */
 canopy_status canopy_tree_verify(const void *q, const void *k, const void *v,
                                  const float *alpha, const float *beta, const float *S0,

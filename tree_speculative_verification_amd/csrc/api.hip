@@ -74,9 +74,13 @@ canopy_status canopy_tree_verify(const void *q, const void *k, const void *v,
     a.O = O; a.U = U; a.ell = ell;
     a.anc_mask = anc_mask; a.depth = depth; a.tree_status = tree_status;
     // Trees of at most 16 nodes fit one MFMA tile: AUTO and NEUMANN run the single-wave
-    // register kernel (Neumann series in registers); FWDSUB and LEVEL keep the blocked kernel.
+    // register kernel (Neumann series in registers). Trees of 17 to 64 nodes run the
+    // wave-per-sub-block kernel for AUTO, FWDSUB and NEUMANN. Everything else (LEVEL, and
+    // FWDSUB at T <= 16) runs the blocked LDS kernel, which serves any T <= 256.
     if (T <= 16 && (solver == CANOPY_SOLVE_AUTO || solver == CANOPY_SOLVE_NEUMANN))
         return from_hip(launch_verify_small(a, waves, stream));
+    if (T > 16 && T <= 64 && solver != CANOPY_SOLVE_LEVEL)
+        return from_hip(launch_verify_mid(a, waves == 8 ? 4 : waves, stream));
     return from_hip(launch_verify(a, waves ? waves : pick_waves(in_dtype), stream));
 }
 

@@ -66,6 +66,20 @@ __device__ __forceinline__ f32x4 mfma_bf16_k16(i16x4 a, i16x4 b, f32x4 c) {
     return __builtin_amdgcn_mfma_f32_16x16x16bf16_1k(a, b, c, 0, 0, 0);
 }
 
+// The same 16-long reduction on fp32 data with exact products: four v_mfma_f32_16x16x4_f32,
+// instruction e pairing value e of every lane (row r of A at index 4g+e with row 4g+e of B).
+// Operands computed on the VALU feed it directly, with no bf16 splitting.
+__device__ __forceinline__ f32x4 mma16f(const float (&a)[4], const float (&b)[4], f32x4 c) {
+#pragma unroll
+    for (int e = 0; e < 4; ++e) c = mfma_f32(a[e], b[e], c);
+    return c;
+}
+__device__ __forceinline__ f32x4 mma16f(const float (&a)[4], f32x4 b, f32x4 c) {
+#pragma unroll
+    for (int e = 0; e < 4; ++e) c = mfma_f32(a[e], b[e], c);
+    return c;
+}
+
 // Operand fragments: 8 consecutive reduction-index values of one row (A) or column (B).
 // bf16 inputs are exact in one bf16 fragment; fp32 data (S0, G, C, U) used with bf16 inputs is
 // split into hi + lo bf16 parts (|x - hi - lo| <= 2^-16 |x|) and multiplied in up to three
@@ -106,6 +120,11 @@ struct Ops<true> {
         r.x = __builtin_bit_cast(bf16x8, *reinterpret_cast<const uint4 *>(
                                              buf + row * ROWB + ((g8 ^ (row & 15)) << 4)));
         return r;
+    }
+    // The inverse of lds_frag: store a fragment into the swizzled row layout.
+    __device__ static __forceinline__ void lds_put(uint8_t *buf, int row, int g8, In f) {
+        *reinterpret_cast<u32x4 *>(buf + row * ROWB + ((g8 ^ (row & 15)) << 4)) =
+            __builtin_bit_cast(u32x4, f.x);
     }
     __device__ static __forceinline__ Sp split(const float (&v)[8]) {
         Sp s;
@@ -182,6 +201,11 @@ struct Ops<false> {
         r.x[0] = a.x; r.x[1] = a.y; r.x[2] = a.z; r.x[3] = a.w;
         r.x[4] = b.x; r.x[5] = b.y; r.x[6] = b.z; r.x[7] = b.w;
         return r;
+    }
+    __device__ static __forceinline__ void lds_put(uint8_t *buf, int row, int g8, In f) {
+        uint8_t *p = buf + row * ROWB;
+        *reinterpret_cast<float4 *>(p + (((2 * g8) ^ (row & 15)) << 4)) = make_float4(f.x[0], f.x[1], f.x[2], f.x[3]);
+        *reinterpret_cast<float4 *>(p + (((2 * g8 + 1) ^ (row & 15)) << 4)) = make_float4(f.x[4], f.x[5], f.x[6], f.x[7]);
     }
     __device__ static __forceinline__ Sp split(const float (&v)[8]) {
         Sp s;
