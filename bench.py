@@ -76,7 +76,11 @@ def verify_flops(B, H, T):
 
 def verify_kernel_name(T, solver):
     """The kernel canopy_tree_verify launches for this size and solver."""
-    return "verify_small_kernel" if T <= 16 and solver in ("auto", "neumann") else "verify_kernel"
+    if T <= 16 and solver in ("auto", "neumann"):
+        return "verify_small_kernel"
+    if 16 < T <= 64 and solver != "level":
+        return "verify_mid_kernel"
+    return "verify_kernel"
 
 
 def kernel_digest():
@@ -138,10 +142,10 @@ def pmc_summary(run_dir, out_path):
         fscale = probe / 1024.0 / max(f["__amd_rocclr_copyBuffer"])
         wscale = probe / 1024.0 / max(w["__amd_rocclr_copyBuffer"])
         ent = {"config": rec["config"], "fetch_scale": round(fscale, 4), "write_scale": round(wscale, 4)}
-        for kname, role in ((rec["roofline"]["kernel"], "verify"), ("commit_kernel", "commit")):
-            kf = [k for k in f if f"canopy::{kname}<" in k]
+        for prefix, role in (("canopy::verify", "verify"), ("canopy::commit_kernel<", "commit")):
+            kf = [k for k in f if k.startswith("void " + prefix)]
             if len(kf) != 1:
-                raise RuntimeError(f"{tag}: expected one {kname} in the counters, found {kf}")
+                raise RuntimeError(f"{tag}: expected one {prefix} kernel in the counters, found {kf}")
             fk = sum(f[kf[0]]) / len(f[kf[0]])
             wk = sum(w[kf[0]]) / len(w[kf[0]])
             ent[role] = {"kernel": kf[0], "fetch_kib": round(fk, 1), "write_kib": round(wk, 1),
