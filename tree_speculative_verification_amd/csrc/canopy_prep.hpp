@@ -1,8 +1,6 @@
 // Tree preprocessing inside one workgroup: validation, inclusive ancestor bitmask, depth and
 // the log cumulative decay l_i = log alpha_i + l_parent(i) ("The tree closed form" on the
-// canopy project page). Pointer jumping: after round r every node knows the union of the
-// masks and the sum of log alpha over the next 2^r nodes of its root path, so ceil(log2(d+1))
-// rounds cover a tree of depth d.
+// canopy project page).
 #pragma once
 #include "canopy_device.hpp"
 #include <limits.h>
@@ -39,72 +37,73 @@ struct PrepIn {
 
 // All NT threads of the block call this. Returns 0 for a valid tree, else 1 + the first node
 // whose parent lies outside -1..i-1 (the block's result is then undefined apart from that).
+//
+// The nodes are cut into 64-node chunks, one wave (one lane per node) per chunk at a time.
+// Inside a chunk, pointer jumping over lane shuffles gathers, for every node, the mask bits,
+// the log-decay sum and the exit (the first ancestor outside the chunk, -1 for none) of its
+// in-chunk root path; after round r a jump pointer is 2^(r+1) levels up, so ceil(log2(d+1))
+// rounds cover an in-chunk depth d. Parents precede children, so every exit lies in an earlier
+// chunk: the chunks are then completed in order, each node taking its exit's full mask words
+// and log-decay sum.
 template <int MAXT, int NT>
 __device__ int tree_prep_compute(PrepSmem<MAXT> &s, const PrepIn<MAXT, NT> &in, int T) {
     constexpr int MW = MAXT / 32;
     constexpr int NPT = PrepIn<MAXT, NT>::NPT;
-    const int tid = threadIdx.x;
+    constexpr int NW = NT / 64;
+    constexpr int NCH = MAXT / 64;
+    const int tid = threadIdx.x, lane = tid & 63, wave = tid >> 6;
     if (tid == 0) s.bad = INT_MAX;
     __syncthreads();
 #pragma unroll
     for (int t = 0; t < NPT; ++t) {
-        const int i = tid + t * NT;
-        if (i < MAXT) {
-            int p = -1;
-            double l = 0.0;
-            if (i < T) {
-                p = in.p[t];
-                if (p < -1 || p >= i) {
-                    atomicMin(&s.bad, i + 1);
-                    p = -1;
-                }
-                l = log(static_cast<double>(in.al[t]));
-            }
-            s.jump[i] = p;
-            s.ell[i] = l;
-#pragma unroll
-            for (int w = 0; w < MW; ++w)
-                s.mask[i][w] = (i < T && w == (i >> 5)) ? (1u << (i & 31)) : 0u;
+        const int c = wave + t * NW;  // the chunk of node tid + t * NT
+        if (c >= NCH) continue;
+        const int i = 64 * c + lane;
+        const bool real = i < T;
+        int p = real ? in.p[t] : -1;
+        if (real && (p < -1 || p >= i)) {
+            atomicMin(&s.bad, i + 1);
+            p = -1;
         }
+        unsigned long long m = real ? (1ull << lane) : 0ull;
+        double l = real ? log(static_cast<double>(in.al[t])) : 0.0;
+        const bool inside = p >= 64 * c;
+        int jmp = inside ? p - 64 * c : -1;
+        int ex = inside ? -1 : p;  // set again from the in-chunk root when the jumps reach it
+        for (int round = 0; round < 6 && __any(jmp >= 0); ++round) {
+            const int src = jmp >= 0 ? jmp : lane;
+            const unsigned long long pm = __shfl(m, src, 64);
+            const double pl = __shfl(l, src, 64);
+            const int pj = __shfl(jmp, src, 64);
+            const int pe = __shfl(ex, src, 64);
+            const bool up = jmp >= 0;
+            m = up ? (m | pm) : m;
+            l = up ? l + pl : l;
+            ex = up ? pe : ex;
+            jmp = up ? pj : jmp;
+        }
+        s.jump[i] = ex;
+        s.ell[i] = l;
+#pragma unroll
+        for (int w = 0; w < MW; ++w)
+            s.mask[i][w] = w == 2 * c ? static_cast<uint32_t>(m)
+                                      : (w == 2 * c + 1 ? static_cast<uint32_t>(m >> 32) : 0u);
     }
     __syncthreads();
     if (s.bad != INT_MAX) return s.bad;
-
-    for (int round = 0; round < 10; ++round) {
-        uint32_t nm[NPT][MW];
-        double nl[NPT];
-        int nj[NPT];
-        int more = 0;
 #pragma unroll
-        for (int t = 0; t < NPT; ++t) {
-            const int i = tid + t * NT;
-            if (i < MAXT) {
-                const int j = s.jump[i];
-                nl[t] = s.ell[i];
-                nj[t] = j;
+    for (int c = 1; c < NCH; ++c) {
+        if (64 * c >= T) break;
+        if (wave == c % NW) {
+            const int i = 64 * c + lane;
+            const int e = s.jump[i];
+            if (e >= 0) {
 #pragma unroll
-                for (int w = 0; w < MW; ++w) nm[t][w] = s.mask[i][w];
-                if (j >= 0) {
-                    nl[t] += s.ell[j];
-                    nj[t] = s.jump[j];
-#pragma unroll
-                    for (int w = 0; w < MW; ++w) nm[t][w] |= s.mask[j][w];
-                }
-                more |= (nj[t] >= 0);
+                for (int w = 0; w < 2 * c; ++w) s.mask[i][w] = s.mask[e][w];
+                s.ell[i] += s.ell[e];
             }
         }
         __syncthreads();
-#pragma unroll
-        for (int t = 0; t < NPT; ++t) {
-            const int i = tid + t * NT;
-            if (i < MAXT) {
-                s.jump[i] = nj[t];
-                s.ell[i] = nl[t];
-#pragma unroll
-                for (int w = 0; w < MW; ++w) s.mask[i][w] = nm[t][w];
-            }
-        }
-        if (!__syncthreads_or(more)) break;
     }
     return 0;
 }

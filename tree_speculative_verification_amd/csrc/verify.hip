@@ -73,6 +73,21 @@ struct Stage<true> {
         *reinterpret_cast<uint2 *>(ch + o) = pack(ch4);
         *reinterpret_cast<uint2 *>(cl + o) = pack(cl4);
     }
+    // G alone at row r, columns c0 .. c0+3.
+    __device__ __forceinline__ void store4G(int r, int c0, const float (&g)[4]) {
+        uint16_t gh4[4], gl4[4];
+#pragma unroll
+        for (int e = 0; e < 4; ++e) {
+            const __bf16 g1 = static_cast<__bf16>(g[e]);
+            gh4[e] = __builtin_bit_cast(uint16_t, g1);
+            gl4[e] = __builtin_bit_cast(uint16_t, static_cast<__bf16>(g[e] - static_cast<float>(g1)));
+        }
+        const int o = off(r, c0);
+        *reinterpret_cast<uint2 *>(gh + o) =
+            make_uint2(gh4[0] | (static_cast<uint32_t>(gh4[1]) << 16), gh4[2] | (static_cast<uint32_t>(gh4[3]) << 16));
+        *reinterpret_cast<uint2 *>(gl + o) =
+            make_uint2(gl4[0] | (static_cast<uint32_t>(gl4[1]) << 16), gl4[2] | (static_cast<uint32_t>(gl4[3]) << 16));
+    }
     // Zero the 16 x 16 tile at (r0, c0) of all four arrays: 128 chunks, two per lane.
     __device__ __forceinline__ void zero_tile(int r0, int c0, int lane) {
 #pragma unroll
@@ -138,6 +153,9 @@ struct Stage<false> {
         const int o = off(r, c0);
         *reinterpret_cast<float4 *>(g + o) = make_float4(gv[0], gv[1], gv[2], gv[3]);
         *reinterpret_cast<float4 *>(c + o) = make_float4(cv[0], cv[1], cv[2], cv[3]);
+    }
+    __device__ __forceinline__ void store4G(int r, int c0, const float (&gv)[4]) {
+        *reinterpret_cast<float4 *>(g + off(r, c0)) = make_float4(gv[0], gv[1], gv[2], gv[3]);
     }
     __device__ __forceinline__ void zero_tile(int r0, int c0, int lane) {
 #pragma unroll
@@ -402,24 +420,45 @@ __global__ __launch_bounds__(NW * 64) void verify_kernel(VerifyArgs a) {
                                        (a.solver == CANOPY_SOLVE_AUTO && maxld <= kLevelMaxDepth);
                 const bool use_fwd = !use_level && a.solver != CANOPY_SOLVE_NEUMANN;
                 if (use_fwd) {
-                    // Each 16 x 16 unit lower-triangular diagonal sub-block I + G_pp is
-                    // inverted once per workgroup, column by column (wave 0; lane: sub-block
-                    // lg, column lr), by forward substitution on e_c. The stage holds -G, so
-                    // x_i = [i == c] + sum_{j<i} st_ij x_j. The inverse replaces G_pp in the
-                    // stage, which the sub-block substitution below no longer needs.
-                    if (wave == 0) {
-                        float x[16];
+                    // Each 16 x 16 unit lower-triangular diagonal sub-block I - N (the stage
+                    // holds N = -G_pp) is inverted by one wave as the product of the factors
+                    // (I + N^(2^s)) of its finite Neumann series ("The tree closed form", the
+                    // squaring form), truncated at the sub-block's own depth, on fp32 MFMA.
+                    // The inverse replaces N in the stage, which the substitution below no
+                    // longer needs. With Z = X Y, Z in the A placement (row r, columns
+                    // 4g..4g+3 in lane (g, r)) is the product of Y's B placement and X's A
+                    // placement.
+                    constexpr int NINV = NW < 4 ? NW : 4;
+                    for (int p = wave; p < 4; p += NINV) {
+                        if (64 * r + 16 * p >= T) break;
+                        const int ip = 64 * r + 16 * p + lr;  // this lane's row in the sub-block
+                        const uint32_t wbits = (ip < T) ? ps.mask[ip][(2 * r) + (p >> 1)] : 0u;
+                        const int dl = (ip < T) ? __popc((wbits >> (16 * (p & 1))) & 0xFFFFu) - 1 : -1;
+                        const int dp = wave_max(dl);
+                        int nf = 0;
+                        while ((1 << nf) <= dp) ++nf;
+                        float xa[4], xb[4], minv[4];
 #pragma unroll
-                        for (int i = 0; i < 16; ++i) {
-                            float row[16];
-                            st.rowG16(16 * lg + i, 16 * lg, row);
-                            float acc = (i == lr) ? 1.f : 0.f;
-#pragma unroll
-                            for (int j = 0; j < i; ++j) acc += row[j] * x[j];
-                            x[i] = acc;
+                        for (int e = 0; e < 4; ++e) {
+                            xa[e] = st.getG(16 * p + lr, 16 * p + 4 * lg + e);
+                            xb[e] = st.getG(16 * p + 4 * lg + e, 16 * p + lr);
+                            minv[e] = (lr == 4 * lg + e ? 1.f : 0.f) + xa[e];
                         }
-                        wave_lds_sync();
-                        st.put_col16(16 * lg, 16 * lg, lr, x);
+                        for (int s2 = 1; s2 < nf; ++s2) {
+                            const f32x4 z = {0.f, 0.f, 0.f, 0.f};
+                            const f32x4 ya = mma16f(xb, xa, z);
+                            const f32x4 yb = mma16f(xa, xb, z);
+#pragma unroll
+                            for (int e = 0; e < 4; ++e) {
+                                xa[e] = ya[e];
+                                xb[e] = yb[e];
+                            }
+                            const f32x4 mi = mma16f(xb, minv, f32x4{minv[0], minv[1], minv[2], minv[3]});
+#pragma unroll
+                            for (int e = 0; e < 4; ++e) minv[e] = mi[e];
+                        }
+                        wave_lds_sync();  // every lane has read its operands from the stage
+                        st.store4G(16 * p + lr, 16 * p + 4 * lg, minv);
                     }
                     __syncthreads();
                 }
