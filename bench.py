@@ -48,6 +48,10 @@ WORKLOADS = {
 for _B in (1, 2, 4, 8):
     WORKLOADS[f"skewed64_b{_B}"] = dict(B=_B, H=32, T=64, tree="skewed", dtype="bf16", seed=2,
                                         desc=f"B={_B} H=32 T=64 skewed trees, bf16 q/k/v, fp32 S0")
+    WORKLOADS[f"random256_b{_B}"] = dict(B=_B, H=32, T=256, tree="random", dtype="bf16", seed=3,
+                                         desc=f"B={_B} H=32 T=256 random recursive trees, bf16 q/k/v, fp32 S0")
+    WORKLOADS[f"random128_b{_B}"] = dict(B=_B, H=32, T=128, tree="random", dtype="bf16", seed=4,
+                                         desc=f"B={_B} H=32 T=128 random recursive trees, bf16 q/k/v, fp32 S0")
 
 
 def verify_bytes(B, H, T, dtype):
@@ -74,12 +78,15 @@ def verify_flops(B, H, T):
     return B * H * (4 * T * d * d + 4 * d * T * T)
 
 
-def verify_kernel_name(T, solver):
-    """The kernel canopy_tree_verify launches for this size and solver."""
+def verify_kernel_name(T, solver, heads=0, waves=0, dtype="bf16"):
+    """The kernel canopy_tree_verify launches for this size, solver, head count and width."""
     if T <= 16 and solver in ("auto", "neumann"):
         return "verify_small_kernel"
     if 16 < T <= 64 and solver != "level":
         return "verify_mid_kernel"
+    if T > 64 and dtype == "bf16" and solver in ("auto", "fwdsub"):
+        if waves in (1, 2) or (waves == 0 and heads <= 64):
+            return "verify_wide_kernel"
     return "verify_kernel"
 
 
@@ -515,7 +522,7 @@ def main(argv=None):
         "verify_nodes_per_s": round(B * T / (us_verify * 1e-6), 1),
         "commit_us": round(us_commit, 3),
         "serial_verify_us": None if us_serial is None else round(us_serial, 3),
-        "roofline": {"bound": "hbm", "kernel": verify_kernel_name(T, args.solver),
+        "roofline": {"bound": "hbm", "kernel": verify_kernel_name(T, args.solver, B * H, args.waves, dt),
                      "achieved": round(achieved, 2), "peak": HBM_PEAK_GBS, "unit": "GB/s",
                      "frac": round(achieved / HBM_PEAK_GBS, 5),
                      "traffic": measured_traffic(args.workload, args.solver, args.waves),

@@ -61,6 +61,9 @@ typedef enum { CANOPY_FP32 = 0, CANOPY_BF16 = 1 } canopy_dtype;
  *    substitute forward over the sub-blocks, each 16 x 16 diagonal inverse formed as the
  *    squaring product (I + N)(I + N^2)(I + N^4)(I + N^8), N = -G_pp, truncated at the
  *    sub-block's depth; NEUMANN sums the whole tree's series, one term per tree level.
+ *  - 65 <= T <= 256 with bf16 inputs (AUTO, FWDSUB), for at most 64 (sequence, head) pairs:
+ *    the same wave-per-sub-block forward substitution, with the Gram tiles formed as the
+ *    solved tiles arrive.
  *  - Otherwise, and for LEVEL: 64-node blocks staged in LDS, the couplings to earlier blocks
  *    applied as matrix-core products; a diagonal block is solved by
  *      FWDSUB   forward substitution over four 16-node sub-blocks, each 16 x 16 diagonal
@@ -112,8 +115,11 @@ canopy_status canopy_tree_prep(const int32_t *parent, const float *alpha, int B,
  *   waves       workgroup width, 1, 2, 4 or 8, or 0 to let the library choose from B, H and T.
  *               T <= 16 (AUTO, NEUMANN): waves per workgroup, each owning 16 value columns.
  *               17 <= T <= 64 (AUTO, FWDSUB, NEUMANN): 16-column tiles per workgroup, whose
- *               waves each own 16 nodes (8 is taken as 4). Otherwise (the blocked kernel):
- *               waves per workgroup, each owning 16 value columns; fp32 inputs use at most 2.
+ *               waves each own 16 nodes (8 is taken as 4).
+ *               T > 64, bf16, AUTO or FWDSUB: 1 or 2 picks the wave-per-sub-block kernel with
+ *               that many 16-column tiles per workgroup, 4 or 8 the blocked kernel.
+ *               Otherwise (the blocked kernel): waves per workgroup, each owning 16 value
+ *               columns; fp32 inputs use at most 2.
  */
 canopy_status canopy_tree_verify(const void *q, const void *k, const void *v,
                                  const float *alpha, const float *beta, const float *S0,

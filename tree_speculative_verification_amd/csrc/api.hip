@@ -26,6 +26,10 @@ bool aligned16(const void *p) { return (reinterpret_cast<uintptr_t>(p) & 15u) ==
 // fp32 inputs stage twice the bytes per block and use 2 waves.
 int pick_waves(canopy_dtype dt) { return dt == CANOPY_BF16 ? 8 : 2; }
 
+// Beyond this many (sequence, head) pairs the blocked kernel's single Gram pass per head wins
+// over the wave-per-sub-block kernel's per-column-tile passes for T > 64.
+constexpr long long kWideMaxHeads = 64;
+
 }  // namespace
 
 extern "C" {
@@ -81,6 +85,18 @@ canopy_status canopy_tree_verify(const void *q, const void *k, const void *v,
         return from_hip(launch_verify_small(a, waves, stream));
     if (T > 16 && T <= 64 && solver != CANOPY_SOLVE_LEVEL)
         return from_hip(launch_verify_mid(a, waves == 8 ? 4 : waves, stream));
+    // Trees of 65 to 256 nodes with bf16 inputs, AUTO or FWDSUB: the wave-per-sub-block kernel
+    // (one workgroup per head and 16 or 32 value columns) while there are few heads, the
+    // blocked kernel (one workgroup per head and all columns, no repeated Gram work) beyond.
+    // An explicit width picks the kernel: 1 or 2 column tiles, or 4 or 8 blocked waves.
+    if (T > 64 && in_dtype == CANOPY_BF16 &&
+        (solver == CANOPY_SOLVE_AUTO || solver == CANOPY_SOLVE_FWDSUB)) {
+        if (waves == 1 || waves == 2) return from_hip(launch_verify_wide(a, waves, stream));
+        if (waves == 0) {
+            const long long heads = static_cast<long long>(B) * H;
+            if (heads <= kWideMaxHeads) return from_hip(launch_verify_wide(a, heads <= 32 ? 1 : 2, stream));
+        }
+    }
     return from_hip(launch_verify(a, waves ? waves : pick_waves(in_dtype), stream));
 }
 

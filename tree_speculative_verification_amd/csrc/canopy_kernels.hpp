@@ -60,6 +60,7 @@ struct SerialCommitArgs {
 hipError_t launch_verify(const VerifyArgs &a, int waves, hipStream_t stream);
 hipError_t launch_verify_small(const VerifyArgs &a, int waves, hipStream_t stream);
 hipError_t launch_verify_mid(const VerifyArgs &a, int col_tiles, hipStream_t stream);
+hipError_t launch_verify_wide(const VerifyArgs &a, int col_tiles, hipStream_t stream);
 hipError_t launch_prep(const PrepArgs &a, hipStream_t stream);
 hipError_t launch_commit(const CommitArgs &a, hipStream_t stream);
 hipError_t launch_serial(const SerialArgs &a, hipStream_t stream);
