@@ -80,6 +80,7 @@ __device__ __forceinline__ f32x4 mma16f(const float (&a)[4], f32x4 b, f32x4 c) {
     return c;
 }
 
+
 // Operand fragments: 8 consecutive reduction-index values of one row (A) or column (B).
 // bf16 inputs are exact in one bf16 fragment; fp32 data (S0, G, C, U) used with bf16 inputs is
 // split into hi + lo bf16 parts (|x - hi - lo| <= 2^-16 |x|) and multiplied in up to three

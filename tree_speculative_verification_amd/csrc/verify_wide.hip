@@ -101,9 +101,16 @@ __global__ __launch_bounds__(1024) void verify_wide_kernel(VerifyArgs a) {
     const int b = bh / H, h = bh % H;
     const int NT = blockDim.x;
     const int tid = threadIdx.x;
-    const int p = tid >> 6;  // this wave's sub-block
-    const int lane = tid & 63, lr = lane & 15, lg = lane >> 4;
     const int nsb = NT >> 6;
+    // This wave's sub-block. Waves w, w+4, w+8, w+12 share a SIMD and sub-block p carries work
+    // proportional to p, so each full group of four waves takes its sub-blocks in alternating
+    // order: the SIMDs then get equal shares.
+    const int p = [&] {
+        const int w = tid >> 6, grpw = w >> 2, j = w & 3;
+        if (4 * grpw + 4 > nsb) return w;
+        return (grpw & 1) ? 4 * grpw + 3 - j : w;
+    }();
+    const int lane = tid & 63, lr = lane & 15, lg = lane >> 4;
     const int nch = (T + 63) >> 6;  // 64-node chunks of the prep
     const int colw = grp * 16 * NCT;
     const size_t rs = static_cast<size_t>(H) * D;
