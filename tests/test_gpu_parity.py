@@ -270,10 +270,12 @@ def test_invalid_tree_and_path_reported(canopy):
     assert_close_state("S_new", Sn[:1], S_or[:1], TOL["fp32"])
 
 
-@pytest.mark.parametrize("kind,T", [("chain", 200), ("chain", 33), ("skewed", 128), ("random", 256)])
+@pytest.mark.parametrize("kind,T", [("chain", 200), ("chain", 33), ("chain", 64), ("chain", 65),
+                                    ("chain", 129), ("skewed", 128), ("random", 256)])
 def test_commit_long_paths(canopy, kind, T):
-    """Paths of every length up to T (chains commit all T nodes): the path is staged 32 nodes at
-    a time, so lengths around and above 32 cover every chunk edge."""
+    """Paths of many lengths up to T (chains commit all T nodes): the commit walks the path 64
+    positions at a time, 4 at a time within those, so chains of 33, 64, 65, 129 and 200 nodes
+    put the path's end on and just past every chunk edge."""
     import torch
     for dtype in ("bf16", "fp32"):
         inp = synth.make_inputs(4, 2, T, tree=kind, dtype=dtype, seed=900 + T)
@@ -294,6 +296,30 @@ def test_commit_long_paths(canopy, kind, T):
         S_or, st_or = oracle_commit(inp)
         assert pst.cpu().numpy().tolist() == st_or.tolist() == [0, 0, 0, 0]
         assert_close_state("S_new", Sn.cpu().numpy(), S_or, TOL[dtype])
+
+
+def test_commit_bad_link_in_a_later_chunk(canopy):
+    """A path of 150 nodes on a chain whose 101st entry is not a child of the 100th: the check
+    of the third 64-position chunk reports it, with the oracle's status code, and the state of
+    that sequence is NaN while the other sequence commits normally."""
+    import torch
+    T = 160
+    inp = synth.make_inputs(2, 2, T, tree="chain", dtype="bf16", seed=4242)
+    for b in range(2):
+        inp["path"][b] = -1
+        inp["path"][b, :150] = np.arange(150)
+        inp["path_len"][b] = 150
+    inp["path"][1, 100] = 120
+    d = to_device(inp)
+    _, U, _ = canopy.tree_verify(d["q"], d["k"], d["v"], d["alpha"], d["beta"], d["S0"], d["parent"])
+    Sn, pst = canopy.commit(d["S0"], d["k"], U, d["alpha"], d["parent"], d["path"], d["path_len"])
+    torch.cuda.synchronize()
+    S_or, st_or = oracle_commit(inp)
+    assert st_or[0] == 0 and st_or[1] > 0
+    assert pst.cpu().numpy().tolist() == st_or.tolist()
+    Sn = Sn.cpu().numpy()
+    assert np.isnan(Sn[1]).all()
+    assert_close_state("S_new", Sn[:1], S_or[:1], TOL["bf16"])
 
 
 def test_commit_empty_path_and_in_place(canopy):

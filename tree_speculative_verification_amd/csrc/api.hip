@@ -106,7 +106,7 @@ canopy_status canopy_commit(const float *S0, const void *k, canopy_dtype in_dtyp
                             float *S_new, int32_t *path_status, hipStream_t stream) {
     if (!S0 || !k || !U || !alpha || !parent || !path || !path_len || !S_new) return CANOPY_ERR_ARG;
     if (!sizes_ok(B, H, T)) return CANOPY_ERR_ARG;
-    if (!aligned16(S0) || !aligned16(U) || !aligned16(S_new)) return CANOPY_ERR_ARG;
+    if (!aligned16(S0) || !aligned16(k) || !aligned16(U) || !aligned16(S_new)) return CANOPY_ERR_ARG;
     if (in_dtype != CANOPY_FP32 && in_dtype != CANOPY_BF16) return CANOPY_ERR_UNSUPPORTED;
     CommitArgs a{S0, k, in_dtype == CANOPY_BF16, U, alpha, parent, path, path_len,
                  B, H, T, S_new, path_status};
