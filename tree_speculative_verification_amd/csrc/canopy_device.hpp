@@ -27,6 +27,17 @@ __device__ __forceinline__ void wave_lds_sync() {
     __builtin_amdgcn_wave_barrier();
 }
 
+// Workgroup barrier for LDS data only: every wave's earlier LDS writes are visible to every
+// wave's later LDS reads. Unlike __syncthreads() it does not wait for this wave's outstanding
+// vector memory operations (global stores, loads into registers or into LDS), so a barrier
+// placed while such requests are in flight does not wait for them; data loaded into LDS must be
+// waited for explicitly (wait_vmem) before the barrier that publishes it.
+__device__ __forceinline__ void lds_barrier() {
+    asm volatile("s_waitcnt lgkmcnt(0)" ::: "memory");
+    __builtin_amdgcn_s_barrier();
+    asm volatile("" ::: "memory");
+}
+
 __device__ __forceinline__ int wave_max(int x) {
 #pragma unroll
     for (int o = 32; o > 0; o >>= 1) x = max(x, __shfl_xor(x, o, 64));

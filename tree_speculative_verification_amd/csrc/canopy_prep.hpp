@@ -12,7 +12,7 @@ struct PrepSmem {
     static constexpr int MW = MAXT / 32;
     int32_t jump[MAXT];
     uint32_t mask[MAXT][MW];
-    double ell[MAXT];
+    alignas(16) double ell[MAXT];
     int bad;
 };
 

@@ -123,6 +123,19 @@ struct Stage<true> {
         return static_cast<float>(*reinterpret_cast<const __bf16 *>(gh + o)) +
                static_cast<float>(*reinterpret_cast<const __bf16 *>(gl + o));
     }
+    // The staged values G[r][c0 .. c0+3] (c0 a multiple of 4): one 8-byte read per part.
+    __device__ __forceinline__ void getG4(int r, int c0, float (&out)[4]) const {
+        const int o = off(r, c0);
+        const uint2 h = *reinterpret_cast<const uint2 *>(gh + o);
+        const uint2 l = *reinterpret_cast<const uint2 *>(gl + o);
+        const uint32_t hw[2] = {h.x, h.y}, lw[2] = {l.x, l.y};
+#pragma unroll
+        for (int e = 0; e < 4; ++e) {
+            const uint32_t hb = (e & 1) ? (hw[e >> 1] >> 16) : (hw[e >> 1] & 0xFFFFu);
+            const uint32_t lb = (e & 1) ? (lw[e >> 1] >> 16) : (lw[e >> 1] & 0xFFFFu);
+            out[e] = __uint_as_float(hb << 16) + __uint_as_float(lb << 16);
+        }
+    }
     // The 16 staged values G[r][c0 .. c0+15] (c0 a multiple of 16).
     __device__ __forceinline__ void rowG16(int r, int c0, float (&out)[16]) const {
 #pragma unroll
@@ -182,6 +195,10 @@ struct Stage<false> {
     __device__ __forceinline__ Ops<false>::Sp fragC(int r, int k0) const { return frag(c, r, k0); }
     __device__ __forceinline__ float getG(int r, int cc) const {
         return *reinterpret_cast<const float *>(g + off(r, cc));
+    }
+    __device__ __forceinline__ void getG4(int r, int c0, float (&out)[4]) const {
+        const float4 x = *reinterpret_cast<const float4 *>(g + off(r, c0));
+        out[0] = x.x; out[1] = x.y; out[2] = x.z; out[3] = x.w;
     }
     __device__ __forceinline__ void rowG16(int r, int c0, float (&out)[16]) const {
 #pragma unroll
@@ -374,22 +391,24 @@ __global__ __launch_bounds__(NW * 64) void verify_kernel(VerifyArgs a) {
                 const int i = i0 + lr;
                 const int jb = j0 + 4 * lg;  // first of this lane's 4 columns
                 const uint32_t bits = (ps.mask[i][jb >> 5] >> (jb & 31)) & 0xFu;
-                float gv[4] = {0.f, 0.f, 0.f, 0.f}, cv[4] = {0.f, 0.f, 0.f, 0.f};
-                if (bits) {
-                    const double li = ps.ell[i];
-                    const float bi = s_beta[i];
+                const double li = ps.ell[i];
+                const float bi = s_beta[i];
+                const double2 l01 = *reinterpret_cast<const double2 *>(&ps.ell[jb]);
+                const double2 l23 = *reinterpret_cast<const double2 *>(&ps.ell[jb + 2]);
+                const double lj[4] = {l01.x, l01.y, l23.x, l23.y};
+                float gv[4], cv[4];
 #pragma unroll
-                    for (int e = 0; e < 4; ++e) {
-                        if ((bits >> e) & 1u) {
-                            const float gam = expf(static_cast<float>(li - ps.ell[jb + e]));
-                            cv[e] = gam * qk[e];
-                            if (i != jb + e) gv[e] = -bi * gam * kk[e];
-                        }
-                    }
+                for (int e = 0; e < 4; ++e) {
+                    // exp(l_i - l_j) as 2^((l_i - l_j) log2 e). Off the path the exponent may
+                    // overflow (or read a node past T); the selects drop those entries.
+                    const float gam = __builtin_amdgcn_exp2f(static_cast<float>((li - lj[e]) * 1.4426950408889634));
+                    const bool on = (bits >> e) & 1u;
+                    cv[e] = on ? gam * qk[e] : 0.f;
+                    gv[e] = (on && i != jb + e) ? -bi * gam * kk[e] : 0.f;
                 }
                 st.store4(16 * ti + lr, 16 * tj + 4 * lg, gv, cv);
             }
-            __syncthreads();
+            lds_barrier();
 
             if (c < r) {
                 // K_c is no longer needed: request K_{c+1} for the next pair of this block.
@@ -409,6 +428,15 @@ __global__ __launch_bounds__(NW * 64) void verify_kernel(VerifyArgs a) {
                 if (more) wait_vmem();
             } else {
                 const bool next = r + 1 < nb;
+                // Past the staging barrier of the diagonal pair nothing reads block r's K, Q
+                // and V or K_c any more (the solve and the read-out use the stage): request
+                // the next block's K, Q, V and K_0 now, to land during the solve.
+                if (next) {
+                    dma_block<BF, NT>(s_ka, a.k, base, rs, 64 * (r + 1), T);
+                    dma_block<BF, NT>(s_qa, a.q, base, rs, 64 * (r + 1), T);
+                    if (NB > 1) dma_block<BF, NT>(s_kb, a.k, base, rs, 0, T);
+                    dma_v<BF>(s_v[wave], a.v, base, rs, col0, 64 * (r + 1), T, lane);
+                }
                 // ---- a4: the diagonal block, per wave on its 16 columns
                 const int ib = 64 * r + lane;
                 uint64_t bm = 0;
@@ -460,7 +488,7 @@ __global__ __launch_bounds__(NW * 64) void verify_kernel(VerifyArgs a) {
                         wave_lds_sync();  // every lane has read its operands from the stage
                         st.store4G(16 * p + lr, 16 * p + 4 * lg, minv);
                     }
-                    __syncthreads();
+                    lds_barrier();
                 }
                 if (a.solver == CANOPY_SOLVE_NEUMANN) {
                     f32x4 z[4];
@@ -526,59 +554,32 @@ __global__ __launch_bounds__(NW * 64) void verify_kernel(VerifyArgs a) {
                         wave_lds_sync();
                     }
                 } else {
-                    // Blocked forward substitution inside the block: four 16-node sub-blocks;
-                    // the inverses of the diagonal sub-blocks are in the stage (see above).
-#pragma unroll
-                    for (int ti = 0; ti < 4; ++ti)
-#pragma unroll
-                        for (int e = 0; e < 4; ++e) Xc[lr][16 * ti + 4 * lg + e] = rhs[ti][e];
-                    wave_lds_sync();
-                    // (2) U_p = (I + G_pp)^-1 (RHS_p - sum_{q<p} G_pq U_q), p = 0..3 (MFMA).
+                    // Blocked forward substitution inside the block over its four 16-node
+                    // sub-blocks, with the inverses of the diagonal sub-blocks in the stage:
+                    //   U_p = (I - N_pp)^-1 (RHS_p + sum_{q<p} N_pq U_q),  N = -G.
+                    // RHS_p and U_q sit in the result placement (rows 4lg..4lg+3 of column
+                    // lr), which is the B placement of a 16-long fp32 MFMA reduction, and the
+                    // stage gives N_pq row lr, columns 4lg..4lg+3 (the A placement), so the
+                    // whole chain stays in registers. Sub-blocks past T have zero RHS and a
+                    // zero stage, so they come out zero.
+                    f32x4 u[4];
 #pragma unroll
                     for (int p = 0; p < 4; ++p) {
-                        if (64 * r + 16 * p >= T) break;
                         f32x4 acc = rhs[p];
 #pragma unroll
-                        for (int ks = 0; ks < 2; ++ks) {
-                            if (32 * ks < 16 * p) {
-                                Sp gf = st.fragG(16 * p + lr, 32 * ks + 8 * lg);
-                                if (32 * ks + 8 * lg >= 16 * p) {
-                                    const float z8[8] = {0.f, 0.f, 0.f, 0.f, 0.f, 0.f, 0.f, 0.f};
-                                    gf = Op::split(z8);
-                                }
-                                float v[8];
-#pragma unroll
-                                for (int e = 0; e < 8; ++e) v[e] = Xc[lr][32 * ks + 8 * lg + e];
-                                acc = Op::mma(gf, Op::split(v), acc);
-                            }
+                        for (int q = 0; q < p; ++q) {
+                            float ga[4];
+                            st.getG4(16 * p + lr, 16 * q + 4 * lg, ga);
+                            acc = mma16f(ga, u[q], acc);
                         }
-#pragma unroll
-                        for (int e = 0; e < 4; ++e) Xc[lr][16 * p + 4 * lg + e] = acc[e];
-                        wave_lds_sync();
-                        float v[8];
-#pragma unroll
-                        for (int e = 0; e < 8; ++e) v[e] = (lg < 2) ? Xc[lr][16 * p + 8 * lg + e] : 0.f;
-                        Sp dfr = st.fragG(16 * p + lr, 16 * p + 8 * (lg & 1));
-                        if (lg >= 2) {
-                            const float z8[8] = {0.f, 0.f, 0.f, 0.f, 0.f, 0.f, 0.f, 0.f};
-                            dfr = Op::split(z8);
-                        }
-                        f32x4 u = {0.f, 0.f, 0.f, 0.f};
-                        u = Op::mma(dfr, Op::split(v), u);
-                        wave_lds_sync();
-#pragma unroll
-                        for (int e = 0; e < 4; ++e) Xc[lr][16 * p + 4 * lg + e] = u[e];
-                        wave_lds_sync();
+                        float mi[4];
+                        st.getG4(16 * p + lr, 16 * p + 4 * lg, mi);
+                        u[p] = mma16f(mi, acc, f32x4{0.f, 0.f, 0.f, 0.f});
                     }
-                }
-                // Block r's K, Q and V are no longer needed and this wave writes no more LDS in
-                // this pair: request the next block's K, Q, V and K_0 now, to land during the
-                // read-out and the stores.
-                if (next) {
-                    dma_block<BF, NT>(s_ka, a.k, base, rs, 64 * (r + 1), T);
-                    dma_block<BF, NT>(s_qa, a.q, base, rs, 64 * (r + 1), T);
-                    if (NB > 1) dma_block<BF, NT>(s_kb, a.k, base, rs, 0, T);
-                    dma_v<BF>(s_v[wave], a.v, base, rs, col0, 64 * (r + 1), T, lane);
+#pragma unroll
+                    for (int p = 0; p < 4; ++p)
+                        *reinterpret_cast<float4 *>(&Xc[lr][16 * p + 4 * lg]) = make_float4(u[p][0], u[p][1], u[p][2], u[p][3]);
+                    wave_lds_sync();
                 }
 #pragma unroll
                 for (int ks = 0; ks < 2; ++ks) {
@@ -592,6 +593,10 @@ __global__ __launch_bounds__(NW * 64) void verify_kernel(VerifyArgs a) {
 #pragma unroll
                     for (int ks = 0; ks < 2; ++ks)
                         oacc[ti] = Op::mma(st.fragC(16 * ti + lr, 32 * ks + 8 * lg), uf[r][ks], oacc[ti]);
+                // The next block's operands must be in LDS before the barrier. The counter that
+                // tracks them also tracks stores, so wait before the stores are issued: nothing
+                // needs them complete.
+                if (next) wait_vmem();
 
                 // ---- a6: outputs of block r
 #pragma unroll
@@ -607,10 +612,9 @@ __global__ __launch_bounds__(NW * 64) void verify_kernel(VerifyArgs a) {
                         const int i = 64 * r + 16 * ti + 4 * lg + e;
                         if (i < T) a.O[base + static_cast<size_t>(i) * rs + col0 + lr] = oacc[ti][e];
                     }
-                if (next) wait_vmem();
             }
             // The stage is free and the next operands are in LDS for every wave.
-            __syncthreads();
+            lds_barrier();
         }
     }
 }
