@@ -20,8 +20,17 @@
  *    caller. The library keeps no pointer after a call returns and allocates nothing.
  *  - Calls only enqueue work on `stream` (0 = the null stream) and return; they do not
  *    synchronise. Inputs are read-only; outputs are fully overwritten.
- *  - d_k = d_v = 128. 1 <= T <= 256. B >= 1, H >= 1, B * H * 256 <= INT_MAX. q, k and v all
- *    have H heads.
+ *  - d_k = d_v = 128. 1 <= T <= 256. B >= 1. Heads follow "Design decisions / Memory layout":
+ *    q and k have H heads, v, alpha, beta, S0 and every per-head output have HV heads, and
+ *    each q/k head serves HV / H value heads (grouped value heads, FLA's layout): value head j
+ *    reads q/k head j / (HV / H). 1 <= H <= HV, H divides HV, B * HV * 256 <= INT_MAX. H = HV
+ *    is the plain one-to-one layout.
+ *  - Ragged batches ("Memory layout": the tree plus a per-sequence length): tree_len [B]
+ *    int32 may be NULL (every tree has T nodes) or give sequence b's node count, 1..T. Arrays
+ *    keep their T-row extent; the nodes past a sequence's length are padding: their inputs are
+ *    never used (they may hold anything, NaN included) and their outputs are not written. A
+ *    length outside 1..T is a malformed tree with status -1 (all T rows then count as the tree
+ *    and hold NaN).
  *  - Node order is the caller's: node i's outputs sit at index i. parent[b,0] must be -1 and
  *    -1 <= parent[b,i] < i; further roots (parent -1) start from S0 too.
  *  - The scale on q is 1 (callers that want 1/sqrt(d_k) pre-scale q).
@@ -66,8 +75,9 @@ typedef enum { CANOPY_FP32 = 0, CANOPY_BF16 = 1 } canopy_dtype;
  *    solved tiles arrive.
  *  - Otherwise, and for LEVEL: 64-node blocks staged in LDS, the couplings to earlier blocks
  *    applied as matrix-core products; a diagonal block is solved by
- *      FWDSUB   forward substitution over four 16-node sub-blocks, each 16 x 16 diagonal
- *               sub-block inverted by substitution and applied on the matrix cores;
+ *      FWDSUB   forward substitution over four 16-node sub-blocks on fp32 matrix-core
+ *               products, each 16 x 16 diagonal inverse formed as the truncated squaring
+ *               product above;
  *      NEUMANN  the finite series sum_{m=0..d} (-G_bb)^m, d the block's in-block depth;
  *      LEVEL    row-by-row substitution with the rows of equal in-block depth together;
  *      AUTO     LEVEL for blocks of in-block depth <= 3, FWDSUB otherwise. */
@@ -88,28 +98,32 @@ const char *canopy_status_string(canopy_status s);
  * Tree preprocessing on the GPU ("The tree closed form"; "Design decisions / Tree order and
  * tiling" for the T x T bitmask).
  *   parent      [B,T] int32, in.
- *   alpha       [B,T,H] fp32, in.
+ *   tree_len    [B] int32, in, may be NULL: per-sequence node counts (see above).
+ *   alpha       [B,T,HV] fp32, in.
  *   anc_mask    [B,T,ceil(T/32)] uint32, out, may be NULL: bit (j % 32) of word j / 32 of row
  *               i is set iff j is in path(i) (strict ancestors and i itself).
  *   depth       [B,T] int32, out, may be NULL: |A(i)|, the root 0.
- *   ell         [B,T,H] fp32, out, may be NULL: l_i = log alpha_i + l_parent(i), a root's
+ *   ell         [B,T,HV] fp32, out, may be NULL: l_i = log alpha_i + l_parent(i), a root's
  *               parent counting 0, summed in fp64 and rounded once.
- *   tree_status [B] int32, out, may be NULL: 0, or 1 + the first node i whose parent is not
- *               in -1..i-1 (then mask and depth rows are 0 and ell is NaN).
+ *   tree_status [B] int32, out, may be NULL: 0; -1 for a tree_len outside 1..T; else 1 + the
+ *               first node i whose parent is not in -1..i-1 (then mask and depth rows are 0
+ *               and ell is NaN).
  */
-canopy_status canopy_tree_prep(const int32_t *parent, const float *alpha, int B, int H, int T,
-                               uint32_t *anc_mask, int32_t *depth, float *ell,
+canopy_status canopy_tree_prep(const int32_t *parent, const int32_t *tree_len, const float *alpha,
+                               int B, int HV, int T, uint32_t *anc_mask, int32_t *depth, float *ell,
                                int32_t *tree_status, hipStream_t stream);
 
 /*
  * Verify a draft tree through one GDN layer: every node's output and pseudo-value in one pass
  * (prep, S0 projections, masked Gram matrices, the triangular solve and the read-out fused).
- *   q, k, v     [B,T,H,128], in_dtype (fp32, or bf16 as 16-bit patterns), in.
- *   alpha, beta [B,T,H] fp32, in.
- *   S0          [B,H,128(k),128(v)] fp32, in: the committed state per (sequence, head).
+ *   q, k        [B,T,H,128], in_dtype (fp32, or bf16 as 16-bit patterns), in.
+ *   v           [B,T,HV,128], in_dtype, in.
+ *   alpha, beta [B,T,HV] fp32, in.
+ *   S0          [B,HV,128(k),128(v)] fp32, in: the committed state per (sequence, value head).
  *   parent      [B,T] int32, in.
- *   O, U        [B,T,H,128] fp32, out: outputs o_i and pseudo-values u_i.
- *   ell         [B,T,H] fp32, out: as in canopy_tree_prep.
+ *   tree_len    [B] int32, in, may be NULL: per-sequence node counts.
+ *   O, U        [B,T,HV,128] fp32, out: outputs o_i and pseudo-values u_i.
+ *   ell         [B,T,HV] fp32, out: as in canopy_tree_prep.
  *   anc_mask, depth, tree_status: optional outputs (NULL to skip), as in canopy_tree_prep.
  *   solver      AUTO, FWDSUB, NEUMANN or LEVEL (see canopy_solver).
  *   waves       workgroup width, 1, 2, 4 or 8, or 0 to let the library choose from B, H and T.
@@ -123,56 +137,62 @@ canopy_status canopy_tree_prep(const int32_t *parent, const float *alpha, int B,
  */
 canopy_status canopy_tree_verify(const void *q, const void *k, const void *v,
                                  const float *alpha, const float *beta, const float *S0,
-                                 const int32_t *parent, int B, int H, int T,
-                                 canopy_dtype in_dtype, float *O, float *U, float *ell,
-                                 uint32_t *anc_mask, int32_t *depth, int32_t *tree_status,
-                                 canopy_solver solver, int waves, hipStream_t stream);
+                                 const int32_t *parent, const int32_t *tree_len, int B, int H,
+                                 int HV, int T, canopy_dtype in_dtype, float *O, float *U,
+                                 float *ell, uint32_t *anc_mask, int32_t *depth,
+                                 int32_t *tree_status, canopy_solver solver, int waves,
+                                 hipStream_t stream);
 
 /*
  * Commit the accepted path: S_new = exp(l_a) S0 + sum_{j in path} exp(l_a - l_j) k_j u_j^T
  * with a the path's last node ("What the commit kernel stores"; "M5"). The decay ratios are
  * suffix sums of log alpha along the path (fp64), so no cancellation of large l enters them.
- *   S0          [B,H,128,128] fp32, in.
+ *   S0          [B,HV,128,128] fp32, in.
  *   k           [B,T,H,128], in_dtype, in: the keys given to canopy_tree_verify.
- *   U           [B,T,H,128] fp32, in: the pseudo-values canopy_tree_verify wrote.
- *   alpha       [B,T,H] fp32, in.
+ *   U           [B,T,HV,128] fp32, in: the pseudo-values canopy_tree_verify wrote.
+ *   alpha       [B,T,HV] fp32, in.
  *   parent      [B,T] int32, in: only the path's own links are checked.
+ *   tree_len    [B] int32, in, may be NULL: per-sequence node counts; path nodes must lie
+ *               below them.
  *   path        [B,T] int32, in: node ids root first; entries past path_len are ignored.
- *   path_len    [B] int32, in: m in 0..T (0 commits nothing: S_new = S0).
- *   S_new       [B,H,128,128] fp32, out; may be the same memory as S0 (in place).
- *   path_status [B] int32, out, may be NULL: 0 valid, -1 path_len out of range, else 1 + the
- *               first position t whose node is out of range or is not a child of path[t-1]
- *               (for t = 0: not a root). S_new of such a sequence is NaN.
+ *   path_len    [B] int32, in: m in 0..n, n the sequence's node count (0 commits nothing:
+ *               S_new = S0).
+ *   S_new       [B,HV,128,128] fp32, out; may be the same memory as S0 (in place).
+ *   path_status [B] int32, out, may be NULL: 0 valid, -1 path_len (or tree_len) out of range,
+ *               else 1 + the first position t whose node is out of range or is not a child of
+ *               path[t-1] (for t = 0: not a root). S_new of such a sequence is NaN.
  */
 canopy_status canopy_commit(const float *S0, const void *k, canopy_dtype in_dtype,
                             const float *U, const float *alpha, const int32_t *parent,
-                            const int32_t *path, const int32_t *path_len, int B, int H, int T,
-                            float *S_new, int32_t *path_status, hipStream_t stream);
+                            const int32_t *tree_len, const int32_t *path, const int32_t *path_len,
+                            int B, int H, int HV, int T, float *S_new, int32_t *path_status,
+                            hipStream_t stream);
 
 /*
  * Serial fork baseline ("Design decisions / Serial baseline"): walk the nodes in order; each
  * node starts from its parent's per-node state snapshot (S0 for a root), takes one step of the
  * gated delta rule and writes its own snapshot, output and pseudo-value. Same inputs and
  * outputs as canopy_tree_verify plus
- *   snapshots   [B,T,H,128,128] fp32, out: every node's state.
+ *   snapshots   [B,T,HV,128,128] fp32, out: every node's state (padding nodes' not written).
  */
 canopy_status canopy_serial_verify(const void *q, const void *k, const void *v,
                                    const float *alpha, const float *beta, const float *S0,
-                                   const int32_t *parent, int B, int H, int T,
-                                   canopy_dtype in_dtype, float *O, float *U, float *snapshots,
-                                   int32_t *tree_status, hipStream_t stream);
+                                   const int32_t *parent, const int32_t *tree_len, int B, int H,
+                                   int HV, int T, canopy_dtype in_dtype, float *O, float *U,
+                                   float *snapshots, int32_t *tree_status, hipStream_t stream);
 
 /*
  * Commit for the serial baseline: the accepted path's last node's snapshot (written by
  * canopy_serial_verify) becomes the new state (S0 itself for an empty path). Path checks and
  * path_status as in canopy_commit.
- *   snapshots   [B,T,H,128,128] fp32, in.
- *   S0          [B,H,128,128] fp32, in.
- *   S_new       [B,H,128,128] fp32, out; may be the same memory as S0.
+ *   snapshots   [B,T,HV,128,128] fp32, in.
+ *   S0          [B,HV,128,128] fp32, in.
+ *   S_new       [B,HV,128,128] fp32, out; may be the same memory as S0.
  */
 canopy_status canopy_serial_commit(const float *snapshots, const float *S0, const int32_t *parent,
-                                   const int32_t *path, const int32_t *path_len, int B, int H, int T,
-                                   float *S_new, int32_t *path_status, hipStream_t stream);
+                                   const int32_t *tree_len, const int32_t *path,
+                                   const int32_t *path_len, int B, int HV, int T, float *S_new,
+                                   int32_t *path_status, hipStream_t stream);
 
 #ifdef __cplusplus
 }

@@ -122,3 +122,68 @@ def commit(parent, path, path_len, k, v, alpha, beta, S0):
     _load().oracle_commit(B, H, T, dk, dv, _p(par), _p(path), _p(plen), _p(k), _p(v),
                           _p(alpha), _p(beta), _p(S0), _p(S_new), _p(status))
     return S_new, status
+
+
+def expand_heads(x, HV):
+    """q or k ([B,T,H,d]) as the HV value heads see them: each of the H heads serves HV // H
+    consecutive value heads, so value head j reads head j // (HV // H) (the canopy page,
+    "Design decisions / Memory layout": q and k have H heads, v, the gates and the state HV)."""
+    H = x.shape[2]
+    assert HV % H == 0 and HV >= H
+    return np.repeat(np.asarray(x), HV // H, axis=2)
+
+
+def gdn_tree_ragged(parent, tree_len, q, k, v, alpha, beta, S0):
+    """Grouped value heads and a ragged batch ("Memory layout": the tree plus a per-sequence
+    length): sequence b is the tree of its first tree_len[b] nodes, run through ``gdn_tree``
+    on its own, with q and k expanded to the value heads. q, k [B,T,H,d]; v [B,T,HV,d];
+    alpha, beta [B,T,HV]; S0 [B,HV,dk,dv]; tree_len [B] or None (all T). Returns O, U, ell
+    (NaN past each sequence's length: padding rows have no value) and status [B]: -1 for a
+    length outside 1..T, else the tree status of the sequence's own nodes."""
+    par = _i32(parent)
+    B, T = par.shape
+    HV = np.asarray(v).shape[2]
+    lens = np.full(B, T, np.int64) if tree_len is None else np.asarray(tree_len, np.int64)
+    qe, ke = expand_heads(q, HV), expand_heads(k, HV)
+    v, alpha, beta, S0 = np.asarray(v), np.asarray(alpha), np.asarray(beta), np.asarray(S0)
+    O = np.full(v.shape, np.nan)
+    U = np.full(v.shape, np.nan)
+    ell = np.full(alpha.shape, np.nan)
+    status = np.zeros(B, np.int32)
+    for b in range(B):
+        n = int(lens[b])
+        if not 1 <= n <= T:
+            status[b] = -1
+            continue
+        sl = (slice(b, b + 1), slice(0, n))
+        status[b] = tree_structure(par[sl])[2][0]
+        if status[b]:
+            continue
+        r = gdn_tree(par[sl], qe[sl], ke[sl], v[sl], alpha[sl], beta[sl], S0[b:b + 1])
+        O[b, :n], U[b, :n], ell[b, :n] = r["O"][0], r["U"][0], r["ell"][0]
+    return dict(O=O, U=U, ell=ell, status=status)
+
+
+def commit_ragged(parent, tree_len, path, path_len, k, v, alpha, beta, S0):
+    """``commit`` for grouped value heads and a ragged batch: sequence b commits on the tree of
+    its first tree_len[b] nodes (a path node at or past it breaks the path), k expanded to the
+    value heads. Returns (S_new [B,HV,dk,dv], status [B]); status -1 also for a length outside
+    1..T."""
+    par, pth, plen = _i32(parent), _i32(path), _i32(path_len)
+    B, T = par.shape
+    HV = np.asarray(v).shape[2]
+    lens = np.full(B, T, np.int64) if tree_len is None else np.asarray(tree_len, np.int64)
+    ke = expand_heads(k, HV)
+    v, alpha, beta, S0 = np.asarray(v), np.asarray(alpha), np.asarray(beta), np.asarray(S0)
+    S_new = np.full(S0.shape, np.nan)
+    status = np.zeros(B, np.int32)
+    for b in range(B):
+        n = int(lens[b])
+        if not 1 <= n <= T:
+            status[b] = -1
+            continue
+        sl = (slice(b, b + 1), slice(0, n))
+        s, st = commit(par[sl], pth[sl], plen[b:b + 1], ke[sl], v[sl], alpha[sl], beta[sl],
+                       S0[b:b + 1])
+        S_new[b], status[b] = s[0], st[0]
+    return S_new, status

@@ -211,27 +211,40 @@ def _l2n(x):
 
 def make_inputs(B: int, H: int, T: int, *, tree: str = "random", dtype: str = "bf16",
                 seed: int = 0, dk: int = 128, dv: int = 128, tree_kw: dict | None = None,
-                parents=None, s0_std: float = 0.1) -> dict:
+                parents=None, s0_std: float = 0.1, HK: int | None = None, tree_len=None,
+                pad: float = float("nan")) -> dict:
     """Draw one layer's inputs.
 
     ``tree`` names a family of ``make_tree``; for random families every batch element gets its
     own tree. ``parents`` (a [B,T] array or one [T] array) overrides the drawn trees. Returns a
-    dict with fp32 arrays q, k, v [B,T,H,d], alpha, beta [B,T,H], S0 [B,H,dk,dv], parent
-    [B,T] int32, a random root-to-leaf path per sequence (``path`` [B,T] root first, padded with
-    -1, and ``path_len`` [B]), and for bf16 inputs the 16-bit patterns q_bits, k_bits, v_bits.
-    q, k, v hold exactly the values the device reads (already rounded for bf16).
+    dict with fp32 arrays q, k [B,T,HK,d], v [B,T,H,d], alpha, beta [B,T,H], S0 [B,H,dk,dv],
+    parent [B,T] int32, a random root-to-leaf path per sequence (``path`` [B,T] root first,
+    padded with -1, and ``path_len`` [B]), and for bf16 inputs the 16-bit patterns q_bits,
+    k_bits, v_bits. q, k, v hold exactly the values the device reads (already rounded for bf16).
+
+    ``HK`` (default H) is the number of q/k heads, a divisor of the H value heads. ``tree_len``
+    ([B] ints in 1..T) makes a ragged batch: sequence b's tree has tree_len[b] nodes, and the
+    rows past it are padding, filled with ``pad`` (q, k, v, alpha, beta) and with parents that
+    are not valid (-5).
     """
     rng = np.random.default_rng(seed)
     tree_kw = tree_kw or {}
+    HK = H if HK is None else HK
+    assert H % HK == 0
+    lens = None if tree_len is None else np.asarray(tree_len, dtype=np.int32)
     if parents is not None:
         par = np.asarray(parents, dtype=np.int32)
         if par.ndim == 1:
             par = np.broadcast_to(par, (B, T)).copy()
-    else:
+    elif lens is None:
         par = np.stack([make_tree(tree, T, rng, **tree_kw) for _ in range(B)]).astype(np.int32)
+    else:
+        par = np.full((B, T), -5, dtype=np.int32)
+        for b in range(B):
+            par[b, :lens[b]] = make_tree(tree, int(lens[b]), rng, **tree_kw)
     assert par.shape == (B, T)
-    xq = rng.standard_normal((B, T, H, dk))
-    xk = rng.standard_normal((B, T, H, dk))
+    xq = rng.standard_normal((B, T, HK, dk))
+    xk = rng.standard_normal((B, T, HK, dk))
     v = rng.standard_normal((B, T, H, dv))
     zb = rng.standard_normal((B, T, H))
     za = rng.standard_normal((B, T, H))
@@ -245,11 +258,18 @@ def make_inputs(B: int, H: int, T: int, *, tree: str = "random", dtype: str = "b
     paths = np.full((B, T), -1, dtype=np.int32)
     plen = np.zeros(B, dtype=np.int32)
     for b in range(B):
-        pth = random_leaf_path(par[b], rng)
+        n = T if lens is None else int(lens[b])
+        pth = random_leaf_path(par[b, :n], rng)
         paths[b, :len(pth)] = pth
         plen[b] = len(pth)
-    out = dict(B=B, H=H, T=T, dk=dk, dv=dv, dtype=dtype, parent=par, alpha=alpha, beta=beta,
-               S0=S0, path=paths, path_len=plen)
+    if lens is not None:
+        for b in range(B):
+            n = int(lens[b])
+            for arr in (q, k, v, alpha, beta):
+                arr[b, n:] = pad
+    out = dict(B=B, H=H, HK=HK, T=T, dk=dk, dv=dv, dtype=dtype, parent=par, alpha=alpha,
+               beta=beta, S0=S0, path=paths, path_len=plen,
+               tree_len=None if lens is None else lens.copy())
     if dtype == "bf16":
         for name, arr in (("q", q), ("k", k), ("v", v)):
             bits = bf16_bits(arr)

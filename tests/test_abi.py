@@ -42,13 +42,16 @@ def test_host_checks_need_no_gpu():
     f = lib.canopy_tree_verify
     f.restype = ctypes.c_int
     nul = ctypes.c_void_p(0)
-    args = [nul] * 7 + [ctypes.c_int(1), ctypes.c_int(1), ctypes.c_int(4), ctypes.c_int(0)] + \
-        [nul] * 6 + [ctypes.c_int(0), ctypes.c_int(0), nul]
+    i = ctypes.c_int
+    # q, k, v, alpha, beta, S0, parent, tree_len; B, H, HV, T, dtype; O, U, ell, mask, depth,
+    # status; solver, waves, stream
+    args = [nul] * 8 + [i(1), i(1), i(1), i(4), i(0)] + [nul] * 6 + [i(0), i(0), nul]
     assert f(*args) == 1
     g = lib.canopy_commit
     g.restype = ctypes.c_int
-    assert g(*([nul, nul, ctypes.c_int(0), nul, nul, nul, nul, nul, ctypes.c_int(1),
-                ctypes.c_int(1), ctypes.c_int(4), nul, nul, nul])) == 1
+    # S0, k, dtype, U, alpha, parent, tree_len, path, path_len, B, H, HV, T, S_new, status, stream
+    assert g(*([nul, nul, i(0), nul, nul, nul, nul, nul, nul, i(1), i(1), i(1), i(4), nul, nul,
+                nul])) == 1
 
 
 def test_product_path_does_not_touch_the_oracle():

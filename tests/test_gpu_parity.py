@@ -414,16 +414,21 @@ def test_host_errors(canopy):
     U = torch.empty_like(O)
     L = torch.empty((1, 4, 1), device="cuda")
     p = lambda t: ctypes.c_void_p(t.data_ptr())
-    args = [p(d["q"]), p(d["k"]), p(d["v"]), p(d["alpha"]), p(d["beta"]), p(d["S0"]), p(d["parent"])]
+    args = [p(d["q"]), p(d["k"]), p(d["v"]), p(d["alpha"]), p(d["beta"]), p(d["S0"]), p(d["parent"]),
+            None]
     outs = [p(O), p(U), p(L), None, None, None]
     s = ctypes.c_void_p(0)
-    assert lib.canopy_tree_verify(*args, 1, 1, 0, 0, *outs, 0, 0, s) == 1      # T = 0
-    assert lib.canopy_tree_verify(*args, 1, 1, 257, 0, *outs, 0, 0, s) == 1    # T > 256
-    assert lib.canopy_tree_verify(*args, 1, 1, 4, 5, *outs, 0, 0, s) == 2      # dtype
-    assert lib.canopy_tree_verify(*args, 1, 1, 4, 0, *outs, 7, 0, s) == 2      # solver
-    assert lib.canopy_tree_verify(*args, 1, 1, 4, 0, *outs, 0, 3, s) == 2      # waves
+    # B, H, HV, T, dtype
+    assert lib.canopy_tree_verify(*args, 1, 1, 1, 0, 0, *outs, 0, 0, s) == 1      # T = 0
+    assert lib.canopy_tree_verify(*args, 1, 1, 1, 257, 0, *outs, 0, 0, s) == 1    # T > 256
+    assert lib.canopy_tree_verify(*args, 1, 2, 1, 4, 0, *outs, 0, 0, s) == 1      # H > HV
+    assert lib.canopy_tree_verify(*args, 1, 2, 3, 4, 0, *outs, 0, 0, s) == 1      # H does not divide HV
+    assert lib.canopy_tree_verify(*args, 1, 0, 1, 4, 0, *outs, 0, 0, s) == 1      # H = 0
+    assert lib.canopy_tree_verify(*args, 1, 1, 1, 4, 5, *outs, 0, 0, s) == 2      # dtype
+    assert lib.canopy_tree_verify(*args, 1, 1, 1, 4, 0, *outs, 7, 0, s) == 2      # solver
+    assert lib.canopy_tree_verify(*args, 1, 1, 1, 4, 0, *outs, 0, 3, s) == 2      # waves
     bad = list(args)
     bad[0] = None
-    assert lib.canopy_tree_verify(*bad, 1, 1, 4, 0, *outs, 0, 0, s) == 1       # null q
-    assert lib.canopy_tree_verify(*args, 1, 1, 4, 0, *outs, 0, 0, s) == 0
+    assert lib.canopy_tree_verify(*bad, 1, 1, 1, 4, 0, *outs, 0, 0, s) == 1       # null q
+    assert lib.canopy_tree_verify(*args, 1, 1, 1, 4, 0, *outs, 0, 0, s) == 0
     torch.cuda.synchronize()

@@ -390,3 +390,74 @@ def test_error_metric_self_check():
     assert per_head_rel_err(x, y) == 1.0
     assert state_rel_err(np.ones((1, 1, 2, 2)), np.ones((1, 1, 2, 2))) == 0.0
     assert max_rel_err([1.0, 2.0], [1.0, 4.0]) == 0.5
+
+
+# --------------------------------------------------------------------------- grouped heads, ragged
+def test_ragged_prefix_equals_full_tree():
+    """Parents precede children, so the first n nodes of a tree form a closed forest and their
+    outputs do not depend on the later nodes: a ragged batch's sequence of n nodes must give
+    the same rows as the full tree's first n rows, whatever the padding holds."""
+    T = 23
+    inp = synth.make_inputs(1, 2, T, tree="random", dtype="fp32", seed=71)
+    full = oracle.gdn_tree(inp["parent"], inp["q"], inp["k"], inp["v"], inp["alpha"],
+                           inp["beta"], inp["S0"])
+    for n in (1, 9, 22):
+        junk = {name: np.array(inp[name], copy=True) for name in ("q", "k", "v", "alpha", "beta")}
+        par = np.array(inp["parent"], copy=True)
+        par[0, n:] = -7
+        for name in junk:
+            junk[name][0, n:] = np.nan
+        r = oracle.gdn_tree_ragged(par, [n], junk["q"], junk["k"], junk["v"], junk["alpha"],
+                                   junk["beta"], inp["S0"])
+        assert r["status"][0] == 0
+        assert np.array_equal(r["O"][0, :n], full["O"][0, :n])
+        assert np.array_equal(r["U"][0, :n], full["U"][0, :n])
+        assert np.isnan(r["O"][0, n:]).all()
+
+
+def test_ragged_bad_lengths():
+    inp = synth.make_inputs(3, 1, 6, tree="chain", dtype="fp32", seed=72)
+    r = oracle.gdn_tree_ragged(inp["parent"], [0, 7, 6], inp["q"], inp["k"], inp["v"],
+                               inp["alpha"], inp["beta"], inp["S0"])
+    assert r["status"].tolist() == [-1, -1, 0]
+    S, st = oracle.commit_ragged(inp["parent"], [6, 0, 3], inp["path"], inp["path_len"], inp["k"],
+                                 inp["v"], inp["alpha"], inp["beta"], inp["S0"])
+    # sequence 2's chain path of 6 nodes is longer than its 3-node tree
+    assert st.tolist() == [0, -1, -1]
+
+
+def test_grouped_heads_expand_key_heads():
+    """With one q/k head serving two value heads: value heads given identical v, gates and
+    state give identical outputs; each value head equals a one-to-one run with the shared key
+    head's q and k; and two value heads with different inputs differ."""
+    T = 12
+    inp = synth.make_inputs(2, 4, T, tree="random", dtype="fp32", seed=73, HK=2)
+    v, al, be, S0 = (np.array(inp[n], copy=True) for n in ("v", "alpha", "beta", "S0"))
+    v[:, :, 1], al[:, :, 1], be[:, :, 1], S0[:, 1] = v[:, :, 0], al[:, :, 0], be[:, :, 0], S0[:, 0]
+    r = oracle.gdn_tree_ragged(inp["parent"], None, inp["q"], inp["k"], v, al, be, S0)
+    assert np.array_equal(r["O"][:, :, 0], r["O"][:, :, 1])
+    assert not np.allclose(r["O"][:, :, 1], r["O"][:, :, 2])
+    for j in range(4):
+        kh = j // 2
+        one = oracle.gdn_tree(inp["parent"], inp["q"][:, :, kh:kh + 1], inp["k"][:, :, kh:kh + 1],
+                              v[:, :, j:j + 1], al[:, :, j:j + 1], be[:, :, j:j + 1], S0[:, j:j + 1])
+        assert np.array_equal(r["O"][:, :, j:j + 1], one["O"])
+        assert np.array_equal(r["U"][:, :, j:j + 1], one["U"])
+
+
+def test_commit_ragged_matches_accepted_state():
+    """The ragged, grouped commit equals the recurrence's state at the accepted node of the
+    sequence's own tree (the full tree's state there, by path locality)."""
+    T = 15
+    lens = [15, 8]
+    inp = synth.make_inputs(2, 4, T, tree="random", dtype="fp32", seed=74, HK=1, tree_len=lens)
+    S, st = oracle.commit_ragged(inp["parent"], inp["tree_len"], inp["path"], inp["path_len"],
+                                 inp["k"], inp["v"], inp["alpha"], inp["beta"], inp["S0"])
+    assert st.tolist() == [0, 0]
+    for b, n in enumerate(lens):
+        acc = np.array([inp["path"][b, inp["path_len"][b] - 1]], np.int32)
+        sl = (slice(b, b + 1), slice(0, n))
+        r = oracle.gdn_tree(inp["parent"][sl], oracle.expand_heads(inp["q"], 4)[sl],
+                            oracle.expand_heads(inp["k"], 4)[sl], inp["v"][sl], inp["alpha"][sl],
+                            inp["beta"][sl], inp["S0"][b:b + 1], accept=acc)
+        assert state_rel_err(S[b:b + 1], r["S_accept"]) < 1e-13

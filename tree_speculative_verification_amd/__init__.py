@@ -52,15 +52,16 @@ def load():
     lib.canopy_version.restype = i
     lib.canopy_status_string.argtypes = [i]
     lib.canopy_status_string.restype = ctypes.c_char_p
-    lib.canopy_tree_prep.argtypes = [P, P, i, i, i, P, P, P, P, u64]
+    lib.canopy_tree_prep.argtypes = [P, P, P, i, i, i, P, P, P, P, u64]
     lib.canopy_tree_prep.restype = i
-    lib.canopy_tree_verify.argtypes = [P, P, P, P, P, P, P, i, i, i, i, P, P, P, P, P, P, i, i, u64]
+    lib.canopy_tree_verify.argtypes = [P, P, P, P, P, P, P, P, i, i, i, i, i, P, P, P, P, P, P, i, i,
+                                       u64]
     lib.canopy_tree_verify.restype = i
-    lib.canopy_commit.argtypes = [P, P, i, P, P, P, P, P, i, i, i, P, P, u64]
+    lib.canopy_commit.argtypes = [P, P, i, P, P, P, P, P, P, i, i, i, i, P, P, u64]
     lib.canopy_commit.restype = i
-    lib.canopy_serial_verify.argtypes = [P, P, P, P, P, P, P, i, i, i, i, P, P, P, P, u64]
+    lib.canopy_serial_verify.argtypes = [P, P, P, P, P, P, P, P, i, i, i, i, i, P, P, P, P, u64]
     lib.canopy_serial_verify.restype = i
-    lib.canopy_serial_commit.argtypes = [P, P, P, P, P, i, i, i, P, P, u64]
+    lib.canopy_serial_commit.argtypes = [P, P, P, P, P, P, i, i, i, P, P, u64]
     lib.canopy_serial_commit.restype = i
     _lib = lib
     return lib
@@ -94,6 +95,18 @@ def _req(t, name, dtype=None, shape=None):
     return t
 
 
+def _tree_len(tree_len, B):
+    return None if tree_len is None else _req(tree_len, "tree_len", torch.int32, (B,))
+
+
+def _heads(q, v):
+    """q/k heads H and value heads HV (v's head count); H must divide HV."""
+    H, HV = q.shape[2], v.shape[2]
+    if HV % H:
+        raise ValueError(f"q/k heads ({H}) must divide value heads ({HV})")
+    return H, HV
+
+
 def _in_dtype(q):
     if q.dtype == torch.bfloat16:
         return _BF16
@@ -102,42 +115,49 @@ def _in_dtype(q):
     raise TypeError(f"q, k, v must be bfloat16 or float32, got {q.dtype}")
 
 
-def tree_prep(parent, alpha):
-    """Ancestor bitmask [B,T,ceil(T/32)] (as int32 bit patterns), depth [B,T], ell [B,T,H] and
-    tree status [B], computed on the GPU."""
+def tree_prep(parent, alpha, tree_len=None):
+    """Ancestor bitmask [B,T,ceil(T/32)] (as int32 bit patterns), depth [B,T], ell [B,T,HV] and
+    tree status [B], computed on the GPU. ``tree_len`` ([B] int32) gives ragged node counts;
+    rows past a sequence's count are left unwritten."""
     B, T = parent.shape
     H = alpha.shape[2]
     _req(parent, "parent", torch.int32, (B, T))
     _req(alpha, "alpha", torch.float32, (B, T, H))
+    tl = _tree_len(tree_len, B)
     W = (T + 31) // 32
     dev = parent.device
     mask = torch.empty((B, T, W), dtype=torch.int32, device=dev)
     depth = torch.empty((B, T), dtype=torch.int32, device=dev)
     ell = torch.empty((B, T, H), dtype=torch.float32, device=dev)
     status = torch.empty((B,), dtype=torch.int32, device=dev)
-    _check(load().canopy_tree_prep(_ptr(parent), _ptr(alpha), B, H, T, _ptr(mask), _ptr(depth),
-                                   _ptr(ell), _ptr(status), _stream()))
+    _check(load().canopy_tree_prep(_ptr(parent), _ptr(tl), _ptr(alpha), B, H, T, _ptr(mask),
+                                   _ptr(depth), _ptr(ell), _ptr(status), _stream()))
     return mask, depth, ell, status
 
 
 def tree_verify(q, k, v, alpha, beta, S0, parent, solver="auto", waves=0, structure=False,
-                out=None):
-    """Every node's output O and pseudo-value U ([B,T,H,128] fp32) and ell ([B,T,H] fp32).
-    With ``structure=True`` also returns the ancestor bitmask, depth and tree status.
-    ``out`` may pass preallocated (O, U, ell)."""
+                out=None, tree_len=None):
+    """Every node's output O and pseudo-value U ([B,T,HV,128] fp32) and ell ([B,T,HV] fp32).
+    q and k are [B,T,H,128] with H dividing v's head count HV (value head j reads q/k head
+    j // (HV // H)). ``tree_len`` ([B] int32) gives ragged node counts; rows past a sequence's
+    count are left unwritten. With ``structure=True`` also returns the ancestor bitmask, depth
+    and tree status. ``out`` may pass preallocated (O, U, ell)."""
     B, T, H, d = q.shape
     dt = _in_dtype(q)
-    for name, t in (("q", q), ("k", k), ("v", v)):
+    H, HV = _heads(q, v)
+    for name, t in (("q", q), ("k", k)):
         _req(t, name, q.dtype, (B, T, H, d))
-    _req(alpha, "alpha", torch.float32, (B, T, H))
-    _req(beta, "beta", torch.float32, (B, T, H))
-    _req(S0, "S0", torch.float32, (B, H, d, d))
+    _req(v, "v", q.dtype, (B, T, HV, d))
+    _req(alpha, "alpha", torch.float32, (B, T, HV))
+    _req(beta, "beta", torch.float32, (B, T, HV))
+    _req(S0, "S0", torch.float32, (B, HV, d, d))
     _req(parent, "parent", torch.int32, (B, T))
+    tl = _tree_len(tree_len, B)
     dev = q.device
     if out is None:
-        O = torch.empty((B, T, H, d), dtype=torch.float32, device=dev)
-        U = torch.empty((B, T, H, d), dtype=torch.float32, device=dev)
-        ell = torch.empty((B, T, H), dtype=torch.float32, device=dev)
+        O = torch.empty((B, T, HV, d), dtype=torch.float32, device=dev)
+        U = torch.empty((B, T, HV, d), dtype=torch.float32, device=dev)
+        ell = torch.empty((B, T, HV), dtype=torch.float32, device=dev)
     else:
         O, U, ell = out
     mask = depth = status = None
@@ -146,60 +166,66 @@ def tree_verify(q, k, v, alpha, beta, S0, parent, solver="auto", waves=0, struct
         depth = torch.empty((B, T), dtype=torch.int32, device=dev)
         status = torch.empty((B,), dtype=torch.int32, device=dev)
     _check(load().canopy_tree_verify(_ptr(q), _ptr(k), _ptr(v), _ptr(alpha), _ptr(beta),
-                                     _ptr(S0), _ptr(parent), B, H, T, dt, _ptr(O), _ptr(U),
-                                     _ptr(ell), _ptr(mask), _ptr(depth), _ptr(status),
+                                     _ptr(S0), _ptr(parent), _ptr(tl), B, H, HV, T, dt, _ptr(O),
+                                     _ptr(U), _ptr(ell), _ptr(mask), _ptr(depth), _ptr(status),
                                      SOLVERS[solver], int(waves), _stream()))
     if structure:
         return O, U, ell, mask, depth, status
     return O, U, ell
 
 
-def commit(S0, k, U, alpha, parent, path, path_len, out=None):
-    """State after the accepted path: S_new [B,H,128,128] fp32 (``out`` may be S0 itself for
-    an in-place commit) and the path status [B]."""
+def commit(S0, k, U, alpha, parent, path, path_len, out=None, tree_len=None):
+    """State after the accepted path: S_new [B,HV,128,128] fp32 (``out`` may be S0 itself for
+    an in-place commit) and the path status [B]. k is [B,T,H,128] with H dividing U's head
+    count HV; ``tree_len`` as in ``tree_verify``."""
     B, T, H, d = k.shape
     dt = _in_dtype(k)
-    _req(S0, "S0", torch.float32, (B, H, d, d))
+    H, HV = _heads(k, U)
+    _req(S0, "S0", torch.float32, (B, HV, d, d))
     _req(k, "k", None, (B, T, H, d))
-    _req(U, "U", torch.float32, (B, T, H, d))
-    _req(alpha, "alpha", torch.float32, (B, T, H))
+    _req(U, "U", torch.float32, (B, T, HV, d))
+    _req(alpha, "alpha", torch.float32, (B, T, HV))
     _req(parent, "parent", torch.int32, (B, T))
     _req(path, "path", torch.int32, (B, T))
     _req(path_len, "path_len", torch.int32, (B,))
-    S_new = torch.empty_like(S0) if out is None else _req(out, "out", torch.float32, (B, H, d, d))
+    tl = _tree_len(tree_len, B)
+    S_new = torch.empty_like(S0) if out is None else _req(out, "out", torch.float32, (B, HV, d, d))
     status = torch.empty((B,), dtype=torch.int32, device=k.device)
     _check(load().canopy_commit(_ptr(S0), _ptr(k), dt, _ptr(U), _ptr(alpha), _ptr(parent),
-                                _ptr(path), _ptr(path_len), B, H, T, _ptr(S_new), _ptr(status),
-                                _stream()))
+                                _ptr(tl), _ptr(path), _ptr(path_len), B, H, HV, T, _ptr(S_new),
+                                _ptr(status), _stream()))
     return S_new, status
 
 
-def serial_verify(q, k, v, alpha, beta, S0, parent, snapshots=None):
-    """The serial fork baseline: O, U [B,T,H,128], every node's state snapshot
-    [B,T,H,128,128] and the tree status [B]."""
+def serial_verify(q, k, v, alpha, beta, S0, parent, snapshots=None, tree_len=None):
+    """The serial fork baseline: O, U [B,T,HV,128], every node's state snapshot
+    [B,T,HV,128,128] and the tree status [B]. Heads and ``tree_len`` as in ``tree_verify``."""
     B, T, H, d = q.shape
     dt = _in_dtype(q)
-    for name, t in (("q", q), ("k", k), ("v", v)):
+    H, HV = _heads(q, v)
+    for name, t in (("q", q), ("k", k)):
         _req(t, name, q.dtype, (B, T, H, d))
-    _req(alpha, "alpha", torch.float32, (B, T, H))
-    _req(beta, "beta", torch.float32, (B, T, H))
-    _req(S0, "S0", torch.float32, (B, H, d, d))
+    _req(v, "v", q.dtype, (B, T, HV, d))
+    _req(alpha, "alpha", torch.float32, (B, T, HV))
+    _req(beta, "beta", torch.float32, (B, T, HV))
+    _req(S0, "S0", torch.float32, (B, HV, d, d))
     _req(parent, "parent", torch.int32, (B, T))
+    tl = _tree_len(tree_len, B)
     dev = q.device
-    O = torch.empty((B, T, H, d), dtype=torch.float32, device=dev)
-    U = torch.empty((B, T, H, d), dtype=torch.float32, device=dev)
+    O = torch.empty((B, T, HV, d), dtype=torch.float32, device=dev)
+    U = torch.empty((B, T, HV, d), dtype=torch.float32, device=dev)
     if snapshots is None:
-        snapshots = torch.empty((B, T, H, d, d), dtype=torch.float32, device=dev)
+        snapshots = torch.empty((B, T, HV, d, d), dtype=torch.float32, device=dev)
     else:
-        _req(snapshots, "snapshots", torch.float32, (B, T, H, d, d))
+        _req(snapshots, "snapshots", torch.float32, (B, T, HV, d, d))
     status = torch.empty((B,), dtype=torch.int32, device=dev)
     _check(load().canopy_serial_verify(_ptr(q), _ptr(k), _ptr(v), _ptr(alpha), _ptr(beta),
-                                       _ptr(S0), _ptr(parent), B, H, T, dt, _ptr(O), _ptr(U),
-                                       _ptr(snapshots), _ptr(status), _stream()))
+                                       _ptr(S0), _ptr(parent), _ptr(tl), B, H, HV, T, dt, _ptr(O),
+                                       _ptr(U), _ptr(snapshots), _ptr(status), _stream()))
     return O, U, snapshots, status
 
 
-def serial_commit(snapshots, S0, parent, path, path_len, out=None):
+def serial_commit(snapshots, S0, parent, path, path_len, out=None, tree_len=None):
     """Serial baseline commit: the snapshot of each sequence's accepted node becomes S_new
     (``out`` may be S0 for an in-place commit); returns (S_new, path_status)."""
     B, T, H, d, _ = snapshots.shape
@@ -208,9 +234,10 @@ def serial_commit(snapshots, S0, parent, path, path_len, out=None):
     _req(parent, "parent", torch.int32, (B, T))
     _req(path, "path", torch.int32, (B, T))
     _req(path_len, "path_len", torch.int32, (B,))
+    tl = _tree_len(tree_len, B)
     S_new = torch.empty_like(S0) if out is None else _req(out, "out", torch.float32, (B, H, d, d))
     status = torch.empty((B,), dtype=torch.int32, device=S0.device)
-    _check(load().canopy_serial_commit(_ptr(snapshots), _ptr(S0), _ptr(parent), _ptr(path),
-                                       _ptr(path_len), B, H, T, _ptr(S_new), _ptr(status),
-                                       _stream()))
+    _check(load().canopy_serial_commit(_ptr(snapshots), _ptr(S0), _ptr(parent), _ptr(tl),
+                                       _ptr(path), _ptr(path_len), B, H, T, _ptr(S_new),
+                                       _ptr(status), _stream()))
     return S_new, status

@@ -14,6 +14,9 @@ bool sizes_ok(int B, int H, int T) {
            static_cast<long long>(B) * H * 256 <= 2147483647LL;
 }
 
+// q/k heads H and value heads HV: each q/k head serves HV / H value heads.
+bool heads_ok(int H, int HV) { return H >= 1 && HV >= H && HV % H == 0; }
+
 canopy_status from_hip(hipError_t e) { return e == hipSuccess ? CANOPY_OK : CANOPY_ERR_HIP; }
 
 // Kernels move 16-byte vectors of these arrays; a misaligned view is rejected on the host.
@@ -46,23 +49,24 @@ const char *canopy_status_string(canopy_status s) {
     }
 }
 
-canopy_status canopy_tree_prep(const int32_t *parent, const float *alpha, int B, int H, int T,
-                               uint32_t *anc_mask, int32_t *depth, float *ell,
+canopy_status canopy_tree_prep(const int32_t *parent, const int32_t *tree_len, const float *alpha,
+                               int B, int HV, int T, uint32_t *anc_mask, int32_t *depth, float *ell,
                                int32_t *tree_status, hipStream_t stream) {
-    if (!parent || !alpha || !sizes_ok(B, H, T)) return CANOPY_ERR_ARG;
-    PrepArgs a{parent, alpha, B, H, T, anc_mask, depth, ell, tree_status};
+    if (!parent || !alpha || !sizes_ok(B, HV, T)) return CANOPY_ERR_ARG;
+    PrepArgs a{parent, tree_len, alpha, B, HV, T, anc_mask, depth, ell, tree_status};
     return from_hip(launch_prep(a, stream));
 }
 
 canopy_status canopy_tree_verify(const void *q, const void *k, const void *v,
                                  const float *alpha, const float *beta, const float *S0,
-                                 const int32_t *parent, int B, int H, int T,
-                                 canopy_dtype in_dtype, float *O, float *U, float *ell,
-                                 uint32_t *anc_mask, int32_t *depth, int32_t *tree_status,
-                                 canopy_solver solver, int waves, hipStream_t stream) {
+                                 const int32_t *parent, const int32_t *tree_len, int B, int H,
+                                 int HV, int T, canopy_dtype in_dtype, float *O, float *U,
+                                 float *ell, uint32_t *anc_mask, int32_t *depth,
+                                 int32_t *tree_status, canopy_solver solver, int waves,
+                                 hipStream_t stream) {
     if (!q || !k || !v || !alpha || !beta || !S0 || !parent || !O || !U || !ell)
         return CANOPY_ERR_ARG;
-    if (!sizes_ok(B, H, T)) return CANOPY_ERR_ARG;
+    if (!sizes_ok(B, HV, T) || !heads_ok(H, HV)) return CANOPY_ERR_ARG;
     if (!aligned16(q) || !aligned16(k) || !aligned16(v) || !aligned16(S0)) return CANOPY_ERR_ARG;
     if (in_dtype != CANOPY_FP32 && in_dtype != CANOPY_BF16) return CANOPY_ERR_UNSUPPORTED;
     if (solver != CANOPY_SOLVE_AUTO && solver != CANOPY_SOLVE_FWDSUB &&
@@ -71,8 +75,8 @@ canopy_status canopy_tree_verify(const void *q, const void *k, const void *v,
     if (waves != 0 && waves != 1 && waves != 2 && waves != 4 && waves != 8) return CANOPY_ERR_UNSUPPORTED;
     VerifyArgs a{};
     a.q = q; a.k = k; a.v = v;
-    a.alpha = alpha; a.beta = beta; a.S0 = S0; a.parent = parent;
-    a.B = B; a.H = H; a.T = T;
+    a.alpha = alpha; a.beta = beta; a.S0 = S0; a.parent = parent; a.tree_len = tree_len;
+    a.B = B; a.H = HV; a.HK = H; a.T = T;
     a.bf16 = in_dtype == CANOPY_BF16;
     a.solver = solver;
     a.O = O; a.U = U; a.ell = ell;
@@ -93,7 +97,7 @@ canopy_status canopy_tree_verify(const void *q, const void *k, const void *v,
         (solver == CANOPY_SOLVE_AUTO || solver == CANOPY_SOLVE_FWDSUB)) {
         if (waves == 1 || waves == 2) return from_hip(launch_verify_wide(a, waves, stream));
         if (waves == 0) {
-            const long long heads = static_cast<long long>(B) * H;
+            const long long heads = static_cast<long long>(B) * HV;
             if (heads <= kWideMaxHeads) return from_hip(launch_verify_wide(a, heads <= 32 ? 1 : 2, stream));
         }
     }
@@ -102,40 +106,42 @@ canopy_status canopy_tree_verify(const void *q, const void *k, const void *v,
 
 canopy_status canopy_commit(const float *S0, const void *k, canopy_dtype in_dtype,
                             const float *U, const float *alpha, const int32_t *parent,
-                            const int32_t *path, const int32_t *path_len, int B, int H, int T,
-                            float *S_new, int32_t *path_status, hipStream_t stream) {
+                            const int32_t *tree_len, const int32_t *path, const int32_t *path_len,
+                            int B, int H, int HV, int T, float *S_new, int32_t *path_status,
+                            hipStream_t stream) {
     if (!S0 || !k || !U || !alpha || !parent || !path || !path_len || !S_new) return CANOPY_ERR_ARG;
-    if (!sizes_ok(B, H, T)) return CANOPY_ERR_ARG;
+    if (!sizes_ok(B, HV, T) || !heads_ok(H, HV)) return CANOPY_ERR_ARG;
     if (!aligned16(S0) || !aligned16(k) || !aligned16(U) || !aligned16(S_new)) return CANOPY_ERR_ARG;
     if (in_dtype != CANOPY_FP32 && in_dtype != CANOPY_BF16) return CANOPY_ERR_UNSUPPORTED;
-    CommitArgs a{S0, k, in_dtype == CANOPY_BF16, U, alpha, parent, path, path_len,
-                 B, H, T, S_new, path_status};
+    CommitArgs a{S0, k, in_dtype == CANOPY_BF16, U, alpha, parent, tree_len, path, path_len,
+                 B, HV, H, T, S_new, path_status};
     return from_hip(launch_commit(a, stream));
 }
 
 canopy_status canopy_serial_verify(const void *q, const void *k, const void *v,
                                    const float *alpha, const float *beta, const float *S0,
-                                   const int32_t *parent, int B, int H, int T,
-                                   canopy_dtype in_dtype, float *O, float *U, float *snapshots,
-                                   int32_t *tree_status, hipStream_t stream) {
+                                   const int32_t *parent, const int32_t *tree_len, int B, int H,
+                                   int HV, int T, canopy_dtype in_dtype, float *O, float *U,
+                                   float *snapshots, int32_t *tree_status, hipStream_t stream) {
     if (!q || !k || !v || !alpha || !beta || !S0 || !parent || !O || !U || !snapshots)
         return CANOPY_ERR_ARG;
-    if (!sizes_ok(B, H, T)) return CANOPY_ERR_ARG;
+    if (!sizes_ok(B, HV, T) || !heads_ok(H, HV)) return CANOPY_ERR_ARG;
     if (!aligned16(S0) || !aligned16(v) || !aligned16(O) || !aligned16(U) || !aligned16(snapshots))
         return CANOPY_ERR_ARG;
     if (in_dtype != CANOPY_FP32 && in_dtype != CANOPY_BF16) return CANOPY_ERR_UNSUPPORTED;
-    SerialArgs a{q, k, v, alpha, beta, S0, parent, B, H, T, in_dtype == CANOPY_BF16,
+    SerialArgs a{q, k, v, alpha, beta, S0, parent, tree_len, B, HV, H, T, in_dtype == CANOPY_BF16,
                  O, U, snapshots, tree_status};
     return from_hip(launch_serial(a, stream));
 }
 
 canopy_status canopy_serial_commit(const float *snapshots, const float *S0, const int32_t *parent,
-                                   const int32_t *path, const int32_t *path_len, int B, int H, int T,
-                                   float *S_new, int32_t *path_status, hipStream_t stream) {
+                                   const int32_t *tree_len, const int32_t *path,
+                                   const int32_t *path_len, int B, int HV, int T, float *S_new,
+                                   int32_t *path_status, hipStream_t stream) {
     if (!snapshots || !S0 || !parent || !path || !path_len || !S_new) return CANOPY_ERR_ARG;
-    if (!sizes_ok(B, H, T)) return CANOPY_ERR_ARG;
+    if (!sizes_ok(B, HV, T)) return CANOPY_ERR_ARG;
     if (!aligned16(snapshots) || !aligned16(S0) || !aligned16(S_new)) return CANOPY_ERR_ARG;
-    SerialCommitArgs a{snapshots, S0, parent, path, path_len, B, H, T, S_new, path_status};
+    SerialCommitArgs a{snapshots, S0, parent, tree_len, path, path_len, B, HV, T, S_new, path_status};
     return from_hip(launch_serial_commit(a, stream));
 }
 

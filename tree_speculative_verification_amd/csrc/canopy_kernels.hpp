@@ -6,11 +6,14 @@
 
 namespace canopy {
 
+// Head counts: H is the number of value heads (v, alpha, beta, S0, O, U, ell, states); q and
+// k have HK heads, HK dividing H, and value head h reads q/k head h / (H / HK). tree_len, when
+// not null, gives each sequence's node count (1..T); arrays keep their T-row extent.
 struct VerifyArgs {
     const void *q, *k, *v;
     const float *alpha, *beta, *S0;
-    const int32_t *parent;
-    int B, H, T;
+    const int32_t *parent, *tree_len;
+    int B, H, HK, T;
     int bf16;    // 1: q, k, v are bf16 bit patterns; 0: fp32
     int solver;  // a canopy_solver value
     float *O, *U, *ell;
@@ -19,7 +22,7 @@ struct VerifyArgs {
 };
 
 struct PrepArgs {
-    const int32_t *parent;
+    const int32_t *parent, *tree_len;
     const float *alpha;
     int B, H, T;
     uint32_t *anc_mask;
@@ -33,8 +36,8 @@ struct CommitArgs {
     const void *k;
     int bf16;
     const float *U, *alpha;
-    const int32_t *parent, *path, *path_len;
-    int B, H, T;
+    const int32_t *parent, *tree_len, *path, *path_len;
+    int B, H, HK, T;
     float *S_new;
     int32_t *path_status;
 };
@@ -42,8 +45,8 @@ struct CommitArgs {
 struct SerialArgs {
     const void *q, *k, *v;
     const float *alpha, *beta, *S0;
-    const int32_t *parent;
-    int B, H, T;
+    const int32_t *parent, *tree_len;
+    int B, H, HK, T;
     int bf16;
     float *O, *U, *snap;
     int32_t *tree_status;
@@ -51,11 +54,31 @@ struct SerialArgs {
 
 struct SerialCommitArgs {
     const float *snap, *S0;
-    const int32_t *parent, *path, *path_len;
+    const int32_t *parent, *tree_len, *path, *path_len;
     int B, H, T;
     float *S_new;
     int32_t *path_status;
 };
+
+// The node count of sequence b: tree_len[b], or T without a length array. A length outside
+// 1..T is reported (bad = true) and the whole T-row extent is then treated as that sequence's
+// tree, whose outputs the kernels replace by NaN.
+struct SeqLen {
+    int n;
+    bool bad;
+};
+__device__ __forceinline__ SeqLen seq_len(const int32_t *tree_len, int b, int T) {
+    if (!tree_len) return {T, false};
+    const int n = tree_len[b];
+    const bool ok = n >= 1 && n <= T;
+    return {ok ? n : T, !ok};
+}
+
+// Offset of (sequence b, node 0, q/k head of value head h, column 0) in a q or k array of HK
+// heads (node stride HK * 128 elements).
+__device__ __forceinline__ size_t qk_base(int b, int h, int H, int HK, int T) {
+    return (static_cast<size_t>(b) * T * HK + h / (H / HK)) * 128;
+}
 
 hipError_t launch_verify(const VerifyArgs &a, int waves, hipStream_t stream);
 hipError_t launch_verify_small(const VerifyArgs &a, int waves, hipStream_t stream);

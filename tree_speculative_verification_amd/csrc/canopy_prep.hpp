@@ -35,8 +35,10 @@ struct PrepIn {
     }
 };
 
-// All NT threads of the block call this. Returns 0 for a valid tree, else 1 + the first node
-// whose parent lies outside -1..i-1 (the block's result is then undefined apart from that).
+// All NT threads of the block call this, T being the tree's node count (nodes at or past T are
+// not part of it, whatever the inputs hold there). Returns 0 for a valid tree, else 1 + the
+// first node whose parent lies outside -1..i-1 (the block's result is then undefined apart
+// from that).
 //
 // The nodes are cut into 64-node chunks, one wave (one lane per node) per chunk at a time.
 // Inside a chunk, pointer jumping over lane shuffles gathers, for every node, the mask bits,
@@ -108,12 +110,13 @@ __device__ int tree_prep_compute(PrepSmem<MAXT> &s, const PrepIn<MAXT, NT> &in, 
     return 0;
 }
 
+// T: the arrays' node extent (loads stay below it); n: the tree's node count (n <= T).
 template <int MAXT, int NT>
 __device__ int tree_prep_block(PrepSmem<MAXT> &s, const int32_t *parent_b, const float *alpha_h,
-                               int astride, int T) {
+                               int astride, int T, int n) {
     PrepIn<MAXT, NT> in;
     in.load(parent_b, alpha_h, astride, T);
-    return tree_prep_compute<MAXT, NT>(s, in, T);
+    return tree_prep_compute<MAXT, NT>(s, in, n);
 }
 
 // Popcount of a node's mask row, minus one: |A(i)|.

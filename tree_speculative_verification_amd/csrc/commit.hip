@@ -26,6 +26,11 @@ constexpr int CROWS = 8;  // state rows per wave
 // nodes), and a slot past the path still costs a load, so small groups beat fewer round trips.
 constexpr int CGRP = 4;
 
+// Where a node's rows start: U (value head, node stride rs) and k (its q/k head, stride krs).
+struct Rows {
+    size_t base, rs, kbase, krs;
+};
+
 // U rows (float4 column c4) and key words (4 state rows from krow) of NG path positions
 // first .. first+NG-1, the positions' node ids broadcast from the lanes that hold them. Slots
 // past the chunk's last position repeat its node and get weight 0.
@@ -33,19 +38,20 @@ template <bool BF, int NG>
 struct NodeGroup {
     float4 u[NG];
     uint32_t k[NG][BF ? 2 : 4];
-    __device__ __forceinline__ void load(const CommitArgs &a, size_t base, size_t rs, int krow, int c4,
-                                         int ndc, int first, int lastpos) {
+    __device__ __forceinline__ void load(const CommitArgs &a, const Rows &rw, int krow, int c4, int ndc,
+                                         int first, int lastpos) {
 #pragma unroll
         for (int tt = 0; tt < NG; ++tt) {
             const int n = __builtin_amdgcn_readlane(ndc, min(first + tt, lastpos));
-            const size_t ro = base + static_cast<size_t>(n) * rs;
+            const size_t ro = rw.base + static_cast<size_t>(n) * rw.rs;
+            const size_t ko = rw.kbase + static_cast<size_t>(n) * rw.krs + krow;
             u[tt] = reinterpret_cast<const float4 *>(a.U + ro)[c4];
             if constexpr (BF) {
-                const uint2 w = *reinterpret_cast<const uint2 *>(static_cast<const uint16_t *>(a.k) + ro + krow);
+                const uint2 w = *reinterpret_cast<const uint2 *>(static_cast<const uint16_t *>(a.k) + ko);
                 k[tt][0] = w.x;
                 k[tt][1] = w.y;
             } else {
-                const u32x4 w = *reinterpret_cast<const u32x4 *>(static_cast<const float *>(a.k) + ro + krow);
+                const u32x4 w = *reinterpret_cast<const u32x4 *>(static_cast<const float *>(a.k) + ko);
 #pragma unroll
                 for (int e = 0; e < 4; ++e) k[tt][e] = w[e];
             }
@@ -84,17 +90,17 @@ struct Chunk {
     float al;
     NodeGroup<BF, NG> grp;
     __device__ __forceinline__ void issue(const CommitArgs &a, const int32_t *par, int c_, int mv, int nd_,
-                                          size_t base, size_t rs, size_t abase, int krow, int c4) {
+                                          const Rows &rw, size_t abase, int krow, int c4) {
         c = c_;
         nd = nd_;
         ndc = min(max(nd, 0), a.T - 1);
         cnt = min(64, mv - 64 * c);  // positions in this chunk (at least 1)
         par_nd = par[ndc];
         al = a.alpha[abase + static_cast<size_t>(ndc) * a.H];
-        grp.load(a, base, rs, krow, c4, ndc, 0, cnt - 1);
+        grp.load(a, rw, krow, c4, ndc, 0, cnt - 1);
     }
     // prev_last: the node at position 64c - 1 (unused for c = 0); on return, the node at 64c + 63.
-    __device__ __forceinline__ void finish(const CommitArgs &a, int mv, size_t base, size_t rs, int krow,
+    __device__ __forceinline__ void finish(const CommitArgs &a, int mv, int Tb, const Rows &rw, int krow,
                                            int c4, float4 (&acc)[4], double &tot, int &prev_last,
                                            int &bad) const {
         const int lane = threadIdx.x;
@@ -103,7 +109,7 @@ struct Chunk {
         // path check: position t holds a node in range whose parent is position t-1's node
         const int up = __shfl_up(nd, 1, 64);
         const int prev = t == 0 ? -1 : (lane == 0 ? prev_last : up);
-        const bool ok = (!inp) | ((nd >= 0) & (nd < a.T) & (par_nd == prev));
+        const bool ok = (!inp) | ((nd >= 0) & (nd < Tb) & (par_nd == prev));
         const unsigned long long badm = __ballot(!ok);
         if (badm) bad = min(bad, 64 * c + __ffsll(static_cast<unsigned long long>(badm)));
         prev_last = __builtin_amdgcn_readlane(nd, 63);
@@ -131,7 +137,7 @@ struct Chunk {
         grp.apply(acc, w, 0, cnt);
         for (int g0 = NG; g0 < cnt; g0 += NG) {  // more than NG positions in this chunk
             NodeGroup<BF, NG> more;
-            more.load(a, base, rs, krow, c4, ndc, g0, cnt - 1);
+            more.load(a, rw, krow, c4, ndc, g0, cnt - 1);
             more.apply(acc, w, g0, cnt);
         }
     }
@@ -149,20 +155,21 @@ __global__ __launch_bounds__(64) void commit_kernel(CommitArgs a) {
     const int krow = chunk * CROWS + 4 * (lane >> 5);    // first of this lane's 4 rows
     const int32_t *pb = a.path + static_cast<size_t>(b) * T;
     const int32_t *par = a.parent + static_cast<size_t>(b) * T;
-    const size_t rs = static_cast<size_t>(H) * D;
-    const size_t base = (static_cast<size_t>(b) * T * H + h) * D;
+    const Rows rw{(static_cast<size_t>(b) * T * H + h) * D, static_cast<size_t>(H) * D,
+                  qk_base(b, h, H, a.HK, T), static_cast<size_t>(a.HK) * D};
     const size_t abase = static_cast<size_t>(b) * T * H + h;
 
     // ---- round 1
     const int m = a.path_len[b];
+    const SeqLen sl = seq_len(a.tree_len, b, T);
     const int nd0 = pb[min(lane, T - 1)];
-    const bool lenok = m >= 0 && m <= T;
+    const bool lenok = !sl.bad && m >= 0 && m <= sl.n;
     const int mv = lenok ? m : 0;
     const int nch = (mv + 63) / 64;
     // ---- round 2: the first chunk's parents, alphas, U rows and keys, then this wave's rows of
     // S0, which are needed last (requests return in order)
     Chunk<BF, NG> first;
-    first.issue(a, par, 0, max(mv, 1), nd0, base, rs, abase, krow, c4);
+    first.issue(a, par, 0, max(mv, 1), nd0, rw, abase, krow, c4);
     __builtin_amdgcn_sched_barrier(0);
     const float *S0 = a.S0 + static_cast<size_t>(bh) * D * D;
     float4 s0[4];
@@ -175,11 +182,11 @@ __global__ __launch_bounds__(64) void commit_kernel(CommitArgs a) {
     for (int q = 0; q < 4; ++q) acc[q] = make_float4(0.f, 0.f, 0.f, 0.f);
     double tot = 0.0;  // log2 of the decay over the chunks folded in so far
     int prev_last = -1, bad = INT_MAX;
-    if (nch > 0) first.finish(a, mv, base, rs, krow, c4, acc, tot, prev_last, bad);
+    if (nch > 0) first.finish(a, mv, sl.n, rw, krow, c4, acc, tot, prev_last, bad);
     for (int c = 1; c < nch; ++c) {  // paths longer than 64 nodes
         Chunk<BF, NG> ch;
-        ch.issue(a, par, c, mv, pb[min(64 * c + lane, T - 1)], base, rs, abase, krow, c4);
-        ch.finish(a, mv, base, rs, krow, c4, acc, tot, prev_last, bad);
+        ch.issue(a, par, c, mv, pb[min(64 * c + lane, T - 1)], rw, abase, krow, c4);
+        ch.finish(a, mv, sl.n, rw, krow, c4, acc, tot, prev_last, bad);
     }
     const int st = !lenok ? -1 : (bad == INT_MAX ? 0 : bad);
     if (a.path_status && h == 0 && chunk == 0 && lane == 0) a.path_status[b] = st;

@@ -13,17 +13,20 @@ __global__ __launch_bounds__(256) void prep_kernel(PrepArgs a) {
     const int H = a.H, T = a.T;
     const int b = bh / H, h = bh % H;
     const size_t sbase = static_cast<size_t>(b) * T * H + h;
-    const int bad = tree_prep_block<MAXT, NT>(ps, a.parent + static_cast<size_t>(b) * T,
-                                              a.alpha + sbase, H, T);
+    const SeqLen sl = seq_len(a.tree_len, b, T);
+    const int Tb = sl.n;  // this sequence's node count
+    const int pbad = tree_prep_block<MAXT, NT>(ps, a.parent + static_cast<size_t>(b) * T,
+                                               a.alpha + sbase, H, T, Tb);
+    const int bad = sl.bad ? -1 : pbad;
     const int tid = threadIdx.x;
     if (a.ell)
-        for (int i = tid; i < T; i += NT)
+        for (int i = tid; i < Tb; i += NT)
             a.ell[sbase + static_cast<size_t>(i) * H] =
                 bad ? __builtin_nanf("") : static_cast<float>(ps.ell[i]);
     if (h != 0) return;
     if (a.tree_status && tid == 0) a.tree_status[b] = bad;
     const int W = (T + 31) >> 5;
-    for (int i = tid; i < T; i += NT) {
+    for (int i = tid; i < Tb; i += NT) {
         if (a.depth) a.depth[static_cast<size_t>(b) * T + i] = bad ? 0 : node_depth<MAXT>(ps, i);
         if (a.anc_mask)
             for (int w = 0; w < W; ++w)

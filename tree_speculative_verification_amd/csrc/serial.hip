@@ -26,10 +26,13 @@ __global__ __launch_bounds__(64) void serial_kernel(SerialArgs a) {
     const size_t rs = static_cast<size_t>(H) * D;
     const size_t base = (static_cast<size_t>(b) * T * H + h) * D;
     const size_t sbase = static_cast<size_t>(b) * T * H + h;
+    const size_t qkbase = qk_base(b, h, H, a.HK, T), qkrs = static_cast<size_t>(a.HK) * D;
     const size_t SS = static_cast<size_t>(D) * D;
+    const SeqLen sl = seq_len(a.tree_len, b, T);
+    const int Tb = sl.n;  // this sequence's node count: nodes past it are padding
 
-    int bad = INT_MAX;
-    for (int i = lane; i < T; i += 64) {
+    int bad = sl.bad ? -1 : INT_MAX;
+    for (int i = lane; i < Tb; i += 64) {
         const int p = par[i];
         if (p < -1 || p >= i) bad = min(bad, i + 1);
     }
@@ -38,7 +41,7 @@ __global__ __launch_bounds__(64) void serial_kernel(SerialArgs a) {
     if (a.tree_status && tile == 0 && h == 0 && lane == 0) a.tree_status[b] = bad == INT_MAX ? 0 : bad;
     if (bad != INT_MAX) {
         const float qnan = __builtin_nanf("");
-        for (int i = rg; i < T; i += 16) {
+        for (int i = rg; i < Tb; i += 16) {
             reinterpret_cast<float4 *>(a.O + base + i * rs + col)[0] = make_float4(qnan, qnan, qnan, qnan);
             reinterpret_cast<float4 *>(a.U + base + i * rs + col)[0] = make_float4(qnan, qnan, qnan, qnan);
         }
@@ -47,7 +50,7 @@ __global__ __launch_bounds__(64) void serial_kernel(SerialArgs a) {
 
     float4 S[8];
     int cur = -2;  // node whose state the registers hold
-    for (int i = 0; i < T; ++i) {
+    for (int i = 0; i < Tb; ++i) {
         const int p = par[i];
         if (p != cur) {
             const float *src = (p < 0) ? a.S0 + static_cast<size_t>(bh) * SS
@@ -58,12 +61,13 @@ __global__ __launch_bounds__(64) void serial_kernel(SerialArgs a) {
             for (int m = 0; m < 8; ++m) S[m] = reinterpret_cast<const float4 *>(src + (rg + 16 * m) * D + col)[0];
         }
         const size_t node = base + static_cast<size_t>(i) * rs;
+        const size_t qknode = qkbase + static_cast<size_t>(i) * qkrs;
         const float al = a.alpha[sbase + static_cast<size_t>(i) * H];
         const float be = a.beta[sbase + static_cast<size_t>(i) * H];
         float kv[8], qv[8];
 #pragma unroll
         for (int m = 0; m < 8; ++m) {
-            const size_t el = node + rg + 16 * m;
+            const size_t el = qknode + rg + 16 * m;
             kv[m] = BF ? bf16_to_f32(static_cast<const uint16_t *>(a.k)[el]) : static_cast<const float *>(a.k)[el];
             qv[m] = BF ? bf16_to_f32(static_cast<const uint16_t *>(a.q)[el]) : static_cast<const float *>(a.q)[el];
         }
@@ -122,14 +126,15 @@ __global__ __launch_bounds__(256) void serial_commit_kernel(SerialCommitArgs a) 
     const int b = bh / H, h = bh % H;
     const int tid = threadIdx.x;
     const int m = a.path_len[b];
+    const SeqLen sl = seq_len(a.tree_len, b, T);
     const int32_t *pb = a.path + static_cast<size_t>(b) * T;
     const int32_t *par = a.parent + static_cast<size_t>(b) * T;
-    if (tid == 0) s_bad = (m < 0 || m > T) ? -1 : INT_MAX;
+    if (tid == 0) s_bad = (sl.bad || m < 0 || m > sl.n) ? -1 : INT_MAX;
     __syncthreads();
     if (s_bad == INT_MAX)
         for (int t = tid; t < m; t += 256) {
             const int n = pb[t];
-            if (!(n >= 0 && n < T && par[n] == (t == 0 ? -1 : pb[t - 1]))) atomicMin(&s_bad, t + 1);
+            if (!(n >= 0 && n < sl.n && par[n] == (t == 0 ? -1 : pb[t - 1]))) atomicMin(&s_bad, t + 1);
         }
     __syncthreads();
     const int st = (s_bad == INT_MAX) ? 0 : s_bad;

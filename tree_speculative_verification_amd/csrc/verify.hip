@@ -248,6 +248,10 @@ __global__ __launch_bounds__(NW * 64) void verify_kernel(VerifyArgs a) {
     const size_t rs = static_cast<size_t>(H) * D;                  // node stride (elements)
     const size_t base = (static_cast<size_t>(b) * T * H + h) * D;  // (b, node 0, h, col 0)
     const size_t sbase = (static_cast<size_t>(b) * T * H + h);     // (b, node 0, h) scalars
+    const size_t qkrs = static_cast<size_t>(a.HK) * D;              // q/k node stride
+    const size_t qkbase = qk_base(b, h, H, a.HK, T);                // (b, node 0, q/k head, col 0)
+    const SeqLen sl = seq_len(a.tree_len, b, T);
+    const int Tb = sl.n;  // this sequence's node count: rows past it are padding
     float(*Xc)[XS] = s_x[wave];  // Xc[column][row]
 
     // ---- loads, latency-critical first: the tree, then block 0 of K and Q, S0, V
@@ -259,8 +263,8 @@ __global__ __launch_bounds__(NW * 64) void verify_kernel(VerifyArgs a) {
         bet[t] = a.beta[sbase + static_cast<size_t>(min(tid + t * NT, T - 1)) * H];
     BC pk, pq;
     if constexpr (kPF) {
-        pk.issue(a.k, base, rs, 0, T);
-        pq.issue(a.q, base, rs, 0, T);
+        pk.issue(a.k, qkbase, qkrs, 0, T);
+        pq.issue(a.q, qkbase, qkrs, 0, T);
     }
     float s0v[4][8];
     {
@@ -273,22 +277,23 @@ __global__ __launch_bounds__(NW * 64) void verify_kernel(VerifyArgs a) {
     VCopy<BF> pv;  // this wave's 16 value columns of a 64-row block
     pv.issue(a.v, base, rs, col0, 0, T, lane);
 
-    const int bad = tree_prep_compute<MAXT, NT>(ps, pin, T);
+    const int pbad = tree_prep_compute<MAXT, NT>(ps, pin, Tb);
+    const int bad = sl.bad ? -1 : pbad;
     if (bad) {
         const float qnan = __builtin_nanf("");
-        for (int i = lg; i < T; i += 4) {
+        for (int i = lg; i < Tb; i += 4) {
             a.O[base + i * rs + col0 + lr] = qnan;
             a.U[base + i * rs + col0 + lr] = qnan;
         }
         if (tile == 0)
-            for (int i = tid; i < T; i += NT) a.ell[sbase + static_cast<size_t>(i) * H] = qnan;
+            for (int i = tid; i < Tb; i += NT) a.ell[sbase + static_cast<size_t>(i) * H] = qnan;
         if (tile == 0 && h == 0) {
             const int W = (T + 31) >> 5;
             if (a.tree_status && tid == 0) a.tree_status[b] = bad;
             if (a.depth)
-                for (int i = tid; i < T; i += NT) a.depth[static_cast<size_t>(b) * T + i] = 0;
+                for (int i = tid; i < Tb; i += NT) a.depth[static_cast<size_t>(b) * T + i] = 0;
             if (a.anc_mask)
-                for (int x = tid; x < T * W; x += NT) a.anc_mask[static_cast<size_t>(b) * T * W + x] = 0u;
+                for (int x = tid; x < Tb * W; x += NT) a.anc_mask[static_cast<size_t>(b) * T * W + x] = 0u;
         }
         return;
     }
@@ -298,18 +303,18 @@ __global__ __launch_bounds__(NW * 64) void verify_kernel(VerifyArgs a) {
         const int i = tid + t * NT;
         if (i < MAXT) {
             float P = 0.f;
-            if (i < T) {
+            if (i < Tb) {
                 P = static_cast<float>(exp(ps.ell[i]));
                 if (tile == 0) a.ell[sbase + static_cast<size_t>(i) * H] = static_cast<float>(ps.ell[i]);
             }
-            s_beta[i] = (i < T) ? bet[t] : 0.f;
+            s_beta[i] = (i < Tb) ? bet[t] : 0.f;
             s_P[i] = P;
         }
     }
     if (tile == 0 && h == 0) {
         const int W = (T + 31) >> 5;
         if (a.tree_status && tid == 0) a.tree_status[b] = 0;
-        for (int i = tid; i < T; i += NT) {
+        for (int i = tid; i < Tb; i += NT) {
             if (a.depth) a.depth[static_cast<size_t>(b) * T + i] = node_depth<MAXT>(ps, i);
             if (a.anc_mask)
                 for (int w = 0; w < W; ++w)
@@ -320,8 +325,8 @@ __global__ __launch_bounds__(NW * 64) void verify_kernel(VerifyArgs a) {
         pk.commit(s_ka);
         pq.commit(s_qa);
     } else {
-        copy_block<BF, NT>(s_ka, a.k, base, rs, 0, T);
-        copy_block<BF, NT>(s_qa, a.q, base, rs, 0, T);
+        copy_block<BF, NT>(s_ka, a.k, qkbase, qkrs, 0, T);
+        copy_block<BF, NT>(s_qa, a.q, qkbase, qkrs, 0, T);
     }
     pv.commit(s_v[wave], lane);
     // S0 columns of this wave as B operands of K S0 and Q S0 (reduction index = key row).
@@ -331,7 +336,7 @@ __global__ __launch_bounds__(NW * 64) void verify_kernel(VerifyArgs a) {
     __syncthreads();
 
     Sp uf[NB][2];  // U of every solved block, as B operands (reduction index = node)
-    const int nb = (T + 63) >> 6;
+    const int nb = (Tb + 63) >> 6;
 
 #pragma unroll
     for (int r = 0; r < NB; ++r) {
@@ -342,7 +347,7 @@ __global__ __launch_bounds__(NW * 64) void verify_kernel(VerifyArgs a) {
         for (int ti = 0; ti < 4; ++ti) {
             const int i0 = 64 * r + 16 * ti;
             f32x4 ak = {0.f, 0.f, 0.f, 0.f}, aq = {0.f, 0.f, 0.f, 0.f};
-            if (i0 < T) {
+            if (i0 < Tb) {
 #pragma unroll
                 for (int ks = 0; ks < 4; ++ks) {
                     const In kf = Op::lds_frag(s_ka, 16 * ti + lr, 4 * ks + lg);
@@ -355,7 +360,7 @@ __global__ __launch_bounds__(NW * 64) void verify_kernel(VerifyArgs a) {
             for (int e = 0; e < 4; ++e) {
                 const int i = i0 + 4 * lg + e;
                 float rv = 0.f, ov = 0.f;
-                if (i < T) {
+                if (i < Tb) {
                     rv = s_beta[i] * (VCopy<BF>::get(s_v[wave], 16 * ti + 4 * lg + e, lr) - s_P[i] * ak[e]);
                     ov = s_P[i] * aq[e];
                 }
@@ -374,7 +379,7 @@ __global__ __launch_bounds__(NW * 64) void verify_kernel(VerifyArgs a) {
             for (int p = wave; p < 16; p += NW) {
                 const int ti = p >> 2, tj = p & 3;
                 const int i0 = 64 * r + 16 * ti, j0 = 64 * c + 16 * tj;
-                const bool need = (i0 < T) && (j0 < T) && (c < r || tj <= ti);
+                const bool need = (i0 < Tb) && (j0 < Tb) && (c < r || tj <= ti);
                 if (!need) {
                     st.zero_tile(16 * ti, 16 * tj, lane);
                     continue;
@@ -413,7 +418,7 @@ __global__ __launch_bounds__(NW * 64) void verify_kernel(VerifyArgs a) {
             if (c < r) {
                 // K_c is no longer needed: request K_{c+1} for the next pair of this block.
                 const bool more = c + 1 < r;
-                if (more) dma_block<BF, NT>(s_kb, a.k, base, rs, 64 * (c + 1), T);
+                if (more) dma_block<BF, NT>(s_kb, a.k, qkbase, qkrs, 64 * (c + 1), T);
                 // ---- a4/a5: couplings to the solved block c
 #pragma unroll
                 for (int ti = 0; ti < 4; ++ti) {
@@ -432,17 +437,17 @@ __global__ __launch_bounds__(NW * 64) void verify_kernel(VerifyArgs a) {
                 // and V or K_c any more (the solve and the read-out use the stage): request
                 // the next block's K, Q, V and K_0 now, to land during the solve.
                 if (next) {
-                    dma_block<BF, NT>(s_ka, a.k, base, rs, 64 * (r + 1), T);
-                    dma_block<BF, NT>(s_qa, a.q, base, rs, 64 * (r + 1), T);
-                    if (NB > 1) dma_block<BF, NT>(s_kb, a.k, base, rs, 0, T);
+                    dma_block<BF, NT>(s_ka, a.k, qkbase, qkrs, 64 * (r + 1), T);
+                    dma_block<BF, NT>(s_qa, a.q, qkbase, qkrs, 64 * (r + 1), T);
+                    if (NB > 1) dma_block<BF, NT>(s_kb, a.k, qkbase, qkrs, 0, T);
                     dma_v<BF>(s_v[wave], a.v, base, rs, col0, 64 * (r + 1), T, lane);
                 }
                 // ---- a4: the diagonal block, per wave on its 16 columns
                 const int ib = 64 * r + lane;
                 uint64_t bm = 0;
-                if (ib < T)
+                if (ib < Tb)
                     bm = (static_cast<uint64_t>(ps.mask[ib][2 * r + 1]) << 32) | ps.mask[ib][2 * r];
-                const int ld = (ib < T) ? __popcll(bm) - 1 : -1;
+                const int ld = (ib < Tb) ? __popcll(bm) - 1 : -1;
                 const int maxld = wave_max(ld);
                 const bool use_level = a.solver == CANOPY_SOLVE_LEVEL ||
                                        (a.solver == CANOPY_SOLVE_AUTO && maxld <= kLevelMaxDepth);
@@ -458,10 +463,10 @@ __global__ __launch_bounds__(NW * 64) void verify_kernel(VerifyArgs a) {
                     // placement.
                     constexpr int NINV = NW < 4 ? NW : 4;
                     for (int p = wave; p < 4; p += NINV) {
-                        if (64 * r + 16 * p >= T) break;
+                        if (64 * r + 16 * p >= Tb) break;
                         const int ip = 64 * r + 16 * p + lr;  // this lane's row in the sub-block
-                        const uint32_t wbits = (ip < T) ? ps.mask[ip][(2 * r) + (p >> 1)] : 0u;
-                        const int dl = (ip < T) ? __popc((wbits >> (16 * (p & 1))) & 0xFFFFu) - 1 : -1;
+                        const uint32_t wbits = (ip < Tb) ? ps.mask[ip][(2 * r) + (p >> 1)] : 0u;
+                        const int dl = (ip < Tb) ? __popc((wbits >> (16 * (p & 1))) & 0xFFFFu) - 1 : -1;
                         const int dp = wave_max(dl);
                         int nf = 0;
                         while ((1 << nf) <= dp) ++nf;
@@ -603,14 +608,14 @@ __global__ __launch_bounds__(NW * 64) void verify_kernel(VerifyArgs a) {
                 for (int m = 0; m < 16; ++m) {
                     const int rl = lg + 4 * m;
                     const int i = 64 * r + rl;
-                    if (i < T) a.U[base + static_cast<size_t>(i) * rs + col0 + lr] = Xc[lr][rl];
+                    if (i < Tb) a.U[base + static_cast<size_t>(i) * rs + col0 + lr] = Xc[lr][rl];
                 }
 #pragma unroll
                 for (int ti = 0; ti < 4; ++ti)
 #pragma unroll
                     for (int e = 0; e < 4; ++e) {
                         const int i = 64 * r + 16 * ti + 4 * lg + e;
-                        if (i < T) a.O[base + static_cast<size_t>(i) * rs + col0 + lr] = oacc[ti][e];
+                        if (i < Tb) a.O[base + static_cast<size_t>(i) * rs + col0 + lr] = oacc[ti][e];
                     }
             }
             // The stage is free and the next operands are in LDS for every wave.

@@ -80,21 +80,25 @@ __global__ __launch_bounds__(64 * NSB) void verify_mid_kernel(VerifyArgs a) {
     const size_t rs = static_cast<size_t>(H) * D;
     const size_t base = (static_cast<size_t>(b) * T * H + h) * D;
     const size_t sbase = static_cast<size_t>(b) * T * H + h;
+    const size_t qkrs = static_cast<size_t>(a.HK) * D;
+    const size_t qkbase = qk_base(b, h, H, a.HK, T);
+    const SeqLen sl = seq_len(a.tree_len, b, T);
+    const int Tb = sl.n;  // this sequence's node count
     const bool writer = grp == 0 && p == 0;  // this head's wave for the per-node outputs
 
-    // ---- every load up front, unconditional (rows and nodes past T read row or node T-1 and
-    // are masked later): tree and gates (lane = node), the wave's own K and Q rows, the
+    // ---- every load up front, unconditional (rows and nodes past T read row or node T-1;
+    // rows and nodes past Tb are padding, dropped by selects later): tree and gates (lane = node), the wave's own K and Q rows, the
     // thread's share of the S0 columns (column c, reduction indices 8kc .. 8kc+7) and the
     // wave's V rows.
     const int node = lane;
-    const bool real = node < T;
+    const bool real = node < Tb;
     const int nodec = min(node, T - 1);
     const int par_in = a.parent[static_cast<size_t>(b) * T + nodec];
     const float alpha_in = a.alpha[sbase + static_cast<size_t>(nodec) * H];
     const float beta_in = a.beta[sbase + static_cast<size_t>(nodec) * H];
     In kp[4], qp[4];
     {
-        const size_t er = base + static_cast<size_t>(min(16 * p + lr, T - 1)) * rs + 8 * lg;
+        const size_t er = qkbase + static_cast<size_t>(min(16 * p + lr, T - 1)) * qkrs + 8 * lg;
 #pragma unroll
         for (int ks = 0; ks < 4; ++ks) {
             kp[ks] = Op::template load_frag<In>(a.k, er + 32 * ks, true);
@@ -126,7 +130,8 @@ __global__ __launch_bounds__(64 * NSB) void verify_mid_kernel(VerifyArgs a) {
     // parents read as -1) and replaced by NaN at the stores.
     const bool badn = real && (par_in < -1 || par_in >= node);
     const unsigned long long badm = __ballot(badn);
-    const int bad = badm ? __ffsll(static_cast<unsigned long long>(badm)) : 0;  // 1 + first bad node
+    // -1 for a length out of range, else 1 + the first bad node
+    const int bad = sl.bad ? -1 : (badm ? __ffsll(static_cast<unsigned long long>(badm)) : 0);
     const float beta = real ? beta_in : 0.f;
     // log2 alpha in fp32 (its error is relative to each term); the path sums in fp64
     unsigned long long mask = real ? (1ull << node) : 0ull;
@@ -224,10 +229,10 @@ __global__ __launch_bounds__(64 * NSB) void verify_mid_kernel(VerifyArgs a) {
             }
 #pragma unroll
             for (int e = 0; e < 4; ++e) {
-                const int i = 16 * p + 4 * lg + e;  // beta and P are 0 past T
+                const int i = 16 * p + 4 * lg + e;  // beta and P are 0 past Tb
                 const float r = bi[e] * (Op::raw_f32(vraw[ct][e]) - Pi[e] * ak[e]), o = Pi[e] * aq[e];
-                rhs[ct][e] = i < T ? r : 0.f;
-                oacc[ct][e] = i < T ? o : 0.f;
+                rhs[ct][e] = i < Tb ? r : 0.f;
+                oacc[ct][e] = i < Tb ? o : 0.f;
             }
         }
     }
@@ -420,7 +425,7 @@ __global__ __launch_bounds__(64 * NSB) void verify_mid_kernel(VerifyArgs a) {
 #pragma unroll
         for (int e = 0; e < 4; ++e) {
             const int i = 16 * p + 4 * lg + e;
-            if (i < T) {
+            if (i < Tb) {
                 const size_t o = base + static_cast<size_t>(i) * rs + colw + 16 * ct + lr;
                 a.U[o] = bad ? qnan : u[ct][e];
                 a.O[o] = bad ? qnan : oacc[ct][e];

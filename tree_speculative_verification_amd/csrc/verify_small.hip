@@ -37,19 +37,23 @@ __global__ __launch_bounds__(64 * NWV) void verify_small_kernel(VerifyArgs a) {
     const size_t rs = static_cast<size_t>(H) * D;
     const size_t base = (static_cast<size_t>(b) * T * H + h) * D;
     const size_t sbase = static_cast<size_t>(b) * T * H + h;
+    const size_t qkrs = static_cast<size_t>(a.HK) * D;
+    const size_t qkbase = qk_base(b, h, H, a.HK, T);
     const bool writer = tile == 0;  // this head's wave for the per-node outputs
+    const SeqLen sl = seq_len(a.tree_len, b, T);
+    const int Tb = sl.n;  // this sequence's node count
 
-    // ---- every load up front, unconditional (rows and nodes past T read row or node T-1 and
-    // are masked later), so that they all issue before the first one is waited for: the tree
-    // and gates (lane = node), K and Q fragments (row lr), S0 fragments (column col0 + lr), V
-    // (result order)
+    // ---- every load up front, unconditional (rows and nodes past T read row or node T-1;
+    // rows and nodes past Tb are padding, dropped by selects later), so that they all issue
+    // before the first one is waited for: the tree and gates (lane = node), K and Q fragments
+    // (row lr), S0 fragments (column col0 + lr), V (result order)
     const int node = lane;
-    const bool real = node < T;
+    const bool real = node < Tb;
     const int nodec = min(node, T - 1);
     const int par_in = a.parent[static_cast<size_t>(b) * T + nodec];
     const float alpha_in = a.alpha[sbase + static_cast<size_t>(nodec) * H];
     const float beta_in = a.beta[sbase + static_cast<size_t>(nodec) * H];
-    const size_t erow = base + static_cast<size_t>(min(lr, T - 1)) * rs + 8 * lg;
+    const size_t erow = qkbase + static_cast<size_t>(min(lr, T - 1)) * qkrs + 8 * lg;
     In kf[4], qf[4];
 #pragma unroll
     for (int ks = 0; ks < 4; ++ks) {
@@ -74,7 +78,8 @@ __global__ __launch_bounds__(64 * NWV) void verify_small_kernel(VerifyArgs a) {
     // no branch separates the loads from their uses.
     const bool badn = real && (par_in < -1 || par_in >= node);
     const unsigned long long badm = __ballot(badn);
-    const int bad = badm ? (__ffsll(static_cast<unsigned long long>(badm))) : 0;  // 1 + first bad node
+    // -1 for a length out of range, else 1 + the first bad node
+    const int bad = sl.bad ? -1 : (badm ? (__ffsll(static_cast<unsigned long long>(badm))) : 0);
     const float beta = real ? beta_in : 0.f;
     // log alpha in fp32 (its error is relative to each term, so it stays relative to any
     // difference l_i - l_j of path sums); the sums themselves in fp64.
@@ -124,8 +129,8 @@ __global__ __launch_bounds__(64 * NWV) void verify_small_kernel(VerifyArgs a) {
         const int i = 4 * lg + e;
         const float bi = __shfl(beta, i, 64), Pi = __shfl(P, i, 64);
         const float r = bi * (Op::raw_f32(vraw[e]) - Pi * ak[e]), o = Pi * aq[e];
-        rhs[e] = i < T ? r : 0.f;
-        o0[e] = i < T ? o : 0.f;
+        rhs[e] = i < Tb ? r : 0.f;
+        o0[e] = i < Tb ? o : 0.f;
     }
 
     // ---- a3: Gram tile with K as the A operand: lane (lg, lr) holds row i = lr, columns
@@ -178,7 +183,7 @@ __global__ __launch_bounds__(64 * NWV) void verify_small_kernel(VerifyArgs a) {
 #pragma unroll
     for (int e = 0; e < 4; ++e) {
         const int i = 4 * lg + e;
-        if (i < T) {
+        if (i < Tb) {
             a.U[base + static_cast<size_t>(i) * rs + col0 + lr] = bad ? qnan : u[e];
             a.O[base + static_cast<size_t>(i) * rs + col0 + lr] = bad ? qnan : oc[e];
         }

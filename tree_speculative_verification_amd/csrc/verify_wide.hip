@@ -116,10 +116,15 @@ __global__ __launch_bounds__(1024) void verify_wide_kernel(VerifyArgs a) {
     const size_t rs = static_cast<size_t>(H) * D;
     const size_t base = (static_cast<size_t>(b) * T * H + h) * D;
     const size_t sbase = static_cast<size_t>(b) * T * H + h;
+    const size_t qkrs = static_cast<size_t>(a.HK) * D;
+    const size_t qkbase = qk_base(b, h, H, a.HK, T);
+    const SeqLen sl = seq_len(a.tree_len, b, T);
+    const int Tb = sl.n;  // this sequence's node count
     const bool writer = grp == 0;  // this head's workgroup for the per-node outputs
     const int32_t *par = a.parent + static_cast<size_t>(b) * T;
 
-    // ---- every load up front, unconditional (rows and nodes past T read row or node T-1):
+    // ---- every load up front, unconditional (rows and nodes past T read row or node T-1; rows
+    // and nodes past Tb are padding, dropped by selects later):
     // the prep chunk of a wave p < nch (lane = node 64p + lane), the wave's K and Q rows, the
     // thread's share of the S0 columns and the wave's V rows.
     const bool chunkw = p < nch;
@@ -130,7 +135,7 @@ __global__ __launch_bounds__(1024) void verify_wide_kernel(VerifyArgs a) {
     const float beta_in = a.beta[sbase + static_cast<size_t>(cnodec) * H];
     In kp[4], qp[4];
     {
-        const size_t er = base + static_cast<size_t>(min(16 * p + lr, T - 1)) * rs + 8 * lg;
+        const size_t er = qkbase + static_cast<size_t>(min(16 * p + lr, T - 1)) * qkrs + 8 * lg;
 #pragma unroll
         for (int ks = 0; ks < 4; ++ks) {
             kp[ks] = Op::template load_frag<In>(a.k, er + 32 * ks, true);
@@ -163,7 +168,7 @@ __global__ __launch_bounds__(1024) void verify_wide_kernel(VerifyArgs a) {
     if (tid < WMAXT / 16) sm.ready[tid] = 0;
     __syncthreads();
     if (chunkw) {
-        const bool real = cnode < T;
+        const bool real = cnode < Tb;
         int pp = real ? par_in : -1;
         if (real && (pp < -1 || pp >= cnode)) {
             atomicMin(&sm.bad, cnode + 1);
@@ -211,7 +216,7 @@ __global__ __launch_bounds__(1024) void verify_wide_kernel(VerifyArgs a) {
         }
     }
     __syncthreads();
-    const int bad = sm.bad == INT_MAX ? 0 : sm.bad;
+    const int bad = sl.bad ? -1 : (sm.bad == INT_MAX ? 0 : sm.bad);
     // ---- prep, phase 2: chunks completed in order (every exit lies in an earlier chunk)
     for (int c = 1; c < nch; ++c) {
         if (p == c) {
@@ -226,7 +231,7 @@ __global__ __launch_bounds__(1024) void verify_wide_kernel(VerifyArgs a) {
         __syncthreads();
     }
     if (chunkw) {
-        const bool real = cnode < T;
+        const bool real = cnode < Tb;
         const double lam = sm.lam[cnode];
         sm.P[cnode] = real ? __builtin_amdgcn_exp2f(static_cast<float>(lam)) : 0.f;
         if (writer && real) {
@@ -267,10 +272,10 @@ __global__ __launch_bounds__(1024) void verify_wide_kernel(VerifyArgs a) {
             }
 #pragma unroll
             for (int e = 0; e < 4; ++e) {
-                const int i = 16 * p + 4 * lg + e;  // beta and P are 0 past T
+                const int i = 16 * p + 4 * lg + e;  // beta and P are 0 past Tb
                 const float r = bi[e] * (bf16_to_f32(vraw[ct][e]) - Pi[e] * ak[e]), o = Pi[e] * aq[e];
-                rhs[ct][e] = i < T ? r : 0.f;
-                oacc[ct][e] = i < T ? o : 0.f;
+                rhs[ct][e] = i < Tb ? r : 0.f;
+                oacc[ct][e] = i < Tb ? o : 0.f;
             }
         }
     }
@@ -297,7 +302,7 @@ __global__ __launch_bounds__(1024) void verify_wide_kernel(VerifyArgs a) {
             const float gam2 = __builtin_amdgcn_exp2f(static_cast<float>(sm.lam[j] - li));
             nB[e] = (on2 && i != j) ? -bj[e] * gam2 * kk[e] : 0.f;
         }
-        if (i < T) dl = __popc((sm.mask[i][p >> 1] >> (16 * (p & 1))) & 0xFFFFu) - 1;
+        if (i < Tb) dl = __popc((sm.mask[i][p >> 1] >> (16 * (p & 1))) & 0xFFFFu) - 1;
         const int dp = wave_max(dl);
         int nf = 0;
         while ((1 << nf) <= dp) ++nf;
@@ -378,7 +383,7 @@ __global__ __launch_bounds__(1024) void verify_wide_kernel(VerifyArgs a) {
 #pragma unroll
         for (int e = 0; e < 4; ++e) {
             const int i = 16 * p + 4 * lg + e;
-            if (i < T) {
+            if (i < Tb) {
                 const size_t o = base + static_cast<size_t>(i) * rs + colw + 16 * ct + lr;
                 a.U[o] = bad ? qnan : u[ct][e];
                 a.O[o] = bad ? qnan : oacc[ct][e];
