@@ -45,6 +45,16 @@ WORKLOADS = {
     "random256_b16": dict(B=16, H=32, T=256, tree="random", dtype="bf16", seed=3,
                           desc="B=16 H=32 T=256 random recursive trees, bf16 q/k/v, fp32 S0"),
 }
+# Grouped value heads ("Qwen3.5-9B shapes": 16 q/k heads serving 32 value heads) and a ragged
+# batch (each sequence's own node count, drawn uniformly from the given range).
+WORKLOADS["topk16_b1_hk16"] = dict(B=1, H=32, HK=16, T=16, tree="topk", tree_kw={"branching": (3, 4)},
+                                   dtype="bf16", seed=1,
+                                   desc="B=1 H=32 value heads, 16 q/k heads, T=16 top-k tree 1+3+12, bf16 q/k/v, fp32 S0")
+WORKLOADS["random256_b16_hk16"] = dict(B=16, H=32, HK=16, T=256, tree="random", dtype="bf16", seed=3,
+                                       desc="B=16 H=32 value heads, 16 q/k heads, T=256 random recursive trees, bf16 q/k/v, fp32 S0")
+WORKLOADS["random256_b16_ragged"] = dict(B=16, H=32, HK=16, T=256, tree="random", dtype="bf16", seed=5,
+                                         ragged=(64, 256),
+                                         desc="B=16 H=32 value heads, 16 q/k heads, ragged random trees of 64-256 nodes (T=256), bf16 q/k/v, fp32 S0")
 for _B in (1, 2, 4, 8):
     WORKLOADS[f"skewed64_b{_B}"] = dict(B=_B, H=32, T=64, tree="skewed", dtype="bf16", seed=2,
                                         desc=f"B={_B} H=32 T=64 skewed trees, bf16 q/k/v, fp32 S0")
@@ -54,19 +64,27 @@ for _B in (1, 2, 4, 8):
                                          desc=f"B={_B} H=32 T=128 random recursive trees, bf16 q/k/v, fp32 S0")
 
 
-def verify_bytes(B, H, T, dtype):
-    """Algorithmic HBM bytes of one verify launch: S0 once per (sequence, head), then per node
-    and head q, k, v (input dtype), alpha and beta (fp32), O and U (fp32) and ell (fp32), plus
-    the parent array."""
+def verify_bytes(B, H, T, dtype, HK=None, nodes=None):
+    """Algorithmic HBM bytes of one verify launch: S0 once per (sequence, value head), then per
+    node and value head v (input dtype), alpha and beta (fp32), O and U (fp32) and ell (fp32),
+    per node and q/k head q and k (input dtype; HK = H when every value head has its own), plus
+    the parent array. ``nodes`` is the batch's real node count (B * T unless ragged)."""
     ib = 2 if dtype == "bf16" else 4
-    per_node_head = 3 * 128 * ib + 8 + 2 * 128 * 4 + 4
-    return B * H * (128 * 128 * 4 + T * per_node_head) + B * T * 4
+    HK = H if HK is None else HK
+    nodes = B * T if nodes is None else nodes
+    per_node = H * (128 * ib + 8 + 2 * 128 * 4 + 4) + HK * 2 * 128 * ib
+    return B * H * 128 * 128 * 4 + nodes * per_node + B * T * 4
 
 
 def commit_bytes(B, H, m_total):
     """S0 read and S_new written per (sequence, head), plus k (bf16) and U rows and alpha of
     the path nodes (m_total path nodes summed over sequences), plus the path arrays."""
     return B * H * 2 * 128 * 128 * 4 + m_total * H * (128 * 2 + 128 * 4 + 4) + m_total * 8
+
+
+def verify_flops_ragged(H, lens):
+    """verify_flops summed over sequences of their own node counts."""
+    return sum(verify_flops(1, H, int(n)) for n in lens)
 
 
 def verify_flops(B, H, T):
@@ -168,9 +186,14 @@ def pmc_summary(run_dir, out_path):
 
 
 def build_inputs(wl):
+    import numpy as np
     import synth
     kw = {k: wl[k] for k in ("B", "H", "T", "tree", "dtype", "seed")}
-    return synth.make_inputs(tree_kw=wl.get("tree_kw"), **kw)
+    lens = None
+    if wl.get("ragged"):
+        lo, hi = wl["ragged"]
+        lens = np.random.default_rng(wl["seed"] + 7919).integers(lo, hi + 1, wl["B"]).astype(np.int32)
+    return synth.make_inputs(tree_kw=wl.get("tree_kw"), HK=wl.get("HK"), tree_len=lens, **kw)
 
 
 def to_device(inp):
@@ -187,6 +210,8 @@ def to_device(inp):
         out[n] = torch.from_numpy(inp[n]).cuda()
     for n in ("parent", "path", "path_len"):
         out[n] = torch.from_numpy(inp[n].astype(np.int32)).cuda()
+    tl = inp.get("tree_len")
+    out["tree_len"] = None if tl is None else torch.from_numpy(tl.astype(np.int32)).cuda()
     return out
 
 
@@ -241,12 +266,19 @@ def cpu_baseline(inp, budget_s=10.0):
     import oracle
     times = []
     t_start = time.perf_counter()
+    plain = inp.get("tree_len") is None and inp.get("HK", inp["H"]) == inp["H"]
     while True:
         t0 = time.perf_counter()
-        oracle.gdn_tree(inp["parent"], inp["q"], inp["k"], inp["v"], inp["alpha"], inp["beta"],
-                        inp["S0"])
-        oracle.commit(inp["parent"], inp["path"], inp["path_len"], inp["k"], inp["v"],
-                      inp["alpha"], inp["beta"], inp["S0"])
+        if plain:
+            oracle.gdn_tree(inp["parent"], inp["q"], inp["k"], inp["v"], inp["alpha"], inp["beta"],
+                            inp["S0"])
+            oracle.commit(inp["parent"], inp["path"], inp["path_len"], inp["k"], inp["v"],
+                          inp["alpha"], inp["beta"], inp["S0"])
+        else:
+            oracle.gdn_tree_ragged(inp["parent"], inp["tree_len"], inp["q"], inp["k"], inp["v"],
+                                   inp["alpha"], inp["beta"], inp["S0"])
+            oracle.commit_ragged(inp["parent"], inp["tree_len"], inp["path"], inp["path_len"],
+                                 inp["k"], inp["v"], inp["alpha"], inp["beta"], inp["S0"])
         times.append(time.perf_counter() - t0)
         if time.perf_counter() - t_start > budget_s and len(times) >= 3:
             break
@@ -440,10 +472,11 @@ def main(argv=None):
 
     def verify():
         tsv.tree_verify(d["q"], d["k"], d["v"], d["alpha"], d["beta"], d["S0"], d["parent"],
-                        solver=args.solver, waves=args.waves, out=(O, U, ell))
+                        solver=args.solver, waves=args.waves, out=(O, U, ell), tree_len=d["tree_len"])
 
     def commit():
-        tsv.commit(d["S0"], d["k"], U, d["alpha"], d["parent"], d["path"], d["path_len"], out=S_new)
+        tsv.commit(d["S0"], d["k"], U, d["alpha"], d["parent"], d["path"], d["path_len"], out=S_new,
+                   tree_len=d["tree_len"])
 
     def step():
         verify()
@@ -477,7 +510,7 @@ def main(argv=None):
 
         def serial():
             tsv.serial_verify(d["q"], d["k"], d["v"], d["alpha"], d["beta"], d["S0"], d["parent"],
-                              snapshots=snaps)
+                              snapshots=snaps, tree_len=d["tree_len"])
         n_ser = max(10, args.steps // 4)
         if args.eager:
             us_serial = time_eager(serial, n_ser, 3)
@@ -495,9 +528,12 @@ def main(argv=None):
         torch.cuda.synchronize()
         del src, dst
 
-    vbytes = verify_bytes(B, H, T, dt)
+    HK = wl.get("HK", H)
+    lens = inp["tree_len"] if inp.get("tree_len") is not None else np.full(B, T)
+    nodes = int(lens.sum())
+    vbytes = verify_bytes(B, H, T, dt, HK=HK, nodes=nodes)
     achieved = vbytes / (us_verify * 1e-6) / 1e9
-    vflops = verify_flops(B, H, T)
+    vflops = verify_flops_ragged(H, lens)
     tflops = vflops / (us_verify * 1e-6) / 1e12
     out = {
         "metric": METRIC,
@@ -513,13 +549,14 @@ def main(argv=None):
         "dtype": "bf16" if dt == "bf16" else "fp32",
         "data": "synthetic",
         "config": {"workload": wl["desc"], "workload_key": args.workload, "B": B, "H": H, "T": T,
-                   "dk": 128, "dv": 128, "tree": wl["tree"], "solver": args.solver,
+                   "q_k_heads": HK, "nodes": nodes, "dk": 128, "dv": 128, "tree": wl["tree"],
+                   "solver": args.solver,
                    "waves": args.waves, "step": "verify + commit of a random root-to-leaf path",
                    "launch": "eager" if args.eager else "hip graph of all timed steps",
                    "copy_probe_bytes": args.copy_probe},
-        "nodes_per_s": round(B * T / (us_step * 1e-6), 1),
+        "nodes_per_s": round(nodes / (us_step * 1e-6), 1),
         "verify_us": round(us_verify, 3),
-        "verify_nodes_per_s": round(B * T / (us_verify * 1e-6), 1),
+        "verify_nodes_per_s": round(nodes / (us_verify * 1e-6), 1),
         "commit_us": round(us_commit, 3),
         "serial_verify_us": None if us_serial is None else round(us_serial, 3),
         "roofline": {"bound": "hbm", "kernel": verify_kernel_name(T, args.solver, B * H, args.waves, dt),
