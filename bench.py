@@ -185,6 +185,53 @@ def pmc_summary(run_dir, out_path):
     return 0
 
 
+def run_conv(args):
+    """The root-path causal convolution (kernel 4, SiLU) and its state commit on the workload's
+    trees, over the channels a GDN layer convolves: q and k of its q/k heads and v of its value
+    heads (2 * 16 * 128 + 32 * 128 = 8192 for the 9B shape), bf16. One JSON line; HBM bytes
+    per launch: x read and y written once per real node, plus the state, weights and parents."""
+    import numpy as np
+    import torch
+    import tree_speculative_verification_amd as tsv
+    wl = WORKLOADS[args.workload]
+    B, T = wl["B"], wl["T"]
+    C = 2 * 16 * 128 + 32 * 128
+    K = 4
+    inp = build_inputs(wl)
+    g = torch.Generator(device="cpu").manual_seed(11)
+    x = torch.randn((B, T, C), generator=g).to(torch.bfloat16).cuda()
+    st = torch.randn((B, K - 1, C), generator=g).to(torch.bfloat16).cuda()
+    w = (torch.randn((C, K), generator=g) * 0.5).cuda()
+    d = to_device(inp)
+    y = torch.empty_like(x)
+    new = torch.empty_like(st)
+    tsv.load()
+    conv = lambda: tsv.tree_conv(x, w, st, d["parent"], silu=True, tree_len=d["tree_len"], out=y)
+    commit = lambda: tsv.conv_commit(x, st, d["parent"], d["path"], d["path_len"],
+                                     tree_len=d["tree_len"], out=new)
+    for _ in range(args.warmup):
+        conv()
+        commit()
+    torch.cuda.synchronize()
+    gc = graph_of(conv, args.steps)
+    us_conv = time_graph(gc, args.steps)
+    del gc
+    gm = graph_of(commit, args.steps)
+    us_commit = time_graph(gm, args.steps)
+    del gm
+    lens = inp["tree_len"] if inp.get("tree_len") is not None else np.full(B, T)
+    nodes = int(lens.sum())
+    cbytes = 2 * nodes * C * 2 + B * (K - 1) * C * 2 + C * K * 4 + B * T * 4
+    out = {"op": "tree_conv (K=4, SiLU) + conv_commit", "workload": wl["desc"],
+           "workload_key": args.workload, "channels": C, "nodes": nodes, "dtype": "bf16",
+           "conv_us": round(us_conv, 3), "conv_commit_us": round(us_commit, 3),
+           "conv_bytes": cbytes, "conv_gbs": round(cbytes / (us_conv * 1e-6) / 1e9, 1),
+           "conv_hbm_frac": round(cbytes / (us_conv * 1e-6) / 1e9 / HBM_PEAK_GBS, 4),
+           "steps": args.steps, "launch": "hip graph of all timed launches"}
+    print(json.dumps(out), flush=True)
+    return 0
+
+
 def build_inputs(wl):
     import numpy as np
     import synth
@@ -433,6 +480,8 @@ def main(argv=None):
     ap.add_argument("--crossover", action="store_true",
                     help="run the depth x width crossover over 24 layers instead of one workload")
     ap.add_argument("--rounds", type=int, default=100, help="crossover: rounds per cell")
+    ap.add_argument("--conv", action="store_true",
+                    help="time the root-path causal convolution and its commit instead")
     ap.add_argument("--batches", type=int, nargs="+", default=[1, 4, 16], help="crossover: batch sizes")
     ap.add_argument("--max-t", type=int, default=0, help="crossover: skip trees larger than this")
     ap.add_argument("--serial-budget", type=float, default=2.0,
@@ -455,6 +504,8 @@ def main(argv=None):
         return 2
     if args.crossover:
         return run_crossover(args)
+    if args.conv:
+        return run_conv(args)
 
     import numpy as np
     import torch

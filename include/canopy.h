@@ -194,6 +194,42 @@ canopy_status canopy_serial_commit(const float *snapshots, const float *S0, cons
                                    const int32_t *path_len, int B, int HV, int T, float *S_new,
                                    int32_t *path_status, hipStream_t stream);
 
+/*
+ * Root-path causal convolution of a draft tree (the canopy page, "M7", stretch item: the short
+ * causal convolution before each GDN layer must follow each node's root path). Depthwise over
+ * C channels with kernel size K:
+ *   y_i[c] = sum_{j<K} w[c][j] * X_i(K-1-j)[c]   (then y = y * sigmoid(y) if silu = 1)
+ * where X_i(0) = x_i, X_i(s) is the input s positions up node i's root path, and positions
+ * before the root read the committed state, its last row first. Accumulates in fp32.
+ *   x           [B,T,C], in_dtype (fp32, or bf16 as 16-bit patterns), in.
+ *   w           [C,K] fp32, in: w[c][K-1] multiplies the node itself (a PyTorch depthwise
+ *               conv1d weight [C,1,K] without its middle axis).
+ *   conv_state  [B,K-1,C], in_dtype, in: the last K-1 committed inputs, oldest first.
+ *   parent      [B,T] int32, in; tree_len [B] int32 or NULL, as for canopy_tree_verify.
+ *   y           [B,T,C], in_dtype, out (bf16: rounded to nearest, ties to even); padding rows
+ *               are not written; a malformed tree's rows are NaN.
+ *   tree_status [B] int32, out, may be NULL: as in canopy_tree_prep.
+ * 2 <= K <= 4, C a positive multiple of 8, 1 <= T <= 256. x, w, conv_state, y 16-byte aligned.
+ */
+canopy_status canopy_tree_conv(const void *x, canopy_dtype in_dtype, const float *w,
+                               const void *conv_state, const int32_t *parent,
+                               const int32_t *tree_len, int B, int T, int C, int K, int silu,
+                               void *y, int32_t *tree_status, hipStream_t stream);
+
+/*
+ * Roll the convolution state forward over the accepted path ("commit must update the
+ * convolution state with the accepted tokens"): state_new holds the last K-1 inputs of the
+ * committed sequence (old state rows, then x of the path's nodes), oldest first. Path checks
+ * and path_status as in canopy_commit; a bad sequence's state_new is NaN.
+ *   x           [B,T,C], in_dtype, in: the inputs given to canopy_tree_conv.
+ *   conv_state  [B,K-1,C], in_dtype, in.
+ *   state_new   [B,K-1,C], in_dtype, out; may be the same memory as conv_state (in place).
+ */
+canopy_status canopy_conv_commit(const void *x, canopy_dtype in_dtype, const void *conv_state,
+                                 const int32_t *parent, const int32_t *tree_len,
+                                 const int32_t *path, const int32_t *path_len, int B, int T, int C,
+                                 int K, void *state_new, int32_t *path_status, hipStream_t stream);
+
 #ifdef __cplusplus
 }
 #endif

@@ -20,7 +20,7 @@ def declared_functions():
 def test_header_declares_the_calls():
     names = declared_functions()
     for n in ("canopy_tree_verify", "canopy_commit", "canopy_serial_verify", "canopy_tree_prep",
-              "canopy_status_string", "canopy_version"):
+              "canopy_tree_conv", "canopy_conv_commit", "canopy_status_string", "canopy_version"):
         assert n in names
 
 
@@ -63,3 +63,21 @@ def test_product_path_does_not_touch_the_oracle():
                 src = open(os.path.join(dirpath, f)).read()
                 assert "import oracle" not in src and "from oracle" not in src, f
                 assert "liboracle" not in src, f
+
+
+def test_conv_host_checks_need_no_gpu():
+    """Convolution sizes are checked on the host: K outside 2..4 or C not a multiple of 8."""
+    lib = ctypes.CDLL(LIB)
+    f = lib.canopy_tree_conv
+    f.restype = ctypes.c_int
+    i = ctypes.c_int
+    buf = ctypes.create_string_buffer(4096 + 16)
+    p = ctypes.c_void_p((ctypes.addressof(buf) + 15) // 16 * 16)  # aligned, never dereferenced
+    nul = ctypes.c_void_p(0)
+    # x, dtype, w, state, parent, tree_len, B, T, C, K, silu, y, status, stream
+    def call(C, K, x=p):
+        return f(x, i(0), p, p, p, nul, i(1), i(4), i(C), i(K), i(0), p, nul, nul)
+    assert call(12, 4) == 1
+    assert call(16, 5) == 1
+    assert call(16, 1) == 1
+    assert call(16, 4, x=nul) == 1

@@ -63,6 +63,10 @@ def load():
     lib.canopy_serial_verify.restype = i
     lib.canopy_serial_commit.argtypes = [P, P, P, P, P, P, i, i, i, P, P, u64]
     lib.canopy_serial_commit.restype = i
+    lib.canopy_tree_conv.argtypes = [P, i, P, P, P, P, i, i, i, i, i, P, P, u64]
+    lib.canopy_tree_conv.restype = i
+    lib.canopy_conv_commit.argtypes = [P, i, P, P, P, P, P, i, i, i, i, P, P, u64]
+    lib.canopy_conv_commit.restype = i
     _lib = lib
     return lib
 
@@ -241,3 +245,42 @@ def serial_commit(snapshots, S0, parent, path, path_len, out=None, tree_len=None
                                        _ptr(path), _ptr(path_len), B, H, T, _ptr(S_new),
                                        _ptr(status), _stream()))
     return S_new, status
+
+
+def tree_conv(x, w, conv_state, parent, silu=False, tree_len=None, out=None):
+    """Root-path causal convolution of a draft tree: y [B,T,C] in x's dtype and the tree status
+    [B]. x [B,T,C] (bf16 or fp32), w [C,K] fp32 (w[:, K-1] multiplies the node itself),
+    conv_state [B,K-1,C] in x's dtype (the last committed inputs, oldest first)."""
+    B, T, C = x.shape
+    K = w.shape[1]
+    dt = _in_dtype(x)
+    _req(x, "x", None, (B, T, C))
+    _req(w, "w", torch.float32, (C, K))
+    _req(conv_state, "conv_state", x.dtype, (B, K - 1, C))
+    _req(parent, "parent", torch.int32, (B, T))
+    tl = _tree_len(tree_len, B)
+    y = torch.empty_like(x) if out is None else _req(out, "out", x.dtype, (B, T, C))
+    status = torch.empty((B,), dtype=torch.int32, device=x.device)
+    _check(load().canopy_tree_conv(_ptr(x), dt, _ptr(w), _ptr(conv_state), _ptr(parent), _ptr(tl),
+                                   B, T, C, K, int(bool(silu)), _ptr(y), _ptr(status), _stream()))
+    return y, status
+
+
+def conv_commit(x, conv_state, parent, path, path_len, tree_len=None, out=None):
+    """The convolution state after the accepted path ([B,K-1,C], x's dtype; ``out`` may be
+    conv_state itself) and the path status [B]."""
+    B, T, C = x.shape
+    K = conv_state.shape[1] + 1
+    dt = _in_dtype(x)
+    _req(x, "x", None, (B, T, C))
+    _req(conv_state, "conv_state", x.dtype, (B, K - 1, C))
+    _req(parent, "parent", torch.int32, (B, T))
+    _req(path, "path", torch.int32, (B, T))
+    _req(path_len, "path_len", torch.int32, (B,))
+    tl = _tree_len(tree_len, B)
+    new = torch.empty_like(conv_state) if out is None else _req(out, "out", x.dtype, (B, K - 1, C))
+    status = torch.empty((B,), dtype=torch.int32, device=x.device)
+    _check(load().canopy_conv_commit(_ptr(x), dt, _ptr(conv_state), _ptr(parent), _ptr(tl),
+                                     _ptr(path), _ptr(path_len), B, T, C, K, _ptr(new),
+                                     _ptr(status), _stream()))
+    return new, status

@@ -145,4 +145,39 @@ canopy_status canopy_serial_commit(const float *snapshots, const float *S0, cons
     return from_hip(launch_serial_commit(a, stream));
 }
 
+// Convolution sizes: channels a positive multiple of 8, kernel size 2..4, and every index of
+// the [B,T,C] arrays within 64-bit range with the grid within int range.
+static bool conv_sizes_ok(int B, int T, int C, int K) {
+    return B >= 1 && T >= 1 && T <= 256 && C >= 8 && C % 8 == 0 && K >= 2 && K <= 4 &&
+           static_cast<long long>(B) * ((static_cast<long long>(T) * (C / 8) + 255) / 256) <= 2147483647LL &&
+           static_cast<long long>(T) * C <= 2147483647LL;
+}
+
+canopy_status canopy_tree_conv(const void *x, canopy_dtype in_dtype, const float *w,
+                               const void *conv_state, const int32_t *parent,
+                               const int32_t *tree_len, int B, int T, int C, int K, int silu,
+                               void *y, int32_t *tree_status, hipStream_t stream) {
+    if (!x || !w || !conv_state || !parent || !y) return CANOPY_ERR_ARG;
+    if (!conv_sizes_ok(B, T, C, K)) return CANOPY_ERR_ARG;
+    if (!aligned16(x) || !aligned16(w) || !aligned16(conv_state) || !aligned16(y)) return CANOPY_ERR_ARG;
+    if (in_dtype != CANOPY_FP32 && in_dtype != CANOPY_BF16) return CANOPY_ERR_UNSUPPORTED;
+    if (silu != 0 && silu != 1) return CANOPY_ERR_UNSUPPORTED;
+    ConvArgs a{x, w, conv_state, parent, tree_len, B, T, C, K, in_dtype == CANOPY_BF16, silu, y,
+               tree_status};
+    return from_hip(launch_tree_conv(a, stream));
+}
+
+canopy_status canopy_conv_commit(const void *x, canopy_dtype in_dtype, const void *conv_state,
+                                 const int32_t *parent, const int32_t *tree_len,
+                                 const int32_t *path, const int32_t *path_len, int B, int T, int C,
+                                 int K, void *state_new, int32_t *path_status, hipStream_t stream) {
+    if (!x || !conv_state || !parent || !path || !path_len || !state_new) return CANOPY_ERR_ARG;
+    if (!conv_sizes_ok(B, T, C, K)) return CANOPY_ERR_ARG;
+    if (!aligned16(x) || !aligned16(conv_state) || !aligned16(state_new)) return CANOPY_ERR_ARG;
+    if (in_dtype != CANOPY_FP32 && in_dtype != CANOPY_BF16) return CANOPY_ERR_UNSUPPORTED;
+    ConvCommitArgs a{x, conv_state, parent, tree_len, path, path_len, B, T, C, K,
+                     in_dtype == CANOPY_BF16, state_new, path_status};
+    return from_hip(launch_conv_commit(a, stream));
+}
+
 }  // extern "C"

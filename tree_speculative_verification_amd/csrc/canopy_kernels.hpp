@@ -60,6 +60,28 @@ struct SerialCommitArgs {
     int32_t *path_status;
 };
 
+// Root-path causal convolution: x [B,T,C], w [C,K] fp32, state [B,K-1,C], y [B,T,C]; x, state
+// and y in the input dtype.
+struct ConvArgs {
+    const void *x;
+    const float *w;
+    const void *state;
+    const int32_t *parent, *tree_len;
+    int B, T, C, K;
+    int bf16, silu;
+    void *y;
+    int32_t *tree_status;
+};
+
+struct ConvCommitArgs {
+    const void *x, *state;
+    const int32_t *parent, *tree_len, *path, *path_len;
+    int B, T, C, K;
+    int bf16;
+    void *state_new;
+    int32_t *path_status;
+};
+
 // The node count of sequence b: tree_len[b], or T without a length array. A length outside
 // 1..T is reported (bad = true) and the whole T-row extent is then treated as that sequence's
 // tree, whose outputs the kernels replace by NaN.
@@ -88,5 +110,7 @@ hipError_t launch_prep(const PrepArgs &a, hipStream_t stream);
 hipError_t launch_commit(const CommitArgs &a, hipStream_t stream);
 hipError_t launch_serial(const SerialArgs &a, hipStream_t stream);
 hipError_t launch_serial_commit(const SerialCommitArgs &a, hipStream_t stream);
+hipError_t launch_tree_conv(const ConvArgs &a, hipStream_t stream);
+hipError_t launch_conv_commit(const ConvCommitArgs &a, hipStream_t stream);
 
 }  // namespace canopy
