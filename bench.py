@@ -185,6 +185,49 @@ def pmc_summary(run_dir, out_path):
     return 0
 
 
+def run_solver_sweep(args):
+    """Verify µs per solver on level trees (root, then levels of W nodes) over T, W and B: the
+    table behind the AUTO dispatch. One JSON line per (T, W, B) cell with every solver's time
+    and the kernel AUTO ran; ``--out`` appends the lines to a file."""
+    import numpy as np
+    import torch
+    import synth
+    import tree_speculative_verification_amd as tsv
+    tsv.load()
+    cells = []
+    for T in (24, 32, 48, 64, 128, 256):
+        for W in (1, 2, 4, 8, 16, 32, 64):
+            if W < T:
+                cells.append((T, W))
+    lines = []
+    for T, W in cells:
+        par = synth.level_tree(T, W)
+        depth = int(synth.tree_depths(par).max())
+        for B in args.batches:
+            inp = synth.make_inputs(B, 32, T, dtype="bf16", seed=7, parents=par)
+            d = to_device(inp)
+            res = {}
+            solvers = ("auto", "fwdsub", "neumann", "level") if T > 64 else ("auto", "fwdsub", "neumann")
+            for sv in solvers:
+                fn = lambda: tsv.tree_verify(d["q"], d["k"], d["v"], d["alpha"], d["beta"], d["S0"],
+                                             d["parent"], solver=sv)
+                fn()
+                torch.cuda.synchronize()
+                g = graph_of(fn, args.steps)
+                res[sv] = round(min(time_graph(g, args.steps) for _ in range(2)), 3)
+                del g
+            best = min((v, k) for k, v in res.items() if k != "auto")[1]
+            line = dict(T=T, W=W, depth=depth, B=B, H=32, us=res, best=best,
+                        auto_kernel=verify_kernel_name(T, "auto", B * 32, 0, "bf16"))
+            print(json.dumps(line), flush=True)
+            lines.append(line)
+    if args.out:
+        with open(args.out, "a") as fh:
+            for line in lines:
+                fh.write(json.dumps(line) + "\n")
+    return 0
+
+
 def run_conv(args):
     """The root-path causal convolution (kernel 4, SiLU) and its state commit on the workload's
     trees, over the channels a GDN layer convolves: q and k of its q/k heads and v of its value
@@ -480,6 +523,8 @@ def main(argv=None):
     ap.add_argument("--crossover", action="store_true",
                     help="run the depth x width crossover over 24 layers instead of one workload")
     ap.add_argument("--rounds", type=int, default=100, help="crossover: rounds per cell")
+    ap.add_argument("--solver-sweep", action="store_true",
+                    help="time every solver on level trees over T, width and --batches")
     ap.add_argument("--conv", action="store_true",
                     help="time the root-path causal convolution and its commit instead")
     ap.add_argument("--batches", type=int, nargs="+", default=[1, 4, 16], help="crossover: batch sizes")
@@ -506,6 +551,8 @@ def main(argv=None):
         return run_crossover(args)
     if args.conv:
         return run_conv(args)
+    if args.solver_sweep:
+        return run_solver_sweep(args)
 
     import numpy as np
     import torch

@@ -80,7 +80,8 @@ typedef enum { CANOPY_FP32 = 0, CANOPY_BF16 = 1 } canopy_dtype;
  *               product above;
  *      NEUMANN  the finite series sum_{m=0..d} (-G_bb)^m, d the block's in-block depth;
  *      LEVEL    row-by-row substitution with the rows of equal in-block depth together;
- *      AUTO     LEVEL for blocks of in-block depth <= 3, FWDSUB otherwise. */
+ *      AUTO     NEUMANN for blocks of in-block depth <= 2, FWDSUB otherwise (measured on
+ *               level trees: the series wins at depth 0-2, substitution from 3 up). */
 typedef enum {
     CANOPY_SOLVE_AUTO = 0,
     CANOPY_SOLVE_FWDSUB = 1,
