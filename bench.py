@@ -447,6 +447,7 @@ def run_crossover(args):
             ell = torch.empty((B, T, H), device="cuda")
             S_par = [s.clone() for s in S0]
             S_ser = [s.clone() for s in S0]
+            S_hyb = [s.clone() for s in S0]
             snaps = torch.empty((B, T, H, 128, 128), device="cuda")
 
             def round_parallel():
@@ -458,6 +459,12 @@ def run_crossover(args):
                 for l in range(L):
                     tsv.serial_verify(q[l], k[l], v[l], al[l], be[l], S_ser[l], parent, snapshots=snaps)
                     tsv.serial_commit(snaps, S_ser[l], parent, path_cur, plen_cur, out=S_ser[l])
+
+            def round_hybrid():
+                for l in range(L):
+                    _, Uh, _, _ = tsv.hybrid_verify(q[l], k[l], v[l], al[l], be[l], S_hyb[l], parent,
+                                                    snapshots=snaps)
+                    tsv.commit(S_hyb[l], k[l], Uh, al[l], parent, path_cur, plen_cur, out=S_hyb[l])
 
             def timed(fn, r0, rounds):
                 """Rounds r0 .. r0+rounds-1 of the chain (each with its own accepted path)."""
@@ -485,16 +492,25 @@ def run_crossover(args):
             R_ser = int(max(0, min(R - 1, args.serial_budget * 1e6 / max(us_ser_probe, 1.0))))
             us_ser = timed(round_serial, 1, R_ser) if R_ser >= 1 else us_ser_probe
             rounds_ser = 1 + R_ser
-            err = None
-            if rounds_ser == R:
-                num = max(float((a - b).abs().max()) / max(float(b.abs().max()), 1e-30) for a, b in zip(S_par, S_ser))
-                err = num
+            us_hyb_probe = timed(round_hybrid, 0, 1)
+            R_hyb = int(max(0, min(R - 1, args.serial_budget * 1e6 / max(us_hyb_probe, 1.0))))
+            us_hyb = timed(round_hybrid, 1, R_hyb) if R_hyb >= 1 else us_hyb_probe
+            rounds_hyb = 1 + R_hyb
+
+            def rel(xs, ys):
+                return max(float((a - b).abs().max()) / max(float(b.abs().max()), 1e-30) for a, b in zip(xs, ys))
+            err = rel(S_par, S_ser) if rounds_ser == R else None
+            err_h = rel(S_par, S_hyb) if rounds_hyb == R else None
             rec = {"W": W, "T": T, "depth": D, "B": B, "H": H, "layers": L,
                    "rounds_parallel": R, "rounds_serial": rounds_ser,
                    "us_per_round_parallel": round(us_par, 2), "us_per_round_serial": round(us_ser, 2),
                    "us_per_layer_parallel": round(us_par / L, 3), "us_per_layer_serial": round(us_ser / L, 3),
                    "speedup_parallel_over_serial": round(us_ser / us_par, 3),
-                   "final_state_rel_err_parallel_vs_serial": err}
+                   "final_state_rel_err_parallel_vs_serial": err,
+                   "rounds_hybrid": rounds_hyb, "us_per_layer_hybrid": round(us_hyb / L, 3),
+                   "speedup_parallel_over_hybrid": round(us_hyb / us_par, 3),
+                   "speedup_hybrid_over_serial": round(us_ser / us_hyb, 3),
+                   "final_state_rel_err_parallel_vs_hybrid": err_h}
             line = json.dumps(rec)
             print(line, flush=True)
             if out:
@@ -602,7 +618,7 @@ def main(argv=None):
         g_c = graph_of(commit, args.steps)
         us_commit = time_graph(g_c, args.steps)
         del g_c
-    us_serial = None
+    us_serial = us_hybrid = None
     if not args.no_serial:
         snaps = torch.empty((B, T, H, 128, 128), device="cuda")
 
@@ -616,6 +632,15 @@ def main(argv=None):
             g_s = graph_of(serial, n_ser)
             us_serial = time_graph(g_s, n_ser)
             del g_s
+        def hybrid():
+            tsv.hybrid_verify(d["q"], d["k"], d["v"], d["alpha"], d["beta"], d["S0"], d["parent"],
+                              snapshots=snaps, tree_len=d["tree_len"])
+        if args.eager:
+            us_hybrid = time_eager(hybrid, n_ser, 3)
+        else:
+            g_h = graph_of(hybrid, n_ser)
+            us_hybrid = time_graph(g_h, n_ser)
+            del g_h
         del snaps
 
     if args.copy_probe:
@@ -657,6 +682,7 @@ def main(argv=None):
         "verify_nodes_per_s": round(nodes / (us_verify * 1e-6), 1),
         "commit_us": round(us_commit, 3),
         "serial_verify_us": None if us_serial is None else round(us_serial, 3),
+        "hybrid_verify_us": None if us_hybrid is None else round(us_hybrid, 3),
         "roofline": {"bound": "hbm", "kernel": verify_kernel_name(T, args.solver, B * H, args.waves, dt),
                      "achieved": round(achieved, 2), "peak": HBM_PEAK_GBS, "unit": "GB/s",
                      "frac": round(achieved / HBM_PEAK_GBS, 5),

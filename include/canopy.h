@@ -183,6 +183,20 @@ canopy_status canopy_serial_verify(const void *q, const void *k, const void *v,
                                    float *snapshots, int32_t *tree_status, hipStream_t stream);
 
 /*
+ * Chain-decomposed hybrid ("What the papers report": SpecLA's chain-decomposed hybrid; "M4",
+ * optional third contender): a heavy-light decomposition of the tree into chains, each chain
+ * run serially with the state in registers, the chains of one level (light edges above them)
+ * in parallel. Same inputs and outputs as canopy_serial_verify, except that only fork nodes
+ * (two or more children) get a snapshot: the other rows of `snapshots` are not written. Its U
+ * feeds canopy_commit like canopy_tree_verify's.
+ */
+canopy_status canopy_hybrid_verify(const void *q, const void *k, const void *v,
+                                   const float *alpha, const float *beta, const float *S0,
+                                   const int32_t *parent, const int32_t *tree_len, int B, int H,
+                                   int HV, int T, canopy_dtype in_dtype, float *O, float *U,
+                                   float *snapshots, int32_t *tree_status, hipStream_t stream);
+
+/*
  * Commit for the serial baseline: the accepted path's last node's snapshot (written by
  * canopy_serial_verify) becomes the new state (S0 itself for an empty path). Path checks and
  * path_status as in canopy_commit.

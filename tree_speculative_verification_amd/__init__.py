@@ -63,6 +63,8 @@ def load():
     lib.canopy_serial_verify.restype = i
     lib.canopy_serial_commit.argtypes = [P, P, P, P, P, P, i, i, i, P, P, u64]
     lib.canopy_serial_commit.restype = i
+    lib.canopy_hybrid_verify.argtypes = [P, P, P, P, P, P, P, P, i, i, i, i, i, P, P, P, P, u64]
+    lib.canopy_hybrid_verify.restype = i
     lib.canopy_tree_conv.argtypes = [P, i, P, P, P, P, i, i, i, i, i, P, P, u64]
     lib.canopy_tree_conv.restype = i
     lib.canopy_conv_commit.argtypes = [P, i, P, P, P, P, P, i, i, i, i, P, P, u64]
@@ -224,6 +226,34 @@ def serial_verify(q, k, v, alpha, beta, S0, parent, snapshots=None, tree_len=Non
         _req(snapshots, "snapshots", torch.float32, (B, T, HV, d, d))
     status = torch.empty((B,), dtype=torch.int32, device=dev)
     _check(load().canopy_serial_verify(_ptr(q), _ptr(k), _ptr(v), _ptr(alpha), _ptr(beta),
+                                       _ptr(S0), _ptr(parent), _ptr(tl), B, H, HV, T, dt, _ptr(O),
+                                       _ptr(U), _ptr(snapshots), _ptr(status), _stream()))
+    return O, U, snapshots, status
+
+
+def hybrid_verify(q, k, v, alpha, beta, S0, parent, snapshots=None, tree_len=None):
+    """The chain-decomposed hybrid: O, U [B,T,HV,128], the snapshot buffer [B,T,HV,128,128]
+    (only fork nodes' rows written) and the tree status [B]. Arguments as ``serial_verify``."""
+    B, T, H, d = q.shape
+    dt = _in_dtype(q)
+    H, HV = _heads(q, v)
+    for name, t in (("q", q), ("k", k)):
+        _req(t, name, q.dtype, (B, T, H, d))
+    _req(v, "v", q.dtype, (B, T, HV, d))
+    _req(alpha, "alpha", torch.float32, (B, T, HV))
+    _req(beta, "beta", torch.float32, (B, T, HV))
+    _req(S0, "S0", torch.float32, (B, HV, d, d))
+    _req(parent, "parent", torch.int32, (B, T))
+    tl = _tree_len(tree_len, B)
+    dev = q.device
+    O = torch.empty((B, T, HV, d), dtype=torch.float32, device=dev)
+    U = torch.empty((B, T, HV, d), dtype=torch.float32, device=dev)
+    if snapshots is None:
+        snapshots = torch.empty((B, T, HV, d, d), dtype=torch.float32, device=dev)
+    else:
+        _req(snapshots, "snapshots", torch.float32, (B, T, HV, d, d))
+    status = torch.empty((B,), dtype=torch.int32, device=dev)
+    _check(load().canopy_hybrid_verify(_ptr(q), _ptr(k), _ptr(v), _ptr(alpha), _ptr(beta),
                                        _ptr(S0), _ptr(parent), _ptr(tl), B, H, HV, T, dt, _ptr(O),
                                        _ptr(U), _ptr(snapshots), _ptr(status), _stream()))
     return O, U, snapshots, status

@@ -134,6 +134,22 @@ canopy_status canopy_serial_verify(const void *q, const void *k, const void *v,
     return from_hip(launch_serial(a, stream));
 }
 
+canopy_status canopy_hybrid_verify(const void *q, const void *k, const void *v,
+                                   const float *alpha, const float *beta, const float *S0,
+                                   const int32_t *parent, const int32_t *tree_len, int B, int H,
+                                   int HV, int T, canopy_dtype in_dtype, float *O, float *U,
+                                   float *snapshots, int32_t *tree_status, hipStream_t stream) {
+    if (!q || !k || !v || !alpha || !beta || !S0 || !parent || !O || !U || !snapshots)
+        return CANOPY_ERR_ARG;
+    if (!sizes_ok(B, HV, T) || !heads_ok(H, HV)) return CANOPY_ERR_ARG;
+    if (!aligned16(S0) || !aligned16(v) || !aligned16(O) || !aligned16(U) || !aligned16(snapshots))
+        return CANOPY_ERR_ARG;
+    if (in_dtype != CANOPY_FP32 && in_dtype != CANOPY_BF16) return CANOPY_ERR_UNSUPPORTED;
+    SerialArgs a{q, k, v, alpha, beta, S0, parent, tree_len, B, HV, H, T, in_dtype == CANOPY_BF16,
+                 O, U, snapshots, tree_status};
+    return from_hip(launch_hybrid(a, stream));
+}
+
 canopy_status canopy_serial_commit(const float *snapshots, const float *S0, const int32_t *parent,
                                    const int32_t *tree_len, const int32_t *path,
                                    const int32_t *path_len, int B, int HV, int T, float *S_new,

@@ -110,6 +110,7 @@ hipError_t launch_prep(const PrepArgs &a, hipStream_t stream);
 hipError_t launch_commit(const CommitArgs &a, hipStream_t stream);
 hipError_t launch_serial(const SerialArgs &a, hipStream_t stream);
 hipError_t launch_serial_commit(const SerialCommitArgs &a, hipStream_t stream);
+hipError_t launch_hybrid(const SerialArgs &a, hipStream_t stream);
 hipError_t launch_tree_conv(const ConvArgs &a, hipStream_t stream);
 hipError_t launch_conv_commit(const ConvCommitArgs &a, hipStream_t stream);
 

@@ -5,8 +5,8 @@
 // and writes its own snapshot, o and u. One wave per (sequence, head, 16 value columns); the
 // wave keeps its 128 x 16 state slice in registers (lane: 8 rows x 4 columns) and reloads it
 // from a snapshot only when a node's parent is not the node just processed.
-#include "canopy_device.hpp"
 #include "canopy_kernels.hpp"
+#include "canopy_step.hpp"
 #include <limits.h>
 
 namespace canopy {
@@ -61,50 +61,11 @@ __global__ __launch_bounds__(64) void serial_kernel(SerialArgs a) {
             for (int m = 0; m < 8; ++m) S[m] = reinterpret_cast<const float4 *>(src + (rg + 16 * m) * D + col)[0];
         }
         const size_t node = base + static_cast<size_t>(i) * rs;
-        const size_t qknode = qkbase + static_cast<size_t>(i) * qkrs;
-        const float al = a.alpha[sbase + static_cast<size_t>(i) * H];
-        const float be = a.beta[sbase + static_cast<size_t>(i) * H];
-        float kv[8], qv[8];
-#pragma unroll
-        for (int m = 0; m < 8; ++m) {
-            const size_t el = qknode + rg + 16 * m;
-            kv[m] = BF ? bf16_to_f32(static_cast<const uint16_t *>(a.k)[el]) : static_cast<const float *>(a.k)[el];
-            qv[m] = BF ? bf16_to_f32(static_cast<const uint16_t *>(a.q)[el]) : static_cast<const float *>(a.q)[el];
-        }
-        float4 part = make_float4(0.f, 0.f, 0.f, 0.f);
-#pragma unroll
-        for (int m = 0; m < 8; ++m) {
-            S[m].x *= al; S[m].y *= al; S[m].z *= al; S[m].w *= al;
-            part.x += S[m].x * kv[m]; part.y += S[m].y * kv[m];
-            part.z += S[m].z * kv[m]; part.w += S[m].w * kv[m];
-        }
-#pragma unroll
-        for (int o = 4; o < 64; o <<= 1) {
-            part.x += __shfl_xor(part.x, o, 64); part.y += __shfl_xor(part.y, o, 64);
-            part.z += __shfl_xor(part.z, o, 64); part.w += __shfl_xor(part.w, o, 64);
-        }
-        float4 vv;
-        if (BF) {
-            const uint16_t *vp = static_cast<const uint16_t *>(a.v) + node + col;
-            vv = make_float4(bf16_to_f32(vp[0]), bf16_to_f32(vp[1]), bf16_to_f32(vp[2]), bf16_to_f32(vp[3]));
-        } else {
-            vv = reinterpret_cast<const float4 *>(static_cast<const float *>(a.v) + node + col)[0];
-        }
-        const float4 u = make_float4(be * (vv.x - part.x), be * (vv.y - part.y),
-                                     be * (vv.z - part.z), be * (vv.w - part.w));
-        float4 o = make_float4(0.f, 0.f, 0.f, 0.f);
-#pragma unroll
-        for (int m = 0; m < 8; ++m) {
-            S[m].x += kv[m] * u.x; S[m].y += kv[m] * u.y;
-            S[m].z += kv[m] * u.z; S[m].w += kv[m] * u.w;
-            o.x += S[m].x * qv[m]; o.y += S[m].y * qv[m];
-            o.z += S[m].z * qv[m]; o.w += S[m].w * qv[m];
-        }
-#pragma unroll
-        for (int s = 4; s < 64; s <<= 1) {
-            o.x += __shfl_xor(o.x, s, 64); o.y += __shfl_xor(o.y, s, 64);
-            o.z += __shfl_xor(o.z, s, 64); o.w += __shfl_xor(o.w, s, 64);
-        }
+        NodeIn in;
+        load_node<BF>(in, a.q, a.k, qkbase + static_cast<size_t>(i) * qkrs, rg, a.v, node + col, a.alpha,
+                      a.beta, sbase + static_cast<size_t>(i) * H);
+        float4 o, u;
+        gdn_step(S, in, o, u);
         float *dst = a.snap + ((static_cast<size_t>(b) * T + i) * H + h) * SS;
 #pragma unroll
         for (int m = 0; m < 8; ++m) reinterpret_cast<float4 *>(dst + (rg + 16 * m) * D + col)[0] = S[m];
