@@ -401,9 +401,12 @@ def crossover_cells():
 
 def run_crossover(args):
     """24 stacked GDN layers, rounds of verify + commit that chain each layer's committed
-    state, parallel (tree verify + commit) against the serial fork baseline (serial verify +
-    snapshot commit), for every depth x width cell and batch size. One round (24 layers) is
-    captured as a HIP graph; the accepted path of every round is copied in before its replay."""
+    state, for every depth x width cell and batch size: the parallel path (24 tree verifies,
+    then one launch committing all 24 layers), the chain hybrid (the same with the hybrid's
+    verify) and the serial fork baseline (serial verify + snapshot commit per layer: committing
+    all layers at once would keep 24 layers of per-node snapshots, 206 GB at B = 16, T = 256).
+    One round (24 layers) is captured as a HIP graph; the accepted path of every round is copied
+    in before its replay."""
     import numpy as np
     import torch
     import synth
@@ -443,7 +446,7 @@ def run_crossover(args):
             path_cur = torch.empty((B, T), dtype=torch.int32, device="cuda")
             plen_cur = torch.empty((B,), dtype=torch.int32, device="cuda")
             O = torch.empty((B, T, H, 128), device="cuda")
-            U = torch.empty_like(O)
+            Us = [torch.empty_like(O) for _ in range(L)]  # every layer's U, for the one commit
             ell = torch.empty((B, T, H), device="cuda")
             S_par = [s.clone() for s in S0]
             S_ser = [s.clone() for s in S0]
@@ -451,9 +454,10 @@ def run_crossover(args):
             snaps = torch.empty((B, T, H, 128, 128), device="cuda")
 
             def round_parallel():
+                # every layer verifies, then one launch commits the accepted path in all of them
                 for l in range(L):
-                    tsv.tree_verify(q[l], k[l], v[l], al[l], be[l], S_par[l], parent, out=(O, U, ell))
-                    tsv.commit(S_par[l], k[l], U, al[l], parent, path_cur, plen_cur, out=S_par[l])
+                    tsv.tree_verify(q[l], k[l], v[l], al[l], be[l], S_par[l], parent, out=(O, Us[l], ell))
+                tsv.commit_layers(S_par, k, Us, al, parent, path_cur, plen_cur, outs=S_par)
 
             def round_serial():
                 for l in range(L):
@@ -461,10 +465,11 @@ def run_crossover(args):
                     tsv.serial_commit(snaps, S_ser[l], parent, path_cur, plen_cur, out=S_ser[l])
 
             def round_hybrid():
+                Uh = []
                 for l in range(L):
-                    _, Uh, _, _ = tsv.hybrid_verify(q[l], k[l], v[l], al[l], be[l], S_hyb[l], parent,
-                                                    snapshots=snaps)
-                    tsv.commit(S_hyb[l], k[l], Uh, al[l], parent, path_cur, plen_cur, out=S_hyb[l])
+                    Uh.append(tsv.hybrid_verify(q[l], k[l], v[l], al[l], be[l], S_hyb[l], parent,
+                                                snapshots=snaps)[1])
+                tsv.commit_layers(S_hyb, k, Uh, al, parent, path_cur, plen_cur, outs=S_hyb)
 
             def timed(fn, r0, rounds):
                 """Rounds r0 .. r0+rounds-1 of the chain (each with its own accepted path)."""
@@ -516,7 +521,7 @@ def run_crossover(args):
             if out:
                 out.write(line + "\n")
                 out.flush()
-            del q, k, v, al, be, S0, S_par, S_ser, snaps, O, U
+            del q, k, v, al, be, S0, S_par, S_ser, S_hyb, snaps, O, Us
             torch.cuda.empty_cache()
     if out:
         out.close()

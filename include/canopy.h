@@ -170,6 +170,21 @@ canopy_status canopy_commit(const float *S0, const void *k, canopy_dtype in_dtyp
                             hipStream_t stream);
 
 /*
+ * Every GDN layer's commit in one launch. After acceptance all L layers commit the same
+ * accepted path on the same tree, each with its own state, keys, pseudo-values and gates, so
+ * one launch serves them all (a decode step commits every layer at once). Arguments as
+ * canopy_commit, with the per-layer ones given as HOST arrays of L device pointers
+ * (1 <= L <= 64): S0[l], k[l], U[l], alpha[l], S_new[l] (S_new[l] may be S0[l]). path_status,
+ * as in canopy_commit, is written once. Results equal L calls of canopy_commit bit for bit.
+ */
+canopy_status canopy_commit_layers(int L, const float *const *S0, const void *const *k,
+                                   canopy_dtype in_dtype, const float *const *U,
+                                   const float *const *alpha, const int32_t *parent,
+                                   const int32_t *tree_len, const int32_t *path,
+                                   const int32_t *path_len, int B, int H, int HV, int T,
+                                   float *const *S_new, int32_t *path_status, hipStream_t stream);
+
+/*
  * Serial fork baseline ("Design decisions / Serial baseline"): walk the nodes in order; each
  * node starts from its parent's per-node state snapshot (S0 for a root), takes one step of the
  * gated delta rule and writes its own snapshot, output and pseudo-value. Same inputs and
@@ -244,6 +259,18 @@ canopy_status canopy_conv_commit(const void *x, canopy_dtype in_dtype, const voi
                                  const int32_t *parent, const int32_t *tree_len,
                                  const int32_t *path, const int32_t *path_len, int B, int T, int C,
                                  int K, void *state_new, int32_t *path_status, hipStream_t stream);
+
+/*
+ * canopy_serial_commit for L layers in one launch (host arrays of L device pointers,
+ * 1 <= L <= 64; path_status written once), the serial baseline's counterpart of
+ * canopy_commit_layers.
+ */
+canopy_status canopy_serial_commit_layers(int L, const float *const *snapshots,
+                                          const float *const *S0, const int32_t *parent,
+                                          const int32_t *tree_len, const int32_t *path,
+                                          const int32_t *path_len, int B, int HV, int T,
+                                          float *const *S_new, int32_t *path_status,
+                                          hipStream_t stream);
 
 #ifdef __cplusplus
 }

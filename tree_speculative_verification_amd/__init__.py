@@ -63,6 +63,10 @@ def load():
     lib.canopy_serial_verify.restype = i
     lib.canopy_serial_commit.argtypes = [P, P, P, P, P, P, i, i, i, P, P, u64]
     lib.canopy_serial_commit.restype = i
+    lib.canopy_commit_layers.argtypes = [i, P, P, i, P, P, P, P, P, P, i, i, i, i, P, P, u64]
+    lib.canopy_commit_layers.restype = i
+    lib.canopy_serial_commit_layers.argtypes = [i, P, P, P, P, P, P, i, i, i, P, P, u64]
+    lib.canopy_serial_commit_layers.restype = i
     lib.canopy_hybrid_verify.argtypes = [P, P, P, P, P, P, P, P, i, i, i, i, i, P, P, P, P, u64]
     lib.canopy_hybrid_verify.restype = i
     lib.canopy_tree_conv.argtypes = [P, i, P, P, P, P, i, i, i, i, i, P, P, u64]
@@ -314,3 +318,59 @@ def conv_commit(x, conv_state, parent, path, path_len, tree_len=None, out=None):
                                      _ptr(path), _ptr(path_len), B, T, C, K, _ptr(new),
                                      _ptr(status), _stream()))
     return new, status
+
+
+def _ptr_array(ts):
+    arr = (ctypes.c_void_p * len(ts))(*[t.data_ptr() for t in ts])
+    return arr
+
+
+def commit_layers(S0s, ks, Us, alphas, parent, path, path_len, outs=None, tree_len=None):
+    """``commit`` for L layers sharing the tree and the accepted path, in one launch: lists of
+    per-layer S0, k, U and alpha (``outs`` may be the S0 list for in-place commits). Returns
+    (list of S_new, path status [B])."""
+    L = len(S0s)
+    assert len(ks) == len(Us) == len(alphas) == L
+    k0 = ks[0]
+    B, T, H, d = k0.shape
+    dt = _in_dtype(k0)
+    H, HV = _heads(k0, Us[0])
+    for l in range(L):
+        _req(S0s[l], "S0", torch.float32, (B, HV, d, d))
+        _req(ks[l], "k", k0.dtype, (B, T, H, d))
+        _req(Us[l], "U", torch.float32, (B, T, HV, d))
+        _req(alphas[l], "alpha", torch.float32, (B, T, HV))
+    _req(parent, "parent", torch.int32, (B, T))
+    _req(path, "path", torch.int32, (B, T))
+    _req(path_len, "path_len", torch.int32, (B,))
+    tl = _tree_len(tree_len, B)
+    if outs is None:
+        outs = [torch.empty_like(s) for s in S0s]
+    for o in outs:
+        _req(o, "out", torch.float32, (B, HV, d, d))
+    status = torch.empty((B,), dtype=torch.int32, device=k0.device)
+    _check(load().canopy_commit_layers(L, _ptr_array(S0s), _ptr_array(ks), dt, _ptr_array(Us),
+                                       _ptr_array(alphas), _ptr(parent), _ptr(tl), _ptr(path),
+                                       _ptr(path_len), B, H, HV, T, _ptr_array(outs), _ptr(status),
+                                       _stream()))
+    return outs, status
+
+
+def serial_commit_layers(snapshots, S0s, parent, path, path_len, outs=None, tree_len=None):
+    """``serial_commit`` for L layers in one launch; returns (list of S_new, path status)."""
+    L = len(S0s)
+    B, T, H, d, _ = snapshots[0].shape
+    for l in range(L):
+        _req(snapshots[l], "snapshots", torch.float32, (B, T, H, d, d))
+        _req(S0s[l], "S0", torch.float32, (B, H, d, d))
+    _req(parent, "parent", torch.int32, (B, T))
+    _req(path, "path", torch.int32, (B, T))
+    _req(path_len, "path_len", torch.int32, (B,))
+    tl = _tree_len(tree_len, B)
+    if outs is None:
+        outs = [torch.empty_like(s) for s in S0s]
+    status = torch.empty((B,), dtype=torch.int32, device=parent.device)
+    _check(load().canopy_serial_commit_layers(L, _ptr_array(snapshots), _ptr_array(S0s), _ptr(parent),
+                                              _ptr(tl), _ptr(path), _ptr(path_len), B, H, T,
+                                              _ptr_array(outs), _ptr(status), _stream()))
+    return outs, status

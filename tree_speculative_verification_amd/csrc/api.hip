@@ -118,6 +118,34 @@ canopy_status canopy_commit(const float *S0, const void *k, canopy_dtype in_dtyp
     return from_hip(launch_commit(a, stream));
 }
 
+canopy_status canopy_commit_layers(int L, const float *const *S0, const void *const *k,
+                                   canopy_dtype in_dtype, const float *const *U,
+                                   const float *const *alpha, const int32_t *parent,
+                                   const int32_t *tree_len, const int32_t *path,
+                                   const int32_t *path_len, int B, int H, int HV, int T,
+                                   float *const *S_new, int32_t *path_status, hipStream_t stream) {
+    if (L < 1 || L > kMaxLayers) return CANOPY_ERR_ARG;
+    if (!S0 || !k || !U || !alpha || !S_new || !parent || !path || !path_len) return CANOPY_ERR_ARG;
+    if (!sizes_ok(B, HV, T) || !heads_ok(H, HV)) return CANOPY_ERR_ARG;
+    if (static_cast<long long>(L) * B * HV * 16 > 2147483647LL) return CANOPY_ERR_ARG;
+    if (in_dtype != CANOPY_FP32 && in_dtype != CANOPY_BF16) return CANOPY_ERR_UNSUPPORTED;
+    CommitLayersArgs la{};
+    la.base = CommitArgs{nullptr, nullptr, in_dtype == CANOPY_BF16, nullptr, nullptr, parent, tree_len,
+                         path, path_len, B, HV, H, T, nullptr, path_status};
+    la.L = L;
+    for (int l = 0; l < L; ++l) {
+        if (!S0[l] || !k[l] || !U[l] || !alpha[l] || !S_new[l]) return CANOPY_ERR_ARG;
+        if (!aligned16(S0[l]) || !aligned16(k[l]) || !aligned16(U[l]) || !aligned16(S_new[l]))
+            return CANOPY_ERR_ARG;
+        la.S0[l] = S0[l];
+        la.k[l] = k[l];
+        la.U[l] = U[l];
+        la.alpha[l] = alpha[l];
+        la.S_new[l] = S_new[l];
+    }
+    return from_hip(launch_commit_layers(la, stream));
+}
+
 canopy_status canopy_serial_verify(const void *q, const void *k, const void *v,
                                    const float *alpha, const float *beta, const float *S0,
                                    const int32_t *parent, const int32_t *tree_len, int B, int H,
@@ -194,6 +222,30 @@ canopy_status canopy_conv_commit(const void *x, canopy_dtype in_dtype, const voi
     ConvCommitArgs a{x, conv_state, parent, tree_len, path, path_len, B, T, C, K,
                      in_dtype == CANOPY_BF16, state_new, path_status};
     return from_hip(launch_conv_commit(a, stream));
+}
+
+canopy_status canopy_serial_commit_layers(int L, const float *const *snapshots,
+                                          const float *const *S0, const int32_t *parent,
+                                          const int32_t *tree_len, const int32_t *path,
+                                          const int32_t *path_len, int B, int HV, int T,
+                                          float *const *S_new, int32_t *path_status,
+                                          hipStream_t stream) {
+    if (L < 1 || L > kMaxLayers) return CANOPY_ERR_ARG;
+    if (!snapshots || !S0 || !S_new || !parent || !path || !path_len) return CANOPY_ERR_ARG;
+    if (!sizes_ok(B, HV, T)) return CANOPY_ERR_ARG;
+    if (static_cast<long long>(L) * B * HV * 4 > 2147483647LL) return CANOPY_ERR_ARG;
+    SerialCommitLayersArgs la{};
+    la.base = SerialCommitArgs{nullptr, nullptr, parent, tree_len, path, path_len, B, HV, T, nullptr,
+                               path_status};
+    la.L = L;
+    for (int l = 0; l < L; ++l) {
+        if (!snapshots[l] || !S0[l] || !S_new[l]) return CANOPY_ERR_ARG;
+        if (!aligned16(snapshots[l]) || !aligned16(S0[l]) || !aligned16(S_new[l])) return CANOPY_ERR_ARG;
+        la.snap[l] = snapshots[l];
+        la.S0[l] = S0[l];
+        la.S_new[l] = S_new[l];
+    }
+    return from_hip(launch_serial_commit_layers(la, stream));
 }
 
 }  // extern "C"

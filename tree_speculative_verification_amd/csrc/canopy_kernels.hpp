@@ -60,6 +60,28 @@ struct SerialCommitArgs {
     int32_t *path_status;
 };
 
+// One launch for the commits of up to kMaxLayers layers that share the tree and the accepted
+// path: per-layer pointers by value, the rest from base (whose own per-layer pointers are
+// unused).
+constexpr int kMaxLayers = 64;
+struct CommitLayersArgs {
+    CommitArgs base;
+    int L;
+    const float *S0[kMaxLayers];
+    const void *k[kMaxLayers];
+    const float *U[kMaxLayers];
+    const float *alpha[kMaxLayers];
+    float *S_new[kMaxLayers];
+};
+
+struct SerialCommitLayersArgs {
+    SerialCommitArgs base;
+    int L;
+    const float *snap[kMaxLayers];
+    const float *S0[kMaxLayers];
+    float *S_new[kMaxLayers];
+};
+
 // Root-path causal convolution: x [B,T,C], w [C,K] fp32, state [B,K-1,C], y [B,T,C]; x, state
 // and y in the input dtype.
 struct ConvArgs {
@@ -111,6 +133,8 @@ hipError_t launch_commit(const CommitArgs &a, hipStream_t stream);
 hipError_t launch_serial(const SerialArgs &a, hipStream_t stream);
 hipError_t launch_serial_commit(const SerialCommitArgs &a, hipStream_t stream);
 hipError_t launch_hybrid(const SerialArgs &a, hipStream_t stream);
+hipError_t launch_commit_layers(const CommitLayersArgs &la, hipStream_t stream);
+hipError_t launch_serial_commit_layers(const SerialCommitLayersArgs &la, hipStream_t stream);
 hipError_t launch_tree_conv(const ConvArgs &a, hipStream_t stream);
 hipError_t launch_conv_commit(const ConvCommitArgs &a, hipStream_t stream);
 

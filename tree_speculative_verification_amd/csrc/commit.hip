@@ -143,9 +143,9 @@ struct Chunk {
     }
 };
 
+// The commit of workgroup g's (sequence, head, 8 state rows).
 template <bool BF, int NG>
-__global__ __launch_bounds__(64) void commit_kernel(CommitArgs a) {
-    const int g = xcd_remap(blockIdx.x, gridDim.x);
+__device__ __forceinline__ void commit_body(const CommitArgs &a, int g) {
     const int chunk = g % (D / CROWS);
     const int bh = g / (D / CROWS);
     const int H = a.H, T = a.T;
@@ -200,6 +200,37 @@ __global__ __launch_bounds__(64) void commit_kernel(CommitArgs a) {
                                                Pa * s0[q].z + acc[q].z, Pa * s0[q].w + acc[q].w);
         reinterpret_cast<float4 *>(Sn + (krow + q) * D)[c4] = o;
     }
+}
+
+template <bool BF, int NG>
+__global__ __launch_bounds__(64) void commit_kernel(CommitArgs a) {
+    commit_body<BF, NG>(a, xcd_remap(blockIdx.x, gridDim.x));
+}
+
+// Every layer's commit in one launch: the layers share the tree and the accepted path, each has
+// its own state, keys, pseudo-values and gates. Layer 0 writes the path status.
+template <bool BF, int NG>
+__global__ __launch_bounds__(64) void commit_layers_kernel(CommitLayersArgs la) {
+    const int g = xcd_remap(blockIdx.x, gridDim.x);
+    const int per_layer = la.base.B * la.base.H * (D / CROWS);
+    const int l = g / per_layer;
+    CommitArgs a = la.base;
+    a.S0 = la.S0[l];
+    a.k = la.k[l];
+    a.U = la.U[l];
+    a.alpha = la.alpha[l];
+    a.S_new = la.S_new[l];
+    if (l != 0) a.path_status = nullptr;
+    commit_body<BF, NG>(a, g - l * per_layer);
+}
+
+hipError_t launch_commit_layers(const CommitLayersArgs &la, hipStream_t stream) {
+    const dim3 grid(static_cast<unsigned>(la.L * la.base.B * la.base.H * (D / CROWS))), block(64);
+    if (la.base.bf16)
+        hipLaunchKernelGGL((commit_layers_kernel<true, CGRP>), grid, block, 0, stream, la);
+    else
+        hipLaunchKernelGGL((commit_layers_kernel<false, CGRP>), grid, block, 0, stream, la);
+    return hipGetLastError();
 }
 
 hipError_t launch_commit(const CommitArgs &a, hipStream_t stream) {

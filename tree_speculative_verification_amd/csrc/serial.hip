@@ -79,9 +79,8 @@ __global__ __launch_bounds__(64) void serial_kernel(SerialArgs a) {
 
 // Commit for the serial baseline: the accepted node's snapshot becomes the new state. One
 // workgroup per (sequence, head, 32 state rows), float4 copies; path checks as canopy_commit.
-__global__ __launch_bounds__(256) void serial_commit_kernel(SerialCommitArgs a) {
+__device__ __forceinline__ void serial_commit_body(const SerialCommitArgs &a, int g) {
     __shared__ int s_bad;
-    const int g = xcd_remap(blockIdx.x, gridDim.x);
     const int chunk = g % 4, bh = g / 4;
     const int H = a.H, T = a.T;
     const int b = bh / H, h = bh % H;
@@ -114,6 +113,29 @@ __global__ __launch_bounds__(256) void serial_commit_kernel(SerialCommitArgs a) 
     const float4 *src = reinterpret_cast<const float4 *>(state + chunk * 32 * D);
 #pragma unroll
     for (int k = 0; k < 4; ++k) dst[tid + 256 * k] = src[tid + 256 * k];
+}
+
+__global__ __launch_bounds__(256) void serial_commit_kernel(SerialCommitArgs a) {
+    serial_commit_body(a, xcd_remap(blockIdx.x, gridDim.x));
+}
+
+// Every layer's serial commit in one launch (layer 0 writes the path status).
+__global__ __launch_bounds__(256) void serial_commit_layers_kernel(SerialCommitLayersArgs la) {
+    const int g = xcd_remap(blockIdx.x, gridDim.x);
+    const int per_layer = la.base.B * la.base.H * 4;
+    const int l = g / per_layer;
+    SerialCommitArgs a = la.base;
+    a.snap = la.snap[l];
+    a.S0 = la.S0[l];
+    a.S_new = la.S_new[l];
+    if (l != 0) a.path_status = nullptr;
+    serial_commit_body(a, g - l * per_layer);
+}
+
+hipError_t launch_serial_commit_layers(const SerialCommitLayersArgs &la, hipStream_t stream) {
+    const dim3 grid(static_cast<unsigned>(la.L * la.base.B * la.base.H * 4)), block(256);
+    hipLaunchKernelGGL(serial_commit_layers_kernel, grid, block, 0, stream, la);
+    return hipGetLastError();
 }
 
 hipError_t launch_serial_commit(const SerialCommitArgs &a, hipStream_t stream) {
