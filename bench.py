@@ -380,6 +380,213 @@ def cpu_baseline(inp, budget_s=10.0):
                 kind="oracle", sample=f"{len(times)} full layers of this workload, median")
 
 
+# The workloads of the timing protocol: every configuration of the pages' workload table that
+# fits one GPU, small and large batch.
+PROTOCOL_WORKLOADS = ["binary7_fp32", "topk16_b1", "skewed64_b1", "skewed64_b16", "random256_b1",
+                      "random256_b16"]
+
+
+def environment():
+    """Software versions, for the record of a measurement."""
+    import subprocess
+    import torch
+    env = {"torch": torch.__version__, "hip_runtime": torch.version.hip, "rocm": None, "hipcc": None,
+           "gpu": torch.cuda.get_device_name(0)}
+    try:
+        with open("/opt/rocm/.info/version") as fh:
+            env["rocm"] = fh.read().strip()
+    except OSError:
+        pass
+    try:
+        r = subprocess.run(["/opt/rocm/bin/hipcc", "--version"], capture_output=True, text=True, timeout=60)
+        env["hipcc"] = next((ln.strip() for ln in r.stdout.splitlines() if "version" in ln.lower()), None)
+    except (OSError, subprocess.SubprocessError):
+        pass
+    return env
+
+
+def gpu_state():
+    """Clocks, temperature and power of GPU 0 as amd-smi reports them (None if unavailable)."""
+    import subprocess
+    for cmd in (["amd-smi", "metric", "-g", "0", "--json"], ["/opt/rocm/bin/amd-smi", "metric", "-g", "0", "--json"]):
+        try:
+            r = subprocess.run(cmd, capture_output=True, text=True, timeout=60)
+        except (OSError, subprocess.SubprocessError):
+            continue
+        if r.returncode != 0:
+            continue
+        try:
+            data = json.loads(r.stdout)
+        except ValueError:
+            return {"raw": r.stdout[:2000]}
+        gpu = data[0] if isinstance(data, list) and data else data
+        if isinstance(gpu, dict) and "gpu_data" in gpu:
+            gpu = gpu["gpu_data"][0] if gpu["gpu_data"] else gpu
+        if isinstance(gpu, dict):
+            return {k: gpu[k] for k in ("clock", "temperature", "power") if k in gpu} or {"keys": sorted(gpu)[:40]}
+        return {"raw": r.stdout[:2000]}
+    return None
+
+
+def oracle_timing(inp, wl, reps=5):
+    """The oracle's wall time per layer (µs), median of `reps`, on every host core and on one.
+    Large workloads run a slice of whole (sequence, head) problems, as many heads of sequence 0
+    as there are threads (all cores) or 2 heads (one core), scaled by the number of such
+    problems in the layer; every (sequence, head) problem costs the same up to its tree."""
+    import oracle
+    all_threads = oracle.num_threads()
+    B, H = wl["B"], wl["H"]
+    res = {}
+    for label, threads in (("all_cores", all_threads), ("one_core", 1)):
+        oracle.set_threads(threads)
+        full = B * H * wl["T"] <= 2048
+        hs = H if full else min(H, max(2, threads))
+        if full:
+            sub = dict(inp)
+            scale = 1.0
+        else:
+            sub = {n: inp[n][:1, :, :hs] for n in ("q", "k", "v", "alpha", "beta")}
+            sub["S0"] = inp["S0"][:1, :hs]
+            for n in ("parent", "path"):
+                sub[n] = inp[n][:1]
+            sub["path_len"] = inp["path_len"][:1]
+            scale = (B * H) / hs
+        times = []
+        for rep in range(reps + 1):  # the first call (thread team start-up) is not timed
+            t0 = time.perf_counter()
+            oracle.gdn_tree(sub["parent"], sub["q"], sub["k"], sub["v"], sub["alpha"], sub["beta"], sub["S0"])
+            oracle.commit(sub["parent"], sub["path"], sub["path_len"], sub["k"], sub["v"], sub["alpha"],
+                          sub["beta"], sub["S0"])
+            if rep:
+                times.append((time.perf_counter() - t0) * scale)
+        times.sort()
+        res[label] = {"us_per_layer": round(times[len(times) // 2] * 1e6, 1), "threads": threads,
+                      "sample": "whole layer" if full else f"sequence 0, {hs} heads, scaled x{scale:g}"}
+    oracle.set_threads(all_threads)
+    return res
+
+
+def _stats(xs):
+    import numpy as np
+    xs = np.asarray(xs, dtype=np.float64)
+    return {"median_us": round(float(np.median(xs)), 3), "p10_us": round(float(np.percentile(xs, 10)), 3),
+            "p90_us": round(float(np.percentile(xs, 90)), 3), "n": int(xs.size)}
+
+
+def run_protocol(args):
+    """Timing distributions per kernel (verify, commit, and the serial and hybrid verifies):
+      warm  a HIP graph of back-to-back calls (--steps, a quarter of them for the serial and
+            hybrid kernels) replayed 10 times with events around each replay: median, p10 and
+            p90 of the per-call average over the replays (stream time);
+      cold  --warmup + --steps eager rounds in which every call is preceded by a fill kernel
+            writing 512 MiB (evicting L2 and the Infinity Cache), outside the events around the
+            call, the compared kernels interleaved call by call: median, p10 and p90 of the
+            per-call stream time (which includes the launch gap of an eager call).
+    Run under rocprofv3 --kernel-trace, the same run gives per-dispatch device times, warm and
+    cold apart (--protocol-summary). Also reports the oracle on all host cores and on one,
+    software versions, and the GPU's clocks, temperature and power before and after."""
+    import torch
+    import tree_speculative_verification_amd as tsv
+    tsv.load()
+    names = args.protocol_workloads or PROTOCOL_WORKLOADS
+    out = open(args.out, "a") if args.out else None
+    flush = torch.empty(512 * 2 ** 20 // 4, dtype=torch.float32, device="cuda")
+    for name in names:
+        wl = WORKLOADS[name]
+        B, H, T = wl["B"], wl["H"], wl["T"]
+        inp = build_inputs(wl)
+        d = to_device(inp)
+        O = torch.empty((B, T, H, 128), device="cuda")
+        U = torch.empty_like(O)
+        ell = torch.empty((B, T, H), device="cuda")
+        S_new = torch.empty_like(d["S0"])
+        snaps = torch.empty((B, T, H, 128, 128), device="cuda")
+        calls = {
+            "verify": lambda: tsv.tree_verify(d["q"], d["k"], d["v"], d["alpha"], d["beta"], d["S0"],
+                                              d["parent"], out=(O, U, ell)),
+            "commit": lambda: tsv.commit(d["S0"], d["k"], U, d["alpha"], d["parent"], d["path"],
+                                         d["path_len"], out=S_new),
+            "serial_verify": lambda: tsv.serial_verify(d["q"], d["k"], d["v"], d["alpha"], d["beta"],
+                                                       d["S0"], d["parent"], snapshots=snaps),
+            "hybrid_verify": lambda: tsv.hybrid_verify(d["q"], d["k"], d["v"], d["alpha"], d["beta"],
+                                                       d["S0"], d["parent"], snapshots=snaps),
+        }
+        state_before = gpu_state()
+        calls["verify"]()  # U for the commit
+        torch.cuda.synchronize()
+        warm = {}
+        for k, fn in calls.items():
+            n = args.steps if k in ("verify", "commit") else max(10, args.steps // 4)
+            g = graph_of(fn, n)
+            g.replay()
+            torch.cuda.synchronize()
+            pairs = [(torch.cuda.Event(enable_timing=True), torch.cuda.Event(enable_timing=True))
+                     for _ in range(10)]
+            for e0, e1 in pairs:
+                e0.record()
+                g.replay()
+                e1.record()
+            torch.cuda.synchronize()
+            warm[k] = _stats([a.elapsed_time(b) * 1000.0 / n for a, b in pairs])
+            warm[k]["calls_per_replay"] = n
+            del g
+        print(f"[protocol] {name}: warm done", file=sys.stderr, flush=True)
+        n = args.steps + args.warmup
+        ev = {k: [(torch.cuda.Event(enable_timing=True), torch.cuda.Event(enable_timing=True))
+                  for _ in range(n)] for k in calls}
+        for it in range(n):
+            for k, fn in calls.items():
+                flush.fill_(float(it))
+                e0, e1 = ev[k][it]
+                e0.record()
+                fn()
+                e1.record()
+            if it % 25 == 24:
+                torch.cuda.synchronize()
+        torch.cuda.synchronize()
+        cold = {k: _stats([a.elapsed_time(b) * 1000.0 for a, b in pairs[args.warmup:]])
+                for k, pairs in ev.items()}
+        print(f"[protocol] {name}: cold done", file=sys.stderr, flush=True)
+        state_after = gpu_state()
+        del snaps
+        torch.cuda.empty_cache()
+        rec = {"workload": name, "desc": wl["desc"], "steps": args.steps, "warmup": args.warmup,
+               "stream_time": {"warm": warm, "cold": cold},
+               "oracle": oracle_timing(inp, wl), "kernel_digest": kernel_digest(),
+               "gpu_state_before": state_before, "gpu_state_after": state_after}
+        if name == names[0]:
+            rec["environment"] = environment()
+        line = json.dumps(rec)
+        print(line, flush=True)
+        if out:
+            out.write(line + "\n")
+            out.flush()
+    if out:
+        out.close()
+    return 0
+
+
+def protocol_summary(trace_csv, warmup=25):
+    """Per-dispatch device times from a rocprofv3 kernel trace of a --protocol run of one
+    workload: each library kernel's dispatches split into cold (the dispatch right before it
+    was the 512 MiB float fill) and warm (the rest), the first `warmup` cold ones of each kernel
+    dropped; median, p10 and p90 of end - start."""
+    rows = list(csv.DictReader(open(trace_csv)))
+    rows.sort(key=lambda r: int(r["Start_Timestamp"]))
+    out, prev = {}, ""
+    for r in rows:
+        name = r["Kernel_Name"]
+        if "canopy::" in name:
+            short = name.split("canopy::")[1].split("(")[0].split("<")[0]
+            phase = "cold" if "FillFunctor<float>" in prev else "warm"
+            dur = (int(r["End_Timestamp"]) - int(r["Start_Timestamp"])) / 1000.0
+            out.setdefault(phase, {}).setdefault(short, []).append(dur)
+        prev = name
+    for k in out.get("cold", {}):
+        out["cold"][k] = out["cold"][k][warmup:]
+    return {ph: {k: _stats(v) for k, v in ks.items()} for ph, ks in out.items()}
+
+
 def crossover_cells():
     """Depth x width level trees: root, then levels of W nodes (the last one partial);
     W = 1 is a chain; shapes that coincide (stars) are kept once; depth 1..64."""
@@ -548,6 +755,13 @@ def main(argv=None):
                     help="time every solver on level trees over T, width and --batches")
     ap.add_argument("--conv", action="store_true",
                     help="time the root-path causal convolution and its commit instead")
+    ap.add_argument("--protocol", action="store_true",
+                    help="per-call timing distributions (median, p10, p90), warm and cold, with "
+                         "the oracle on all cores and one, versions and GPU clocks")
+    ap.add_argument("--protocol-workloads", nargs="+", default=None, choices=sorted(WORKLOADS))
+    ap.add_argument("--protocol-summary", default="", metavar="CSV",
+                    help="device-time distributions from the rocprofv3 kernel trace CSV of a "
+                         "--protocol run (no GPU work)")
     ap.add_argument("--batches", type=int, nargs="+", default=[1, 4, 16], help="crossover: batch sizes")
     ap.add_argument("--max-t", type=int, default=0, help="crossover: skip trees larger than this")
     ap.add_argument("--serial-budget", type=float, default=2.0,
@@ -562,6 +776,9 @@ def main(argv=None):
     args = ap.parse_args(argv)
     if args.pmc_summary:
         return pmc_summary(args.pmc_summary, args.out or TRAFFIC_FILE)
+    if args.protocol_summary:
+        print(json.dumps(protocol_summary(args.protocol_summary)), flush=True)
+        return 0
 
     if args.gpus != 1 or int(os.environ.get("WORLD_SIZE", "1")) != 1:
         print("bench.py measures one GPU only: the verify and commit kernels shard by (sequence, "
@@ -574,6 +791,8 @@ def main(argv=None):
         return run_conv(args)
     if args.solver_sweep:
         return run_solver_sweep(args)
+    if args.protocol:
+        return run_protocol(args)
 
     import numpy as np
     import torch

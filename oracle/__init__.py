@@ -43,6 +43,7 @@ def _load():
         P = ctypes.c_void_p
         i = ctypes.c_int
         _lib.oracle_num_threads.restype = i
+        _lib.oracle_set_threads.argtypes = [i]
         _lib.oracle_tree_check.argtypes = [i, P]
         _lib.oracle_tree_check.restype = i
         _lib.oracle_tree_structure.argtypes = [i, i, P, P, P, P]
@@ -66,6 +67,11 @@ def _p(a):
 def num_threads() -> int:
     """OpenMP threads the oracle runs on (OMP_NUM_THREADS, else all cores)."""
     return int(_load().oracle_num_threads())
+
+
+def set_threads(n: int) -> None:
+    """Run later oracle calls on n OpenMP threads (timing on one core versus all of them)."""
+    _load().oracle_set_threads(int(n))
 
 
 def tree_structure(parent):

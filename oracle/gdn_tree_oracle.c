@@ -40,6 +40,15 @@ int oracle_num_threads(void) {
 #endif
 }
 
+/* Sets the OpenMP thread count of later calls (n >= 1); used to time the oracle on one core. */
+void oracle_set_threads(int n) {
+#ifdef _OPENMP
+    if (n >= 1) omp_set_num_threads(n);
+#else
+    (void)n;
+#endif
+}
+
 /* 0 if every node satisfies -1 <= parent[i] < i, else 1 + the first node that does not.
  * (Parents precede children; node 0 is therefore a root.) */
 int oracle_tree_check(int T, const int32_t *parent) {

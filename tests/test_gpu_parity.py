@@ -112,7 +112,7 @@ def test_tile_edges(canopy, T, dtype):
     d = to_device(inp)
     ref = run_oracle(inp)
     for solver, waves in (("fwdsub", 1), ("neumann", 2), ("level", 4), ("auto", 8), ("fwdsub", 8),
-                          ("auto", 2), ("neumann", 4)):
+                          ("auto", 2), ("neumann", 4), ("fwdsub", 4), ("auto", 4)):
         _say("edge", T, dtype, kind, solver, waves)
         O, U, ell, mask, depth, st = _verify(canopy, d, solver=solver, waves=waves)
         assert_close_heads("O", O, ref["O"], TOL[dtype])
