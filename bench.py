@@ -587,6 +587,57 @@ def protocol_summary(trace_csv, warmup=25):
     return {ph: {k: _stats(v) for k, v in ks.items()} for ph, ks in out.items()}
 
 
+def run_peaks(args):
+    """Measured references for the roofline fractions: HBM bandwidth of a large device copy
+    (read + write) and of a large reduction (read), dense MFMA throughput of a large bf16 and
+    fp32 library GEMM (hipBLASLt through torch.matmul), and the time of an empty graph-replayed
+    launch (a one-element fill), the floor of any single-launch step."""
+    import torch
+    res = {}
+
+    def ev_time(fn, reps):
+        fn()
+        torch.cuda.synchronize()
+        e0 = torch.cuda.Event(enable_timing=True)
+        e1 = torch.cuda.Event(enable_timing=True)
+        e0.record()
+        for _ in range(reps):
+            fn()
+        e1.record()
+        torch.cuda.synchronize()
+        return e0.elapsed_time(e1) / 1000.0 / reps  # seconds per call
+
+    n = 2 ** 31 // 4  # 2 GiB of fp32
+    a = torch.empty(n, dtype=torch.float32, device="cuda").fill_(1.0)
+    b = torch.empty_like(a)
+    t = ev_time(lambda: b.copy_(a), 20)
+    res["hbm_copy_gbs"] = round(2 * a.numel() * 4 / t / 1e9, 1)
+    t = ev_time(lambda: a.sum(), 20)
+    res["hbm_read_gbs"] = round(a.numel() * 4 / t / 1e9, 1)
+    del a, b
+    torch.cuda.empty_cache()
+    for name, dt in (("bf16", torch.bfloat16), ("fp32", torch.float32)):
+        m = 8192
+        x = torch.randn(m, m, device="cuda").to(dt)
+        y = torch.randn(m, m, device="cuda").to(dt)
+        t = ev_time(lambda: torch.matmul(x, y), 10)
+        res[f"gemm_{name}_tflops"] = round(2 * m ** 3 / t / 1e12, 1)
+        del x, y
+    torch.cuda.empty_cache()
+    z = torch.empty(1, device="cuda")
+    g = graph_of(lambda: z.fill_(0.0), 200)
+    res["empty_launch_us"] = round(time_graph(g, 200), 3)
+    res["notes"] = ("copy counts read + write bytes; GEMMs are 8192^3 through torch.matmul; the empty "
+                    "launch is a one-element fill replayed 200 times in one graph")
+    res["environment"] = environment()
+    line = json.dumps(res)
+    print(line, flush=True)
+    if args.out:
+        with open(args.out, "w") as fh:
+            fh.write(line + "\n")
+    return 0
+
+
 def crossover_cells():
     """Depth x width level trees: root, then levels of W nodes (the last one partial);
     W = 1 is a chain; shapes that coincide (stars) are kept once; depth 1..64."""
@@ -759,6 +810,8 @@ def main(argv=None):
                     help="per-call timing distributions (median, p10, p90), warm and cold, with "
                          "the oracle on all cores and one, versions and GPU clocks")
     ap.add_argument("--protocol-workloads", nargs="+", default=None, choices=sorted(WORKLOADS))
+    ap.add_argument("--peaks", action="store_true",
+                    help="measured HBM, GEMM and launch references for the roofline fractions")
     ap.add_argument("--protocol-summary", default="", metavar="CSV",
                     help="device-time distributions from the rocprofv3 kernel trace CSV of a "
                          "--protocol run (no GPU work)")
@@ -793,6 +846,8 @@ def main(argv=None):
         return run_solver_sweep(args)
     if args.protocol:
         return run_protocol(args)
+    if args.peaks:
+        return run_peaks(args)
 
     import numpy as np
     import torch
