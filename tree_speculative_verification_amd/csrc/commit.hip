@@ -198,7 +198,7 @@ __device__ __forceinline__ void commit_body(const CommitArgs &a, int g) {
         const float4 o = st != 0 ? make_float4(qnan, qnan, qnan, qnan)
                                  : make_float4(Pa * s0[q].x + acc[q].x, Pa * s0[q].y + acc[q].y,
                                                Pa * s0[q].z + acc[q].z, Pa * s0[q].w + acc[q].w);
-        reinterpret_cast<float4 *>(Sn + (krow + q) * D)[c4] = o;
+        __builtin_nontemporal_store(f32x4{o.x, o.y, o.z, o.w}, reinterpret_cast<f32x4 *>(Sn + (krow + q) * D) + c4);
     }
 }
 

@@ -619,7 +619,7 @@ __global__ __launch_bounds__(NW * 64) void verify_kernel(VerifyArgs a) {
 #pragma unroll
                     for (int e = 0; e < 4; ++e) {
                         const int i = 64 * r + 16 * ti + 4 * lg + e;
-                        if (i < Tb) a.O[base + static_cast<size_t>(i) * rs + col0 + lr] = oacc[ti][e];
+                        if (i < Tb) store_nt(a.O + base + static_cast<size_t>(i) * rs + col0 + lr, oacc[ti][e]);
                     }
             }
             // The stage is free and the next operands are in LDS for every wave.

@@ -185,7 +185,7 @@ __global__ __launch_bounds__(64 * NWV) void verify_small_kernel(VerifyArgs a) {
         const int i = 4 * lg + e;
         if (i < Tb) {
             a.U[base + static_cast<size_t>(i) * rs + col0 + lr] = bad ? qnan : u[e];
-            a.O[base + static_cast<size_t>(i) * rs + col0 + lr] = bad ? qnan : oc[e];
+            store_nt(a.O + base + static_cast<size_t>(i) * rs + col0 + lr, bad ? qnan : oc[e]);
         }
     }
 }

@@ -386,7 +386,7 @@ __global__ __launch_bounds__(1024) void verify_wide_kernel(VerifyArgs a) {
             if (i < Tb) {
                 const size_t o = base + static_cast<size_t>(i) * rs + colw + 16 * ct + lr;
                 a.U[o] = bad ? qnan : u[ct][e];
-                a.O[o] = bad ? qnan : oacc[ct][e];
+                store_nt(a.O + o, bad ? qnan : oacc[ct][e]);
             }
         }
     (void)nsb;
