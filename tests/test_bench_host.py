@@ -1,0 +1,123 @@
+"""Host-side logic of the benchmark (no GPU): the algorithmic byte and flop counts behind the
+roofline fractions, checked against the workload table's figures (bytes per node and head,
+per-launch totals at C1-C4); the kernel the bench names for each size; the traffic file's
+digest gate; the warm/cold split of a kernel trace; the one-GPU exit."""
+import csv
+import json
+import os
+
+import pytest
+
+import bench
+
+
+def test_bytes_per_node_and_head():
+    # bf16: q, k, v (768 B), alpha and beta (8 B), O and U (1,024 B), ell (4 B) = 1,804 B;
+    # fp32 inputs: 2,572 B. Per (sequence, head) 64 KiB of S0, plus 4 B of parent per node.
+    for dt, per in (("bf16", 1804), ("fp32", 2572)):
+        one = bench.verify_bytes(1, 1, 1, dt)
+        two = bench.verify_bytes(1, 1, 2, dt)
+        assert two - one == per + 4
+        assert one == 65536 + per + 4
+
+
+@pytest.mark.parametrize("args,expect", [
+    ((1, 2, 7, "fp32"), 167_108),              # C1: 0.167 MB
+    ((1, 32, 16, "bf16"), 3_020_864),          # C2: 3.02 MB
+    ((1, 32, 64, "bf16"), 5_792_000),          # C3 per sequence: 5.79 MB
+    ((16, 32, 256, "bf16"), 270_024_704),      # C4: 270 MB
+])
+def test_verify_bytes_at_the_configs(args, expect):
+    assert bench.verify_bytes(*args) == expect
+
+
+def test_grouped_heads_and_ragged_bytes():
+    # 16 q/k heads for 32 value heads: q and k bytes halve; a ragged batch counts real nodes
+    full = bench.verify_bytes(1, 32, 16, "bf16")
+    grouped = bench.verify_bytes(1, 32, 16, "bf16", HK=16)
+    assert full - grouped == 16 * 16 * 2 * 128 * 2
+    assert bench.verify_bytes(2, 32, 16, "bf16", nodes=20) < bench.verify_bytes(2, 32, 16, "bf16")
+
+
+def test_commit_bytes_c2():
+    # C2 commit with a 3-node path: 4.27 MB (S0 read and S_new written per head dominate)
+    assert bench.commit_bytes(1, 32, 3) == 4_268_440
+
+
+def test_verify_flops_dense_tile():
+    assert bench.verify_flops(1, 32, 16) == 37_748_736            # C2: 37.7 MFLOP
+    assert bench.verify_flops(16, 32, 256) == 25_769_803_776      # C4: 25.8 GFLOP
+    assert bench.verify_flops_ragged(32, [16, 16]) == bench.verify_flops(2, 32, 16)
+
+
+@pytest.mark.parametrize("T,solver,heads,waves,dtype,kernel", [
+    (16, "auto", 32, 0, "bf16", "verify_small_kernel"),
+    (16, "neumann", 32, 0, "fp32", "verify_small_kernel"),
+    (16, "fwdsub", 32, 0, "bf16", "verify_kernel"),
+    (17, "auto", 32, 0, "bf16", "verify_mid_kernel"),
+    (64, "level", 512, 0, "bf16", "verify_kernel"),
+    (128, "auto", 64, 0, "bf16", "verify_wide_kernel"),
+    (128, "auto", 128, 0, "bf16", "verify_kernel"),
+    (256, "fwdsub", 512, 2, "bf16", "verify_wide_kernel"),
+    (256, "auto", 32, 0, "fp32", "verify_kernel"),
+    (256, "auto", 32, 8, "bf16", "verify_kernel"),
+])
+def test_kernel_names_follow_the_dispatch(T, solver, heads, waves, dtype, kernel):
+    assert bench.verify_kernel_name(T, solver, heads, waves, dtype) == kernel
+
+
+def test_traffic_gated_by_digest(tmp_path, monkeypatch):
+    entry = {"verify": {"hbm_bytes_per_launch": 123}}
+    path = tmp_path / "traffic.json"
+    path.write_text(json.dumps({"kernel_digest": bench.kernel_digest(),
+                                "workloads": {"topk16_b1:auto:0": entry}}))
+    monkeypatch.setattr(bench, "TRAFFIC_FILE", str(path))
+    assert bench.measured_traffic("topk16_b1", "auto", 0) == 123
+    assert bench.measured_traffic("topk16_b1", "auto", 8) is None
+    path.write_text(json.dumps({"kernel_digest": "0" * 16, "workloads": {"topk16_b1:auto:0": entry}}))
+    assert bench.measured_traffic("topk16_b1", "auto", 0) is None
+
+
+def test_digest_follows_the_kernel_sources(tmp_path, monkeypatch):
+    (tmp_path / "a.hip").write_text("x")
+    (tmp_path / "api.hip").write_text("host side")
+    monkeypatch.setattr(bench, "KERNEL_SOURCE_DIR", str(tmp_path))
+    d0 = bench.kernel_digest()
+    (tmp_path / "api.hip").write_text("host side, changed")
+    assert bench.kernel_digest() == d0          # the C ABI file is not device code
+    (tmp_path / "a.hip").write_text("y")
+    assert bench.kernel_digest() != d0
+
+
+def test_protocol_summary_splits_warm_and_cold(tmp_path):
+    fill = "void at::native::vectorized_elementwise_kernel<4, at::native::FillFunctor<float>, x>"
+    other_fill = "void at::native::vectorized_elementwise_kernel<4, at::native::FillFunctor<long>, x>"
+    ver = "void canopy::verify_small_kernel<true, 1>(canopy::VerifyArgs)"
+    rows, t = [], 0
+
+    def add(name, dur):
+        nonlocal t
+        rows.append({"Kernel_Name": name, "Start_Timestamp": str(t), "End_Timestamp": str(t + dur)})
+        t += dur + 100
+
+    add(other_fill, 10)
+    add(ver, 5000)          # after an int64 fill: warm
+    for _ in range(3):
+        add(ver, 3000)      # warm
+    for d in (9000, 7000, 8000):
+        add(fill, 50000)
+        add(ver, d)         # cold
+    path = tmp_path / "trace.csv"
+    with open(path, "w", newline="") as fh:
+        w = csv.DictWriter(fh, fieldnames=list(rows[0]))
+        w.writeheader()
+        w.writerows(rows)
+    res = bench.protocol_summary(str(path), warmup=1)
+    assert res["warm"]["verify_small_kernel"]["n"] == 4
+    assert res["cold"]["verify_small_kernel"]["n"] == 2                 # first cold call dropped
+    assert res["cold"]["verify_small_kernel"]["median_us"] == pytest.approx(7.5)
+
+
+def test_more_than_one_gpu_is_refused(capsys):
+    assert bench.main(["--gpus", "2"]) == 2
+    assert "one GPU" in capsys.readouterr().err
