@@ -1,5 +1,6 @@
 """Parity of the chain-decomposed hybrid (heavy-light chains, each serial, chains of a level in
-parallel) against the oracle's per-path recurrence, through the C ABI."""
+parallel) against the oracle's per-path recurrence, through the C ABI, at each workgroup width
+(8 or 16 waves for one sequence's heads, 4 beyond)."""
 import numpy as np
 import pytest
 
@@ -32,6 +33,8 @@ TREES = [
     (1, 3, 50, "star", "bf16", {}),
     (2, 2, 200, "random", "bf16", {}),
     (1, 2, 256, "level", "fp32", {"width": 4}),
+    (2, 20, 40, "random", "bf16", {}),      # more than 32 (sequence, head) pairs: 4 waves
+    (1, 32, 130, "skewed", "bf16", {}),     # one sequence, T > 64: 16 waves
 ]
 
 

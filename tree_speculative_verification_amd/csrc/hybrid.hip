@@ -165,14 +165,25 @@ __global__ __launch_bounds__(NW * 64) void hybrid_kernel(SerialArgs a) {
     }
 }
 
-hipError_t launch_hybrid(const SerialArgs &a, hipStream_t stream) {
-    constexpr int NW = 4;
+template <int NW>
+static hipError_t launch_hybrid_nw(const SerialArgs &a, hipStream_t stream) {
     const dim3 grid(static_cast<unsigned>(a.B * a.H * (D / 16))), block(NW * 64);
     if (a.bf16)
         hipLaunchKernelGGL((hybrid_kernel<true, NW>), grid, block, 0, stream, a);
     else
         hipLaunchKernelGGL((hybrid_kernel<false, NW>), grid, block, 0, stream, a);
     return hipGetLastError();
+}
+
+// Waves per workgroup: more waves run more chains of a level at once but leave fewer
+// workgroups per CU. Measured on MI355X (µs, 4 / 8 / 16 waves): B = 1, H = 32, T = 16:
+// 17.4 / 15.1 / 15.7; T = 256 random: 118 / 96 / 86; B = 16, T = 64: 283 / 403 / 700. With
+// 64 or more (sequence, head) pairs, 8 waves also lost on level trees of width 2-8 at
+// T = 128-256 (up to 2.5x at B = 4), so only a single sequence's 32 heads get wider groups.
+hipError_t launch_hybrid(const SerialArgs &a, hipStream_t stream) {
+    if (static_cast<long long>(a.B) * a.H <= 32)
+        return a.T > 64 ? launch_hybrid_nw<16>(a, stream) : launch_hybrid_nw<8>(a, stream);
+    return launch_hybrid_nw<4>(a, stream);
 }
 
 }  // namespace canopy
