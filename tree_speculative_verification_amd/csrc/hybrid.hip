@@ -2,12 +2,15 @@
 // optional third contender: heavy-light decomposition, each chain serial, chains in parallel).
 // The tree is cut into heavy paths: every node's heavy child is the child with the largest
 // subtree (the lowest id on ties), and a chain starts at a root or at a light child. A chain's
-// level is the number of light edges above it, at most log2(T). Chains of one level run in
-// parallel, one per wave, each walking its nodes in order with the state slice in registers
-// (the serial recurrence, canopy_step.hpp); it starts from the snapshot of its head's parent,
-// which a chain of the level above wrote, or from S0 for a root. Only fork nodes (two or more
-// children) write snapshots. One workgroup per (sequence, head, 16 value columns), NW waves;
-// the decomposition is computed in LDS from the ancestor bitmask of the shared tree prep.
+// level is the number of light edges above it, at most log2(T). The chains form one work list
+// ordered by (level, head id); each wave takes the next chain, waits until the snapshot of its
+// head's parent exists (a chain of a lower level writes it), and walks the chain node by node
+// with the state slice in registers (the serial recurrence, canopy_step.hpp), starting from that
+// snapshot or from S0 for a root. Only fork nodes (two or more children) write snapshots, and
+// each publishes a flag once its snapshot is written. Chains are handed out in level order, so
+// the chain a wave waits for is always already held by a wave that does not wait on anything
+// later: the list drains. One workgroup per (sequence, head, 16 value columns), NW waves; the
+// decomposition is computed in LDS from the ancestor bitmask of the shared tree prep.
 #include "canopy_kernels.hpp"
 #include "canopy_prep.hpp"
 #include "canopy_step.hpp"
@@ -17,13 +20,25 @@ namespace canopy {
 
 constexpr int HMAXT = 256;
 
+// Spin (with sleeps) until another wave of the workgroup has published `flag` with a release
+// store; the acquire makes that wave's earlier stores visible. Every wave of a workgroup is
+// resident and the publisher never waits on this wave, so the wait ends; the bound only
+// guarantees exit.
+__device__ __forceinline__ void wait_ready(int *flag) {
+    for (int n = 0; n < (1 << 24); ++n) {
+        if (__hip_atomic_load(flag, __ATOMIC_ACQUIRE, __HIP_MEMORY_SCOPE_WORKGROUP) != 0) return;
+        __builtin_amdgcn_s_sleep(1);
+    }
+}
+
 template <bool BF, int NW>
 __global__ __launch_bounds__(NW * 64) void hybrid_kernel(SerialArgs a) {
     constexpr int NT = NW * 64, TILES = D / 16;
     __shared__ PrepSmem<HMAXT> ps;
     __shared__ int s_par[HMAXT], s_best[HMAXT], s_heavy[HMAXT], s_nch[HMAXT], s_level[HMAXT];
     __shared__ uint32_t s_headmask[HMAXT / 32];
-    __shared__ int s_maxlevel;
+    __shared__ int s_order[HMAXT], s_ready[HMAXT];
+    __shared__ int s_maxlevel, s_nheads, s_next;
     const int g = xcd_remap(blockIdx.x, gridDim.x);
     const int tile = g % TILES, bh = g / TILES;
     const int H = a.H, T = a.T;
@@ -62,10 +77,14 @@ __global__ __launch_bounds__(NW * 64) void hybrid_kernel(SerialArgs a) {
             s_best[i] = -1;
             s_nch[i] = 0;
             s_level[i] = -1;
+            s_ready[i] = 0;
         }
     }
     if (tid < HMAXT / 32) s_headmask[tid] = 0u;
-    if (tid == 0) s_maxlevel = 0;
+    if (tid == 0) {
+        s_maxlevel = 0;
+        s_next = 0;
+    }
     __syncthreads();
     // subtree size of node i = the nodes whose inclusive mask holds i; the heavy child of each
     // node by an atomic max over (size, -id), and the child counts
@@ -101,67 +120,70 @@ __global__ __launch_bounds__(NW * 64) void hybrid_kernel(SerialArgs a) {
     }
     __syncthreads();
 
-    // ---- the chains, level by level; wave w takes the heads of a level numbered w, w + NW, ...
-    const int maxlevel = s_maxlevel;
-    for (int lvl = 0; lvl <= maxlevel; ++lvl) {
-        int k = 0;  // heads of this level seen so far, in id order
-        for (int c0 = 0; c0 < Tb; c0 += 64) {
-            const int i = c0 + lane;
-            const unsigned long long hm = __ballot(i < Tb && s_level[i] == lvl);
-            unsigned long long mine = hm;
-            // keep the heads whose running number k + rank is this wave's modulo NW
-            unsigned long long take = 0ull;
-            int r = 0;
-            while (mine) {
-                const int bit = __ffsll(static_cast<unsigned long long>(mine)) - 1;
-                mine &= mine - 1ull;
-                if ((k + r) % NW == wave) take |= 1ull << bit;
-                ++r;
-            }
-            k += r;
-            while (take) {
-                const int head = c0 + __ffsll(static_cast<unsigned long long>(take)) - 1;
-                take &= take - 1ull;
-                // ---- one chain from head: state from the parent's snapshot (or S0)
-                const int p = s_par[head];
-                const float *src = (p < 0) ? a.S0 + static_cast<size_t>(bh) * SS
-                                           : a.snap + ((static_cast<size_t>(b) * T + p) * H + h) * SS;
-                float4 S[8];
-#pragma unroll
-                for (int m = 0; m < 8; ++m) S[m] = reinterpret_cast<const float4 *>(src + (rg + 16 * m) * D + col)[0];
-                int node = head;
-                NodeIn cur;
-                load_node<BF>(cur, a.q, a.k, qkbase + static_cast<size_t>(node) * qkrs, rg, a.v,
-                              base + static_cast<size_t>(node) * rs + col, a.alpha, a.beta,
-                              sbase + static_cast<size_t>(node) * H);
-                while (node >= 0) {
-                    const int nxt = s_heavy[node];
-                    // the next node's inputs are requested before this step (the node itself
-                    // again at the chain's end, unused)
-                    const int nl = nxt >= 0 ? nxt : node;
-                    NodeIn nin;
-                    load_node<BF>(nin, a.q, a.k, qkbase + static_cast<size_t>(nl) * qkrs, rg, a.v,
-                                  base + static_cast<size_t>(nl) * rs + col, a.alpha, a.beta,
-                                  sbase + static_cast<size_t>(nl) * H);
-                    float4 o, u;
-                    gdn_step(S, cur, o, u);
-                    const size_t nodeo = base + static_cast<size_t>(node) * rs + col;
-                    if (rg == 0) {
-                        reinterpret_cast<float4 *>(a.O + nodeo)[0] = o;
-                        reinterpret_cast<float4 *>(a.U + nodeo)[0] = u;
-                    }
-                    if (s_nch[node] >= 2) {  // a fork: light chains start from this state
-                        float *dst = a.snap + ((static_cast<size_t>(b) * T + node) * H + h) * SS;
-#pragma unroll
-                        for (int m = 0; m < 8; ++m) reinterpret_cast<float4 *>(dst + (rg + 16 * m) * D + col)[0] = S[m];
-                    }
-                    cur = nin;
-                    node = nxt;
-                }
+    // ---- the work list: heads in (level, id) order, built by wave 0
+    if (wave == 0) {
+        const int maxlevel = s_maxlevel;
+        int cnt = 0;
+        for (int lvl = 0; lvl <= maxlevel; ++lvl) {
+            for (int c0 = 0; c0 < Tb; c0 += 64) {
+                const int i = c0 + lane;
+                const unsigned long long hm = __ballot(i < Tb && s_level[i] == lvl);
+                if ((hm >> lane) & 1ull) s_order[cnt + __popcll(hm & ((1ull << lane) - 1ull))] = i;
+                cnt += __popcll(hm);
             }
         }
-        // the level's fork snapshots are complete before the next level reads them
-        __syncthreads();
+        if (lane == 0) s_nheads = cnt;
+    }
+    __syncthreads();
+
+    // ---- the chains, each wave taking the next one from the list
+    const int nheads = s_nheads;
+    for (;;) {
+        int idx = 0;
+        if (lane == 0) idx = atomicAdd(&s_next, 1);
+        idx = __shfl(idx, 0, 64);
+        if (idx >= nheads) break;
+        const int head = s_order[idx];
+        const int p = s_par[head];
+        // the head's inputs are requested before waiting for its starting state
+        int node = head;
+        NodeIn cur;
+        load_node<BF>(cur, a.q, a.k, qkbase + static_cast<size_t>(node) * qkrs, rg, a.v,
+                      base + static_cast<size_t>(node) * rs + col, a.alpha, a.beta,
+                      sbase + static_cast<size_t>(node) * H);
+        if (p >= 0) wait_ready(&s_ready[p]);
+        // ---- one chain from head: state from the parent's snapshot (or S0)
+        const float *src = (p < 0) ? a.S0 + static_cast<size_t>(bh) * SS
+                                   : a.snap + ((static_cast<size_t>(b) * T + p) * H + h) * SS;
+        float4 S[8];
+#pragma unroll
+        for (int m = 0; m < 8; ++m) S[m] = reinterpret_cast<const float4 *>(src + (rg + 16 * m) * D + col)[0];
+        while (node >= 0) {
+            const int nxt = s_heavy[node];
+            // the next node's inputs are requested before this step (the node itself again at
+            // the chain's end, unused)
+            const int nl = nxt >= 0 ? nxt : node;
+            NodeIn nin;
+            load_node<BF>(nin, a.q, a.k, qkbase + static_cast<size_t>(nl) * qkrs, rg, a.v,
+                          base + static_cast<size_t>(nl) * rs + col, a.alpha, a.beta,
+                          sbase + static_cast<size_t>(nl) * H);
+            float4 o, u;
+            gdn_step(S, cur, o, u);
+            const size_t nodeo = base + static_cast<size_t>(node) * rs + col;
+            if (rg == 0) {
+                reinterpret_cast<float4 *>(a.O + nodeo)[0] = o;
+                reinterpret_cast<float4 *>(a.U + nodeo)[0] = u;
+            }
+            if (s_nch[node] >= 2) {  // a fork: light chains start from this state
+                float *dst = a.snap + ((static_cast<size_t>(b) * T + node) * H + h) * SS;
+#pragma unroll
+                for (int m = 0; m < 8; ++m) reinterpret_cast<float4 *>(dst + (rg + 16 * m) * D + col)[0] = S[m];
+                // the snapshot is written before the flag that lets other waves read it
+                __hip_atomic_store(&s_ready[node], 1, __ATOMIC_RELEASE, __HIP_MEMORY_SCOPE_WORKGROUP);
+            }
+            cur = nin;
+            node = nxt;
+        }
     }
 }
 
