@@ -202,9 +202,8 @@ canopy_status canopy_serial_verify(const void *q, const void *k, const void *v,
  * optional third contender): a heavy-light decomposition of the tree into chains, each chain
  * run serially with the state in registers, the chains in parallel, each starting as soon as
  * the snapshot it starts from is written. Same inputs and outputs as canopy_serial_verify,
- * except that only fork nodes
- * (two or more children) get a snapshot: the other rows of `snapshots` are not written. Its U
- * feeds canopy_commit like canopy_tree_verify's.
+ * except that only fork nodes (two or more children) get a snapshot: the other rows of
+ * `snapshots` are not written. Its U feeds canopy_commit like canopy_tree_verify's.
  */
 canopy_status canopy_hybrid_verify(const void *q, const void *k, const void *v,
                                    const float *alpha, const float *beta, const float *S0,
