@@ -835,7 +835,7 @@ def main(argv=None):
 
     if args.gpus != 1 or int(os.environ.get("WORLD_SIZE", "1")) != 1:
         print("bench.py measures one GPU only: the verify and commit kernels shard by (sequence, "
-              "head) with no exchange, and this build runs on a single MI355X. Use --gpus 1.",
+              "head) with no exchange, and this benchmark measures one MI355X. Use --gpus 1.",
               file=sys.stderr)
         return 2
     if args.crossover:
