@@ -127,12 +127,19 @@ __global__ __launch_bounds__(1024) void verify_wide_kernel(VerifyArgs a) {
     // and nodes past Tb are padding, dropped by selects later):
     // the prep chunk of a wave p < nch (lane = node 64p + lane), the wave's K and Q rows, the
     // thread's share of the S0 columns and the wave's V rows.
+    // Only the prep waves (one per 64-node chunk) load the tree and gates, and only the first
+    // NPAIR threads load S0: at the start of the kernel every wave's requests queue behind each
+    // other, so requests nothing reads cost time.
     const bool chunkw = p < nch;
     const int cnode = 64 * p + lane;
     const int cnodec = min(cnode, T - 1);
-    const int par_in = par[cnodec];
-    const float alpha_in = a.alpha[sbase + static_cast<size_t>(cnodec) * H];
-    const float beta_in = a.beta[sbase + static_cast<size_t>(cnodec) * H];
+    int par_in = -1;
+    float alpha_in = 1.f, beta_in = 0.f;
+    if (chunkw) {
+        par_in = par[cnodec];
+        alpha_in = a.alpha[sbase + static_cast<size_t>(cnodec) * H];
+        beta_in = a.beta[sbase + static_cast<size_t>(cnodec) * H];
+    }
     In kp[4], qp[4];
     {
         const size_t er = qkbase + static_cast<size_t>(min(16 * p + lr, T - 1)) * qkrs + 8 * lg;
@@ -149,10 +156,12 @@ __global__ __launch_bounds__(1024) void verify_wide_kernel(VerifyArgs a) {
         const float *S0p = a.S0 + static_cast<size_t>(bh) * D * D + colw;
 #pragma unroll
         for (int m = 0; m < PPT; ++m) {
-            const int x = min(tid + m * NT, NPAIR - 1);
-            const int c = x % (16 * NCT), kc = x / (16 * NCT);
+            const int x = tid + m * NT;
+            if (x < NPAIR) {
+                const int c = x % (16 * NCT), kc = x / (16 * NCT);
 #pragma unroll
-            for (int e = 0; e < 8; ++e) s0v[m][e] = S0p[(8 * kc + e) * D + c];
+                for (int e = 0; e < 8; ++e) s0v[m][e] = S0p[(8 * kc + e) * D + c];
+            }
         }
     }
     uint16_t vraw[NCT][4];
