@@ -3,7 +3,7 @@
 // general kernel (the canopy project page, "The tree closed form"), specialised to a single
 // 16-node tile:
 //   prep   pointer jumping over lanes (lane i = node i) with shuffles: ancestor mask, depth,
-//          l_i = sum of log alpha over path(i) (fp64 sums)
+//          path sums of log2 alpha (fp64), l_i = ln 2 times the sum
 //   a2     KS = K S0, QS = Q S0 (MFMA, K and Q fragments loaded straight from global memory)
 //   a3     K K^T and K Q^T (MFMA with K as the A operand, so lane (g, r) holds row r, columns
 //          4g..4g+3), masked and decay-weighted into -G (strict ancestors) and C (path)
@@ -81,10 +81,11 @@ __global__ __launch_bounds__(64 * NWV) void verify_small_kernel(VerifyArgs a) {
     // -1 for a length out of range, else 1 + the first bad node
     const int bad = sl.bad ? -1 : (badm ? (__ffsll(static_cast<unsigned long long>(badm))) : 0);
     const float beta = real ? beta_in : 0.f;
-    // log alpha in fp32 (its error is relative to each term, so it stays relative to any
-    // difference l_i - l_j of path sums); the sums themselves in fp64.
+    // log2 alpha by the hardware logarithm (about 1 ulp, an error relative to each term, so it
+    // stays relative to any difference of path sums); the sums themselves in fp64. ell holds
+    // path sums of log2 alpha: l = ell ln 2, P = 2^ell, decay ratios 2^(ell_i - ell_j).
     uint32_t mask = real ? (1u << node) : 0u;
-    double ell = real ? static_cast<double>(logf(alpha_in)) : 0.0;
+    double ell = real ? static_cast<double>(__builtin_amdgcn_logf(alpha_in)) : 0.0;
     int jmp = (real && !badn) ? par_in : -1;
     // After round r every node's jump pointer is 2^(r+1) levels up; depth < 16 ends it in 4.
     for (int round = 0; round < 4 && __any(jmp >= 0); ++round) {
@@ -97,8 +98,8 @@ __global__ __launch_bounds__(64 * NWV) void verify_small_kernel(VerifyArgs a) {
         ell = up ? ell + pl : ell;
         jmp = up ? pj : jmp;
     }
-    const float ellf = static_cast<float>(ell);
-    const float P = real ? expf(ellf) : 0.f;
+    const float ellf = static_cast<float>(ell * 0.69314718055994530942);  // l = ln P
+    const float P = real ? __builtin_amdgcn_exp2f(static_cast<float>(ell)) : 0.f;
     const int depth = real ? __popc(mask) - 1 : -1;
     // Tree depth by ballots on its 4 bits (depth < 16).
     int dmax = 0;
@@ -153,7 +154,7 @@ __global__ __launch_bounds__(64 * NWV) void verify_small_kernel(VerifyArgs a) {
             const int j = 4 * lg + e;
             const double lj = __shfl(ell, j, 64);
             // Off the path the exponent may overflow; the selects drop those entries.
-            const float gam = expf(static_cast<float>(li - lj));
+            const float gam = __builtin_amdgcn_exp2f(static_cast<float>(li - lj));
             const bool onpath = (mi >> j) & 1u;
             cm[e] = onpath ? gam * qk[e] : 0.f;
             gneg[e] = (onpath && i != j) ? -bi * gam * kk[e] : 0.f;
