@@ -12,7 +12,7 @@ struct PrepSmem {
     static constexpr int MW = MAXT / 32;
     int32_t jump[MAXT];
     uint32_t mask[MAXT][MW];
-    alignas(16) double ell[MAXT];
+    alignas(16) double ell[MAXT];  // path sums of log2 alpha: l = ell ln 2, P = 2^ell
     int bad;
 };
 
@@ -68,7 +68,9 @@ __device__ int tree_prep_compute(PrepSmem<MAXT> &s, const PrepIn<MAXT, NT> &in, 
             p = -1;
         }
         unsigned long long m = real ? (1ull << lane) : 0ull;
-        double l = real ? log(static_cast<double>(in.al[t])) : 0.0;
+        // log2 alpha by the hardware logarithm (about 1 ulp, relative to each term); the path
+        // sums in fp64
+        double l = real ? static_cast<double>(__builtin_amdgcn_logf(in.al[t])) : 0.0;
         const bool inside = p >= 64 * c;
         int jmp = inside ? p - 64 * c : -1;
         int ex = inside ? -1 : p;  // set again from the in-chunk root when the jumps reach it

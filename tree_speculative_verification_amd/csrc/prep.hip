@@ -22,7 +22,7 @@ __global__ __launch_bounds__(256) void prep_kernel(PrepArgs a) {
     if (a.ell)
         for (int i = tid; i < Tb; i += NT)
             a.ell[sbase + static_cast<size_t>(i) * H] =
-                bad ? __builtin_nanf("") : static_cast<float>(ps.ell[i]);
+                bad ? __builtin_nanf("") : static_cast<float>(ps.ell[i] * 0.69314718055994530942);
     if (h != 0) return;
     if (a.tree_status && tid == 0) a.tree_status[b] = bad;
     const int W = (T + 31) >> 5;

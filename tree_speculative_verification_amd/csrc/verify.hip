@@ -307,8 +307,9 @@ __global__ __launch_bounds__(NW * 64) void verify_kernel(VerifyArgs a) {
         if (i < MAXT) {
             float P = 0.f;
             if (i < Tb) {
-                P = static_cast<float>(exp(ps.ell[i]));
-                if (tile == 0) a.ell[sbase + static_cast<size_t>(i) * H] = static_cast<float>(ps.ell[i]);
+                P = __builtin_amdgcn_exp2f(static_cast<float>(ps.ell[i]));
+                if (tile == 0)
+                    a.ell[sbase + static_cast<size_t>(i) * H] = static_cast<float>(ps.ell[i] * 0.69314718055994530942);
             }
             s_beta[i] = (i < Tb) ? bet[t] : 0.f;
             s_P[i] = P;
@@ -407,9 +408,10 @@ __global__ __launch_bounds__(NW * 64) void verify_kernel(VerifyArgs a) {
                 float gv[4], cv[4];
 #pragma unroll
                 for (int e = 0; e < 4; ++e) {
-                    // exp(l_i - l_j) as 2^((l_i - l_j) log2 e). Off the path the exponent may
-                    // overflow (or read a node past T); the selects drop those entries.
-                    const float gam = __builtin_amdgcn_exp2f(static_cast<float>((li - lj[e]) * 1.4426950408889634));
+                    // exp(l_i - l_j) as 2 to the difference of the log2 path sums. Off the path
+                    // the exponent may overflow (or read a node past T); the selects drop those
+                    // entries.
+                    const float gam = __builtin_amdgcn_exp2f(static_cast<float>(li - lj[e]));
                     const bool on = (bits >> e) & 1u;
                     cv[e] = on ? gam * qk[e] : 0.f;
                     gv[e] = (on && i != jb + e) ? -bi * gam * kk[e] : 0.f;
