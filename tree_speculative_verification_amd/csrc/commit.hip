@@ -113,13 +113,23 @@ struct Chunk {
         const unsigned long long badm = __ballot(!ok);
         if (badm) bad = min(bad, 64 * c + __ffsll(static_cast<unsigned long long>(badm)));
         prev_last = __builtin_amdgcn_readlane(nd, 63);
-        // suffix sums of log2 alpha inside the chunk (fp64)
+        // suffix sums of log2 alpha inside the chunk (fp64). Lanes past the chunk's cnt
+        // positions hold 0, so shuffle steps 1 and 2 cover every sum of a chunk of at most 4
+        // positions (accepted paths are short); longer chunks take all six.
         const double la = inp ? static_cast<double>(__builtin_amdgcn_logf(al)) : 0.0;
         double v = la;
+        if (cnt <= 4) {
 #pragma unroll
-        for (int off = 1; off < 64; off <<= 1) {
-            const double tv = __shfl_down(v, off, 64);
-            v = lane + off < 64 ? v + tv : v;
+            for (int off = 1; off < 4; off <<= 1) {
+                const double tv = __shfl_down(v, off, 64);
+                v = lane + off < 64 ? v + tv : v;
+            }
+        } else {
+#pragma unroll
+            for (int off = 1; off < 64; off <<= 1) {
+                const double tv = __shfl_down(v, off, 64);
+                v = lane + off < 64 ? v + tv : v;
+            }
         }
         const double ctot = __shfl(v, 0, 64);  // log2 of the chunk's total decay
         tot += ctot;
