@@ -1,0 +1,314 @@
+"""The entry points captured in a HIP graph: every replay gives bit for bit what eager calls give
+on the inputs the static buffers hold at that replay.
+
+Each case captures one step (verify + commit; the hybrid and the serial fork with their
+commits; the convolution + its commit; the layered commit) with preallocated outputs, then
+replays it four times. Before each replay the static inputs are overwritten with one of two
+seeded input sets and the outputs with NaN, and unrelated eager work runs between replays;
+after each replay the outputs must equal those of eager calls on the same input set. The first
+replay is also checked against the oracle. One case per verify kernel (at most 16 nodes, 17 to
+64 nodes, 65 to 256 nodes with few heads, the blocked kernel in bf16 and fp32), plus a ragged
+batch."""
+from __future__ import annotations
+
+import numpy as np
+import pytest
+
+import oracle
+import synth
+from gpu_util import TOL, assert_close_heads, assert_close_state, oracle_commit, run_oracle, to_device
+
+pytestmark = pytest.mark.gpu
+
+REPLAYS = 4
+
+
+@pytest.fixture(scope="module")
+def canopy():
+    import torch
+    import tree_speculative_verification_amd as tsv
+    assert torch.cuda.is_available()
+    tsv.load()
+    return tsv
+
+
+def _say(*a):
+    print("[gpu]", *a, flush=True)
+
+
+def _np(t):
+    return t.detach().cpu().numpy()
+
+
+def _same(name, x, y):
+    x, y = np.asarray(x), np.asarray(y)
+    if x.dtype.kind == "f":
+        ok = np.array_equal(x, y, equal_nan=True)
+    else:
+        ok = np.array_equal(x, y)
+    assert ok, f"{name}: replay differs from the eager call"
+
+
+def _nan_like(t):
+    import torch
+    return torch.full_like(t, float("nan"))
+
+
+def _noise(canopy, d):
+    """Unrelated eager work between replays: a verify on its own outputs."""
+    canopy.tree_verify(d["q"], d["k"], d["v"], d["alpha"], d["beta"], d["S0"], d["parent"])
+
+
+CASES = [
+    # (B, H, T, tree, dtype, solver, waves, HK, lens)
+    (1, 32, 16, "topk", "bf16", "auto", 0, None, None),
+    (2, 8, 40, "random", "bf16", "auto", 0, None, None),
+    (1, 8, 130, "random", "bf16", "auto", 0, None, None),
+    (2, 8, 130, "random", "bf16", "auto", 8, 4, None),
+    (2, 4, 100, "skewed", "fp32", "level", 0, None, None),
+    (3, 4, 90, "random", "bf16", "auto", 0, 2, [90, 17, 1]),
+]
+
+
+@pytest.mark.parametrize("B,H,T,tree,dtype,solver,waves,HK,lens", CASES)
+def test_verify_commit_graph(canopy, B, H, T, tree, dtype, solver, waves, HK, lens):
+    import torch
+    seed = 5000 + T + B
+    kw = {"branching": (3, 4)} if tree == "topk" else None
+    sets = [synth.make_inputs(B, H, T, tree=tree, tree_kw=kw, dtype=dtype, seed=seed + s, HK=HK,
+                              tree_len=lens) for s in range(2)]
+    devs = [to_device(x) for x in sets]
+    tl = None if lens is None else torch.tensor(lens, dtype=torch.int32, device="cuda")
+    st = {n: t.clone() for n, t in devs[0].items()}
+    Ov = torch.empty((B, T, H, 128), dtype=torch.float32, device="cuda")
+    Ev = torch.empty((B, T, H), dtype=torch.float32, device="cuda")
+
+    def step(d, O, U, ell, Sn):
+        canopy.tree_verify(d["q"], d["k"], d["v"], d["alpha"], d["beta"], d["S0"], d["parent"],
+                           solver=solver, waves=waves, out=(O, U, ell), tree_len=tl)
+        _, pst = canopy.commit(d["S0"], d["k"], U, d["alpha"], d["parent"], d["path"], d["path_len"],
+                               out=Sn, tree_len=tl)
+        return pst
+
+    # eager results on both input sets, outputs pre-filled with NaN (padding rows stay NaN)
+    eager = []
+    for d in devs:
+        O, U, ell, Sn = (_nan_like(Ov), _nan_like(Ov), _nan_like(Ev), _nan_like(d["S0"]))
+        pst = step(d, O, U, ell, Sn)
+        torch.cuda.synchronize()
+        eager.append([_np(O), _np(U), _np(ell), _np(Sn), _np(pst)])
+
+    O, U, ell, Sn = (_nan_like(Ov), _nan_like(Ov), _nan_like(Ev), _nan_like(devs[0]["S0"]))
+    torch.cuda.synchronize()
+    _say("capture", B, H, T, tree, dtype, solver, waves, HK, lens)
+    g = torch.cuda.CUDAGraph()
+    with torch.cuda.graph(g):
+        pst = step(st, O, U, ell, Sn)
+    for r in range(REPLAYS):
+        src = r % 2
+        for n, t in st.items():
+            t.copy_(devs[src][n])
+        for t in (O, U, ell, Sn):
+            t.fill_(float("nan"))
+        pst.fill_(-7)
+        _noise(canopy, devs[1 - src])
+        torch.cuda.synchronize()
+        g.replay()
+        torch.cuda.synchronize()
+        _say("replay", r, "input set", src)
+        for name, x, y in zip(("O", "U", "ell", "S_new", "path status"),
+                              (_np(O), _np(U), _np(ell), _np(Sn), _np(pst)), eager[src]):
+            _same(name, x, y)
+        if r == 0:
+            inp = sets[0]
+            tol = TOL[dtype]
+            ref = oracle.gdn_tree_ragged(inp["parent"], lens, inp["q"], inp["k"], inp["v"],
+                                         inp["alpha"], inp["beta"], inp["S0"])
+            pad = np.isnan(ref["O"])  # rows past a sequence's length: left unwritten (NaN)
+            for name, x in (("O", _np(O)), ("U", _np(U))):
+                assert np.isnan(x[pad]).all(), f"{name}: a padding row was written"
+                assert_close_heads(name, np.where(pad, 0.0, x), np.where(pad, 0.0, ref[name]), tol)
+            S_ref, _ = oracle.commit_ragged(inp["parent"], lens, inp["path"], inp["path_len"], inp["k"],
+                                            inp["v"], inp["alpha"], inp["beta"], inp["S0"])
+            assert_close_state("S_new", _np(Sn), S_ref, tol)
+            assert _np(pst).tolist() == [0] * B
+    del g
+
+
+def test_hybrid_serial_graph(canopy):
+    """The chain hybrid with the closed-form commit of its U, and the serial fork with its
+    snapshot commit, in one graph."""
+    import torch
+    B, H, T = 2, 4, 48
+    sets = [synth.make_inputs(B, H, T, tree="random", dtype="bf16", seed=5200 + s) for s in range(2)]
+    devs = [to_device(x) for x in sets]
+    st = {n: t.clone() for n, t in devs[0].items()}
+    snaps_h = torch.empty((B, T, H, 128, 128), dtype=torch.float32, device="cuda")
+    snaps_s = torch.empty_like(snaps_h)
+
+    def step(d, Sh, Ss):
+        Oh, Uh, _, tsh = canopy.hybrid_verify(d["q"], d["k"], d["v"], d["alpha"], d["beta"], d["S0"],
+                                              d["parent"], snapshots=snaps_h)
+        _, psh = canopy.commit(d["S0"], d["k"], Uh, d["alpha"], d["parent"], d["path"], d["path_len"],
+                               out=Sh)
+        Os, _, _, tss = canopy.serial_verify(d["q"], d["k"], d["v"], d["alpha"], d["beta"], d["S0"],
+                                             d["parent"], snapshots=snaps_s)
+        _, pss = canopy.serial_commit(snaps_s, d["S0"], d["parent"], d["path"], d["path_len"], out=Ss)
+        return Oh, Uh, Os, tsh, psh, tss, pss
+
+    names = ("hybrid O", "hybrid U", "serial O", "hybrid tree status", "hybrid path status",
+             "serial tree status", "serial path status", "hybrid S_new", "serial S_new")
+    eager = []
+    for d in devs:
+        Sh, Ss = _nan_like(d["S0"]), _nan_like(d["S0"])
+        outs = step(d, Sh, Ss)
+        torch.cuda.synchronize()
+        eager.append([_np(t) for t in outs] + [_np(Sh), _np(Ss)])
+    Sh, Ss = _nan_like(devs[0]["S0"]), _nan_like(devs[0]["S0"])
+    torch.cuda.synchronize()
+    _say("capture hybrid + commit, serial + serial commit", B, H, T)
+    g = torch.cuda.CUDAGraph()
+    with torch.cuda.graph(g):
+        outs = step(st, Sh, Ss)
+    for r in range(REPLAYS):
+        src = r % 2
+        for n, t in st.items():
+            t.copy_(devs[src][n])
+        for t in (outs[0], outs[1], outs[2], Sh, Ss, snaps_h, snaps_s):
+            t.fill_(float("nan"))
+        _noise(canopy, devs[1 - src])
+        torch.cuda.synchronize()
+        g.replay()
+        torch.cuda.synchronize()
+        _say("replay", r, "input set", src)
+        for name, x, y in zip(names, [_np(t) for t in outs] + [_np(Sh), _np(Ss)], eager[src]):
+            _same(name, x, y)
+        if r == 0:
+            ref = run_oracle(sets[0])
+            assert_close_heads("hybrid O", _np(outs[0]), ref["O"], TOL["bf16"])
+            assert_close_heads("serial O", _np(outs[2]), ref["O"], TOL["bf16"])
+            S_ref, _ = oracle_commit(sets[0])
+            assert_close_state("hybrid S_new", _np(Sh), S_ref, TOL["bf16"])
+            assert_close_state("serial S_new", _np(Ss), S_ref, TOL["bf16"])
+            assert all(_np(t).tolist() == [0] * B for t in outs[3:])
+    del g
+
+
+def test_conv_graph(canopy):
+    import torch
+    B, T, C, K = 2, 40, 256, 4
+    rng = np.random.default_rng(5300)
+    sets = []
+    for s in range(2):
+        par = np.stack([synth.make_tree("random", T, rng) for _ in range(B)]).astype(np.int32)
+        path = np.full((B, T), -1, np.int32)
+        plen = np.zeros(B, np.int32)
+        for b in range(B):
+            leaf = int(rng.integers(0, T))
+            chain = []
+            while leaf >= 0:
+                chain.append(leaf)
+                leaf = int(par[b, leaf])
+            chain.reverse()
+            path[b, :len(chain)] = chain
+            plen[b] = len(chain)
+        sets.append({
+            "x": torch.from_numpy(rng.standard_normal((B, T, C)).astype(np.float32)).cuda().to(torch.bfloat16),
+            "state": torch.from_numpy(rng.standard_normal((B, K - 1, C)).astype(np.float32)).cuda().to(torch.bfloat16),
+            "parent": torch.from_numpy(par).cuda(),
+            "path": torch.from_numpy(path).cuda(),
+            "path_len": torch.from_numpy(plen).cuda(),
+        })
+    w = torch.from_numpy((rng.standard_normal((C, K)) * 0.5).astype(np.float32)).cuda()
+    st = {n: t.clone() for n, t in sets[0].items()}
+
+    def step(d, y, new):
+        _, tst = canopy.tree_conv(d["x"], w, d["state"], d["parent"], silu=True, out=y)
+        _, pst = canopy.conv_commit(d["x"], d["state"], d["parent"], d["path"], d["path_len"], out=new)
+        return tst, pst
+
+    eager = []
+    for d in sets:
+        y, new = _nan_like(d["x"]), _nan_like(d["state"])
+        tst, pst = step(d, y, new)
+        torch.cuda.synchronize()
+        eager.append([_np(y.float()), _np(new.float()), _np(tst), _np(pst)])
+    y, new = _nan_like(sets[0]["x"]), _nan_like(sets[0]["state"])
+    torch.cuda.synchronize()
+    _say("capture conv + conv commit", B, T, C, K)
+    g = torch.cuda.CUDAGraph()
+    with torch.cuda.graph(g):
+        tst, pst = step(st, y, new)
+    for r in range(REPLAYS):
+        src = r % 2
+        for n, t in st.items():
+            t.copy_(sets[src][n])
+        y.fill_(float("nan"))
+        new.fill_(float("nan"))
+        canopy.tree_conv(sets[1 - src]["x"], w, sets[1 - src]["state"], sets[1 - src]["parent"])
+        torch.cuda.synchronize()
+        g.replay()
+        torch.cuda.synchronize()
+        _say("replay", r, "input set", src)
+        for name, a, b in zip(("y", "conv state", "tree status", "path status"),
+                              (_np(y.float()), _np(new.float()), _np(tst), _np(pst)), eager[src]):
+            _same(name, a, b)
+        assert _np(tst).tolist() == [0] * B and _np(pst).tolist() == [0] * B
+    del g
+
+
+def test_commit_layers_graph(canopy):
+    import torch
+    L, B, H, T = 3, 2, 4, 24
+    sets = []
+    for s in range(2):
+        base = synth.make_inputs(B, H, T, tree="random", dtype="bf16", seed=5400 + 10 * s)
+        layers = []
+        for l in range(L):
+            x = synth.make_inputs(B, H, T, dtype="bf16", seed=5401 + 10 * s + l, parents=base["parent"])
+            x["path"], x["path_len"] = base["path"], base["path_len"]
+            layers.append(to_device(x))
+        Us = [canopy.tree_verify(d["q"], d["k"], d["v"], d["alpha"], d["beta"], d["S0"], d["parent"])[1]
+              for d in layers]
+        sets.append((layers, Us))
+    torch.cuda.synchronize()
+    st_layers = [{n: t.clone() for n, t in d.items()} for d in sets[0][0]]
+    st_U = [u.clone() for u in sets[0][1]]
+
+    def step(layers, Us, outs):
+        d0 = layers[0]
+        _, pst = canopy.commit_layers([d["S0"] for d in layers], [d["k"] for d in layers], Us,
+                                      [d["alpha"] for d in layers], d0["parent"], d0["path"],
+                                      d0["path_len"], outs=outs)
+        return pst
+
+    eager = []
+    for layers, Us in sets:
+        outs = [_nan_like(d["S0"]) for d in layers]
+        pst = step(layers, Us, outs)
+        torch.cuda.synchronize()
+        eager.append([_np(o) for o in outs] + [_np(pst)])
+    outs = [_nan_like(d["S0"]) for d in st_layers]
+    torch.cuda.synchronize()
+    _say("capture commit_layers", L, B, H, T)
+    g = torch.cuda.CUDAGraph()
+    with torch.cuda.graph(g):
+        pst = step(st_layers, st_U, outs)
+    for r in range(REPLAYS):
+        src = r % 2
+        for dst, srcd in zip(st_layers, sets[src][0]):
+            for n, t in dst.items():
+                t.copy_(srcd[n])
+        for dst, u in zip(st_U, sets[src][1]):
+            dst.copy_(u)
+        for o in outs:
+            o.fill_(float("nan"))
+        _noise(canopy, sets[1 - src][0][0])
+        torch.cuda.synchronize()
+        g.replay()
+        torch.cuda.synchronize()
+        _say("replay", r, "input set", src)
+        for l in range(L):
+            _same(f"S_new layer {l}", _np(outs[l]), eager[src][l])
+        _same("path status", _np(pst), eager[src][L])
+    del g
