@@ -170,6 +170,40 @@ canopy_status canopy_commit(const float *S0, const void *k, canopy_dtype in_dtyp
                             hipStream_t stream);
 
 /*
+ * One decode step of a layer: commit the previous tree's accepted path, then verify the new
+ * draft tree from the committed state. The result equals canopy_commit followed by
+ * canopy_tree_verify with S0 = S_new (the commit of "What the commit kernel stores" and the
+ * closed form of "The tree closed form"; the two steps are only ordered, not changed). For a
+ * new tree of at most 16 nodes after a previous tree of at most 64 (AUTO or NEUMANN) both run
+ * in one launch and the committed state goes from registers straight into the projections;
+ * otherwise the two kernels run one after the other on the stream.
+ *   S0, k_prev, U_prev, alpha_prev, parent_prev, tree_len_prev, path, path_len: as S0, k, U,
+ *               alpha, parent, tree_len, path and path_len of canopy_commit, for the previous
+ *               tree of T_prev nodes (k_prev [B,T_prev,H,128] in in_dtype).
+ *   q, k, v, alpha, beta, parent, tree_len, solver, waves: as in canopy_tree_verify, for the
+ *               new tree of T nodes.
+ *   S_new       [B,HV,128,128] fp32, out: the committed state; may be the same memory as S0.
+ *   path_status [B] int32, out, may be NULL: as in canopy_commit. A sequence whose path is
+ *               rejected gets a NaN state, and its verify outputs are NaN as well.
+ *   O, U, ell, anc_mask, depth, tree_status: as in canopy_tree_verify. With T == T_prev, U
+ *               may be the same memory as U_prev (each value column of a head is read and
+ *               written by the same wave, the reads first), so a decode loop of one tree
+ *               size can keep one U buffer.
+ * Errors: the checks of both calls, before anything is enqueued.
+ */
+canopy_status canopy_commit_verify(const float *S0, const void *k_prev, const float *U_prev,
+                                   const float *alpha_prev, const int32_t *parent_prev,
+                                   const int32_t *tree_len_prev, const int32_t *path,
+                                   const int32_t *path_len, int T_prev, const void *q,
+                                   const void *k, const void *v, const float *alpha,
+                                   const float *beta, const int32_t *parent,
+                                   const int32_t *tree_len, int B, int H, int HV, int T,
+                                   canopy_dtype in_dtype, float *S_new, int32_t *path_status,
+                                   float *O, float *U, float *ell, uint32_t *anc_mask,
+                                   int32_t *depth, int32_t *tree_status, canopy_solver solver,
+                                   int waves, hipStream_t stream);
+
+/*
  * Every GDN layer's commit in one launch. After acceptance all L layers commit the same
  * accepted path on the same tree, each with its own state, keys, pseudo-values and gates, so
  * one launch serves them all (a decode step commits every layer at once). Arguments as

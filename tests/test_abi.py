@@ -19,8 +19,9 @@ def declared_functions():
 
 def test_header_declares_the_calls():
     names = declared_functions()
-    for n in ("canopy_tree_verify", "canopy_commit", "canopy_serial_verify", "canopy_tree_prep",
-              "canopy_tree_conv", "canopy_conv_commit", "canopy_status_string", "canopy_version"):
+    for n in ("canopy_tree_verify", "canopy_commit", "canopy_commit_verify", "canopy_serial_verify",
+              "canopy_tree_prep", "canopy_tree_conv", "canopy_conv_commit", "canopy_status_string",
+              "canopy_version"):
         assert n in names
 
 
@@ -52,6 +53,13 @@ def test_host_checks_need_no_gpu():
     # S0, k, dtype, U, alpha, parent, tree_len, path, path_len, B, H, HV, T, S_new, status, stream
     assert g(*([nul, nul, i(0), nul, nul, nul, nul, nul, nul, i(1), i(1), i(1), i(4), nul, nul,
                 nul])) == 1
+    cv = lib.canopy_commit_verify
+    cv.restype = ctypes.c_int
+    # S0, k_prev, U_prev, alpha_prev, parent_prev, tree_len_prev, path, path_len, T_prev; q, k,
+    # v, alpha, beta, parent, tree_len; B, H, HV, T, dtype; S_new, path_status, O, U, ell, mask,
+    # depth, status; solver, waves, stream
+    assert cv(*([nul] * 8 + [i(4)] + [nul] * 7 + [i(1), i(1), i(1), i(4), i(0)] + [nul] * 8 +
+                [i(0), i(0), nul])) == 1
 
 
 def test_product_path_does_not_touch_the_oracle():

@@ -59,6 +59,9 @@ def load():
     lib.canopy_tree_verify.restype = i
     lib.canopy_commit.argtypes = [P, P, i, P, P, P, P, P, P, i, i, i, i, P, P, u64]
     lib.canopy_commit.restype = i
+    lib.canopy_commit_verify.argtypes = [P, P, P, P, P, P, P, P, i, P, P, P, P, P, P, P, i, i, i, i, i,
+                                         P, P, P, P, P, P, P, P, i, i, u64]
+    lib.canopy_commit_verify.restype = i
     lib.canopy_serial_verify.argtypes = [P, P, P, P, P, P, P, P, i, i, i, i, i, P, P, P, P, u64]
     lib.canopy_serial_verify.restype = i
     lib.canopy_serial_commit.argtypes = [P, P, P, P, P, P, i, i, i, P, P, u64]
@@ -205,6 +208,58 @@ def commit(S0, k, U, alpha, parent, path, path_len, out=None, tree_len=None):
                                 _ptr(tl), _ptr(path), _ptr(path_len), B, H, HV, T, _ptr(S_new),
                                 _ptr(status), _stream()))
     return S_new, status
+
+
+def commit_verify(S0, k_prev, U_prev, alpha_prev, parent_prev, path, path_len, q, k, v, alpha, beta,
+                  parent, solver="auto", waves=0, structure=False, S_out=None, out=None,
+                  tree_len_prev=None, tree_len=None):
+    """One decode step: ``commit`` of the previous tree's accepted path (its k_prev, U_prev,
+    alpha_prev, parent_prev, path, path_len) into S0, then ``tree_verify`` of the new tree from
+    the committed state. Returns (S_new, path status, O, U, ell) and, with ``structure=True``,
+    also the ancestor bitmask, depth and tree status. ``S_out`` may be S0 (in place); ``out``
+    may pass preallocated (O, U, ell), whose U may be U_prev when both trees have T rows."""
+    B, T, H, d = q.shape
+    Tp = k_prev.shape[1]
+    dt = _in_dtype(q)
+    H, HV = _heads(q, v)
+    for name, t in (("q", q), ("k", k)):
+        _req(t, name, q.dtype, (B, T, H, d))
+    _req(v, "v", q.dtype, (B, T, HV, d))
+    _req(alpha, "alpha", torch.float32, (B, T, HV))
+    _req(beta, "beta", torch.float32, (B, T, HV))
+    _req(parent, "parent", torch.int32, (B, T))
+    _req(S0, "S0", torch.float32, (B, HV, d, d))
+    _req(k_prev, "k_prev", q.dtype, (B, Tp, H, d))
+    _req(U_prev, "U_prev", torch.float32, (B, Tp, HV, d))
+    _req(alpha_prev, "alpha_prev", torch.float32, (B, Tp, HV))
+    _req(parent_prev, "parent_prev", torch.int32, (B, Tp))
+    _req(path, "path", torch.int32, (B, Tp))
+    _req(path_len, "path_len", torch.int32, (B,))
+    tl = _tree_len(tree_len, B)
+    tlp = _tree_len(tree_len_prev, B)
+    dev = q.device
+    S_new = torch.empty_like(S0) if S_out is None else _req(S_out, "S_out", torch.float32, (B, HV, d, d))
+    pstatus = torch.empty((B,), dtype=torch.int32, device=dev)
+    if out is None:
+        O = torch.empty((B, T, HV, d), dtype=torch.float32, device=dev)
+        U = torch.empty((B, T, HV, d), dtype=torch.float32, device=dev)
+        ell = torch.empty((B, T, HV), dtype=torch.float32, device=dev)
+    else:
+        O, U, ell = out
+    mask = depth = status = None
+    if structure:
+        mask = torch.empty((B, T, (T + 31) // 32), dtype=torch.int32, device=dev)
+        depth = torch.empty((B, T), dtype=torch.int32, device=dev)
+        status = torch.empty((B,), dtype=torch.int32, device=dev)
+    _check(load().canopy_commit_verify(_ptr(S0), _ptr(k_prev), _ptr(U_prev), _ptr(alpha_prev),
+                                       _ptr(parent_prev), _ptr(tlp), _ptr(path), _ptr(path_len), Tp,
+                                       _ptr(q), _ptr(k), _ptr(v), _ptr(alpha), _ptr(beta), _ptr(parent),
+                                       _ptr(tl), B, H, HV, T, dt, _ptr(S_new), _ptr(pstatus), _ptr(O),
+                                       _ptr(U), _ptr(ell), _ptr(mask), _ptr(depth), _ptr(status),
+                                       SOLVERS[solver], int(waves), _stream()))
+    if structure:
+        return S_new, pstatus, O, U, ell, mask, depth, status
+    return S_new, pstatus, O, U, ell
 
 
 def serial_verify(q, k, v, alpha, beta, S0, parent, snapshots=None, tree_len=None):

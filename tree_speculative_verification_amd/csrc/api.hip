@@ -118,6 +118,56 @@ canopy_status canopy_commit(const float *S0, const void *k, canopy_dtype in_dtyp
     return from_hip(launch_commit(a, stream));
 }
 
+canopy_status canopy_commit_verify(const float *S0, const void *k_prev, const float *U_prev,
+                                   const float *alpha_prev, const int32_t *parent_prev,
+                                   const int32_t *tree_len_prev, const int32_t *path,
+                                   const int32_t *path_len, int T_prev, const void *q,
+                                   const void *k, const void *v, const float *alpha,
+                                   const float *beta, const int32_t *parent,
+                                   const int32_t *tree_len, int B, int H, int HV, int T,
+                                   canopy_dtype in_dtype, float *S_new, int32_t *path_status,
+                                   float *O, float *U, float *ell, uint32_t *anc_mask,
+                                   int32_t *depth, int32_t *tree_status, canopy_solver solver,
+                                   int waves, hipStream_t stream) {
+    // The commit's own checks (on the previous tree's sizes), then the verify's, which reads
+    // the committed state.
+    if (!S0 || !k_prev || !U_prev || !alpha_prev || !parent_prev || !path || !path_len || !S_new)
+        return CANOPY_ERR_ARG;
+    if (!sizes_ok(B, HV, T_prev) || !heads_ok(H, HV)) return CANOPY_ERR_ARG;
+    if (!aligned16(S0) || !aligned16(k_prev) || !aligned16(U_prev) || !aligned16(S_new))
+        return CANOPY_ERR_ARG;
+    if (!q || !k || !v || !alpha || !beta || !parent || !O || !U || !ell) return CANOPY_ERR_ARG;
+    if (!sizes_ok(B, HV, T)) return CANOPY_ERR_ARG;
+    if (!aligned16(q) || !aligned16(k) || !aligned16(v)) return CANOPY_ERR_ARG;
+    if (in_dtype != CANOPY_FP32 && in_dtype != CANOPY_BF16) return CANOPY_ERR_UNSUPPORTED;
+    if (solver != CANOPY_SOLVE_AUTO && solver != CANOPY_SOLVE_FWDSUB &&
+        solver != CANOPY_SOLVE_NEUMANN && solver != CANOPY_SOLVE_LEVEL)
+        return CANOPY_ERR_UNSUPPORTED;
+    if (waves != 0 && waves != 1 && waves != 2 && waves != 4 && waves != 8) return CANOPY_ERR_UNSUPPORTED;
+    // A tree of at most 16 nodes after a previous tree of at most 64 (one path position per
+    // lane): one launch, the committed state kept in registers for the verify. Otherwise the
+    // commit kernel, then the verify kernel on the committed state.
+    if (T <= 16 && T_prev <= 64 && (solver == CANOPY_SOLVE_AUTO || solver == CANOPY_SOLVE_NEUMANN)) {
+        VerifyArgs a{};
+        a.q = q; a.k = k; a.v = v;
+        a.alpha = alpha; a.beta = beta; a.S0 = S0; a.parent = parent; a.tree_len = tree_len;
+        a.B = B; a.H = HV; a.HK = H; a.T = T;
+        a.bf16 = in_dtype == CANOPY_BF16;
+        a.solver = solver;
+        a.O = O; a.U = U; a.ell = ell;
+        a.anc_mask = anc_mask; a.depth = depth; a.tree_status = tree_status;
+        const PrevCommitArgs c{k_prev, U_prev, alpha_prev, parent_prev, tree_len_prev, path,
+                               path_len, T_prev, S_new, path_status};
+        return from_hip(launch_commit_verify_small(a, c, waves, stream));
+    }
+    const canopy_status st = canopy_commit(S0, k_prev, in_dtype, U_prev, alpha_prev, parent_prev,
+                                           tree_len_prev, path, path_len, B, H, HV, T_prev, S_new,
+                                           path_status, stream);
+    if (st != CANOPY_OK) return st;
+    return canopy_tree_verify(q, k, v, alpha, beta, S_new, parent, tree_len, B, H, HV, T, in_dtype,
+                              O, U, ell, anc_mask, depth, tree_status, solver, waves, stream);
+}
+
 canopy_status canopy_commit_layers(int L, const float *const *S0, const void *const *k,
                                    canopy_dtype in_dtype, const float *const *U,
                                    const float *const *alpha, const int32_t *parent,

@@ -42,6 +42,18 @@ struct CommitArgs {
     int32_t *path_status;
 };
 
+// The commit that precedes a verify in one call: the previous tree's accepted path applied to
+// VerifyArgs::S0, the result written to S_new and used as the verify's initial state. Arrays
+// of the previous tree have T rows (its own node count); heads as in VerifyArgs.
+struct PrevCommitArgs {
+    const void *k;
+    const float *U, *alpha;
+    const int32_t *parent, *tree_len, *path, *path_len;
+    int T;
+    float *S_new;
+    int32_t *path_status;
+};
+
 struct SerialArgs {
     const void *q, *k, *v;
     const float *alpha, *beta, *S0;
@@ -126,6 +138,8 @@ __device__ __forceinline__ size_t qk_base(int b, int h, int H, int HK, int T) {
 
 hipError_t launch_verify(const VerifyArgs &a, int waves, hipStream_t stream);
 hipError_t launch_verify_small(const VerifyArgs &a, int waves, hipStream_t stream);
+hipError_t launch_commit_verify_small(const VerifyArgs &a, const PrevCommitArgs &c, int waves,
+                                      hipStream_t stream);
 hipError_t launch_verify_mid(const VerifyArgs &a, int col_tiles, hipStream_t stream);
 hipError_t launch_verify_wide(const VerifyArgs &a, int col_tiles, hipStream_t stream);
 hipError_t launch_prep(const PrepArgs &a, hipStream_t stream);

@@ -14,14 +14,42 @@
 // tiles (R, the series terms, U) with rows 4g..4g+3 of column r in lane (g, r): exactly the A
 // and B placements of a 16-long MFMA reduction, so the series and the read-out move no data
 // between lanes. A workgroup holds NWV waves, each on its own 16 value columns of one head.
+//
+// The fused variant first commits the previous tree's accepted path into the wave's 128 x 16
+// slice of the state ("Design decisions / What the commit kernel stores"): S = P_a S0 +
+// sum_t w_t k_t u_t^T as fp32 MFMA products over path positions, four per instruction, the key
+// rows permuted so that the result lands in the B-operand placement of S0 that the
+// projections read. The slice is written out as the new state and the verify runs from it
+// without another pass over memory.
 #include "canopy_device.hpp"
 #include "canopy_kernels.hpp"
 #include <limits.h>
 
 namespace canopy {
 
-template <bool BF, int NWV>
-__global__ __launch_bounds__(64 * NWV) void verify_small_kernel(VerifyArgs a) {
+// Fused commit: one path position's operands for the rank-update product. Lane (g, r) takes
+// the node of its position (g within the group of four) and loads the key values at the rows
+// R(t, r) = 32 (t / 2) + 8 (r / 4) + 4 (t % 2) + r % 4 of the 8 output tiles t, and U at column
+// col0 + r. With A[r][g] = k[R(t, r)] the product's lane (g, r) receives rows R(t, 4g + e),
+// i.e. rows 32 ks + 8 g + e' of the S0 fragment (ks = t / 2, e' = 4 (t % 2) + e).
+template <bool BF>
+__device__ __forceinline__ void prev_operands(const PrevCommitArgs &c, size_t kbase, size_t krs,
+                                              size_t ubase, size_t urs, int node, int lr,
+                                              float (&ka)[8], float &u) {
+    const size_t ko = kbase + static_cast<size_t>(node) * krs + 8 * (lr >> 2) + (lr & 3);
+#pragma unroll
+    for (int t = 0; t < 8; ++t) {
+        const size_t o = ko + 32 * (t >> 1) + 4 * (t & 1);
+        if constexpr (BF)
+            ka[t] = bf16_to_f32(static_cast<const uint16_t *>(c.k)[o]);
+        else
+            ka[t] = static_cast<const float *>(c.k)[o];
+    }
+    u = c.U[ubase + static_cast<size_t>(node) * urs];
+}
+
+template <bool BF, int NWV, bool FUSE>
+__global__ __launch_bounds__(64 * NWV) void verify_small_kernel(VerifyArgs a, PrevCommitArgs c) {
     using Op = Ops<BF>;
     using In = typename Op::In;
     using Sp = typename Op::Sp;
@@ -42,6 +70,13 @@ __global__ __launch_bounds__(64 * NWV) void verify_small_kernel(VerifyArgs a) {
     const bool writer = tile == 0;  // this head's wave for the per-node outputs
     const SeqLen sl = seq_len(a.tree_len, b, T);
     const int Tb = sl.n;  // this sequence's node count
+
+    // ---- fused commit, first request: the accepted path (lane = path position)
+    int pm = 0, pnd = -1;
+    if constexpr (FUSE) {
+        pm = c.path_len[b];
+        pnd = c.path[static_cast<size_t>(b) * c.T + min(lane, c.T - 1)];
+    }
 
     // ---- every load up front, unconditional (rows and nodes past T read row or node T-1;
     // rows and nodes past Tb are padding, dropped by selects later), so that they all issue
@@ -72,6 +107,26 @@ __global__ __launch_bounds__(64 * NWV) void verify_small_kernel(VerifyArgs a) {
 #pragma unroll
     for (int e = 0; e < 4; ++e)
         vraw[e] = Op::load_raw(a.v, base + static_cast<size_t>(min(4 * lg + e, T - 1)) * rs + col0 + lr);
+
+    // ---- fused commit, second request: the path nodes' parents and gates, and the operands
+    // of path positions 0..3 (all that a short accepted path has). Positions past the path take
+    // node 0 (a real node of any previous tree), whose finite values meet a zero weight.
+    int pndc = 0, ppar = -1, pmv = 0;
+    bool plenok = false;
+    SeqLen psl{1, false};
+    float pal = 1.f, ka0[8], ub0 = 0.f;
+    const size_t pkbase = FUSE ? qk_base(b, h, H, a.HK, c.T) : 0;
+    const size_t pubase = (static_cast<size_t>(b) * (FUSE ? c.T : 0) * H + h) * D + col0 + lr;
+    if constexpr (FUSE) {
+        psl = seq_len(c.tree_len, b, c.T);
+        plenok = !psl.bad && pm >= 0 && pm <= psl.n;
+        pmv = plenok ? pm : 0;
+        pndc = min(max(pnd, 0), c.T - 1);
+        ppar = c.parent[static_cast<size_t>(b) * c.T + pndc];
+        pal = c.alpha[(static_cast<size_t>(b) * c.T + pndc) * H + h];
+        const int sn = __shfl(pndc, lg, 64);
+        prev_operands<BF>(c, pkbase, qkrs, pubase, rs, lg < pmv ? sn : 0, lr, ka0, ub0);
+    }
 
     // ---- prep: validation, then pointer jumping across lanes. A malformed tree is computed
     // through like a forest (bad parents read as -1) and replaced by NaN at the stores, so that
@@ -111,6 +166,66 @@ __global__ __launch_bounds__(64 * NWV) void verify_small_kernel(VerifyArgs a) {
         if (a.tree_status && lane == 0) a.tree_status[b] = bad;
         if (real && a.depth) a.depth[static_cast<size_t>(b) * T + node] = bad ? 0 : depth;
         if (real && a.anc_mask) a.anc_mask[static_cast<size_t>(b) * T + node] = bad ? 0u : mask;
+    }
+
+    // ---- fused commit: path check (each node a child of the one before, inside the previous
+    // tree), suffix sums of log2 alpha in fp64, w_t = 2^(suffix after t), P_a = 2^(total), the
+    // rank update on MFMA, then the new state in place of the S0 fragment
+    if constexpr (FUSE) {
+        const bool inp = lane < pmv;
+        const int up = __shfl_up(pnd, 1, 64);
+        const int prevn = lane == 0 ? -1 : up;
+        const bool ok = !inp || (pnd >= 0 && pnd < psl.n && ppar == prevn);
+        const unsigned long long pbad = __ballot(!ok);
+        // -1 for a length out of range, else 1 + the first bad position
+        const int pst = !plenok ? -1 : (pbad ? __ffsll(static_cast<unsigned long long>(pbad)) : 0);
+        const double la = inp ? static_cast<double>(__builtin_amdgcn_logf(pal)) : 0.0;
+        double sv = la;  // lanes at or past the path hold 0
+        if (pmv <= 4) {
+#pragma unroll
+            for (int off = 1; off < 4; off <<= 1) {
+                const double tv = __shfl_down(sv, off, 64);
+                sv = lane + off < 64 ? sv + tv : sv;
+            }
+        } else {
+#pragma unroll
+            for (int off = 1; off < 64; off <<= 1) {
+                const double tv = __shfl_down(sv, off, 64);
+                sv = lane + off < 64 ? sv + tv : sv;
+            }
+        }
+        const float Pa = __builtin_amdgcn_exp2f(static_cast<float>(__shfl(sv, 0, 64)));
+        const float w = __builtin_amdgcn_exp2f(static_cast<float>(sv - la));  // decay after t
+        f32x4 dS[8];
+#pragma unroll
+        for (int t = 0; t < 8; ++t) dS[t] = f32x4{0.f, 0.f, 0.f, 0.f};
+        {
+            const float wv = __shfl(w, lg, 64);
+            const float bu = lg < pmv ? wv * ub0 : 0.f;
+#pragma unroll
+            for (int t = 0; t < 8; ++t) dS[t] = mfma_f32(ka0[t], bu, dS[t]);
+        }
+        for (int p0 = 4; p0 < pmv; p0 += 4) {  // paths longer than 4 nodes
+            const int pos = min(p0 + lg, 63);
+            const int sn = __shfl(pndc, pos, 64);
+            float ka[8], uu;
+            prev_operands<BF>(c, pkbase, qkrs, pubase, rs, p0 + lg < pmv ? sn : 0, lr, ka, uu);
+            const float wv = __shfl(w, pos, 64);
+            const float bu = p0 + lg < pmv ? wv * uu : 0.f;
+#pragma unroll
+            for (int t = 0; t < 8; ++t) dS[t] = mfma_f32(ka[t], bu, dS[t]);
+        }
+        const float qnan = __builtin_nanf("");
+        float *Sn = c.S_new + static_cast<size_t>(bh) * D * D + col0 + lr;
+#pragma unroll
+        for (int ks = 0; ks < 4; ++ks)
+#pragma unroll
+            for (int e = 0; e < 8; ++e) {
+                const float x = pst != 0 ? qnan : Pa * s0v[ks][e] + dS[2 * ks + (e >> 2)][e & 3];
+                s0v[ks][e] = x;
+                store_nt(Sn + static_cast<size_t>(32 * ks + 8 * lg + e) * D, x);
+            }
+        if (c.path_status && tile == 0 && h == 0 && lane == 0) c.path_status[b] = pst;
     }
 
     // ---- a2: projections; result order: lane (lg, lr) holds rows 4lg+e of column lr
@@ -191,21 +306,21 @@ __global__ __launch_bounds__(64 * NWV) void verify_small_kernel(VerifyArgs a) {
     }
 }
 
-template <bool BF>
-static void launch_small_nwv(const VerifyArgs &a, int nwv, hipStream_t stream) {
+template <bool BF, bool FUSE>
+static void launch_small_nwv(const VerifyArgs &a, const PrevCommitArgs &c, int nwv, hipStream_t stream) {
     const unsigned heads = static_cast<unsigned>(a.B * a.H);
     switch (nwv) {
         case 1:
-            hipLaunchKernelGGL((verify_small_kernel<BF, 1>), dim3(heads * 8), dim3(64), 0, stream, a);
+            hipLaunchKernelGGL((verify_small_kernel<BF, 1, FUSE>), dim3(heads * 8), dim3(64), 0, stream, a, c);
             break;
         case 2:
-            hipLaunchKernelGGL((verify_small_kernel<BF, 2>), dim3(heads * 4), dim3(128), 0, stream, a);
+            hipLaunchKernelGGL((verify_small_kernel<BF, 2, FUSE>), dim3(heads * 4), dim3(128), 0, stream, a, c);
             break;
         case 4:
-            hipLaunchKernelGGL((verify_small_kernel<BF, 4>), dim3(heads * 2), dim3(256), 0, stream, a);
+            hipLaunchKernelGGL((verify_small_kernel<BF, 4, FUSE>), dim3(heads * 2), dim3(256), 0, stream, a, c);
             break;
         default:
-            hipLaunchKernelGGL((verify_small_kernel<BF, 8>), dim3(heads), dim3(512), 0, stream, a);
+            hipLaunchKernelGGL((verify_small_kernel<BF, 8, FUSE>), dim3(heads), dim3(512), 0, stream, a, c);
             break;
     }
 }
@@ -213,10 +328,23 @@ static void launch_small_nwv(const VerifyArgs &a, int nwv, hipStream_t stream) {
 // waves: waves per workgroup (1, 2, 4 or 8; 0 picks the default).
 hipError_t launch_verify_small(const VerifyArgs &a, int waves, hipStream_t stream) {
     const int nwv = waves == 0 ? 1 : waves;
+    const PrevCommitArgs none{};
     if (a.bf16)
-        launch_small_nwv<true>(a, nwv, stream);
+        launch_small_nwv<true, false>(a, none, nwv, stream);
     else
-        launch_small_nwv<false>(a, nwv, stream);
+        launch_small_nwv<false, false>(a, none, nwv, stream);
+    return hipGetLastError();
+}
+
+// The commit of the previous tree's path (c.T <= 64: one path position per lane) fused in front
+// of the verify of a tree of at most 16 nodes; a.S0 is the state before the commit.
+hipError_t launch_commit_verify_small(const VerifyArgs &a, const PrevCommitArgs &c, int waves,
+                                      hipStream_t stream) {
+    const int nwv = waves == 0 ? 1 : waves;
+    if (a.bf16)
+        launch_small_nwv<true, true>(a, c, nwv, stream);
+    else
+        launch_small_nwv<false, true>(a, c, nwv, stream);
     return hipGetLastError();
 }
 
