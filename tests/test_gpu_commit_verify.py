@@ -126,12 +126,14 @@ def test_topk16_step(canopy):
     assert np.array_equal(r["ell"], s["ell"])
 
 
-@pytest.mark.parametrize("plen", [0, 1, 3, 4, 5, 9, 16, 40, 64])
-def test_path_lengths(canopy, plen):
-    """A chain of 64 nodes before a random 16-node tree, paths of every length class: none, one
-    operand group, a partial and a full group, and up to all 64 positions (one per lane)."""
+@pytest.mark.parametrize("Tp,plen", [(64, 0), (64, 1), (64, 3), (64, 4), (64, 5), (64, 9), (64, 16),
+                                     (64, 40), (64, 64), (16, 0), (16, 1), (16, 5), (16, 16), (9, 9)])
+def test_path_lengths(canopy, Tp, plen):
+    """A chain before a random 16-node tree, paths of every length class: none, one operand
+    group, a partial and a full group, up to every position. Previous trees of up to 64 nodes
+    read the path's nodes after the path; those of up to 16 read every node up front."""
     B, H = 2, 4
-    prev, new = _pair(B, H, 64, 16, "bf16", 6100 + plen, tree_prev="chain")
+    prev, new = _pair(B, H, Tp, 16, "bf16", 6100 + plen + Tp, tree_prev="chain")
     prev["path"][:] = -1
     prev["path"][:, :plen] = np.arange(plen)
     prev["path_len"][:] = plen
@@ -142,12 +144,13 @@ def test_path_lengths(canopy, plen):
         assert np.array_equal(r["S"], prev["S0"].astype(np.float32)), "an empty path must keep S0"
 
 
-@pytest.mark.parametrize("dtype", ["bf16", "fp32"])
-def test_grouped_ragged(canopy, dtype):
-    """Grouped heads (2 q/k heads, 4 value heads) and ragged batches on both trees."""
-    lens_prev, lens = [40, 9, 1], [16, 5, 1]
-    prev, new = _pair(3, 4, 40, 16, dtype, 6200, HK=2, lens_prev=lens_prev, lens=lens)
-    _say("grouped ragged", dtype)
+@pytest.mark.parametrize("dtype,Tp", [("bf16", 40), ("fp32", 40), ("bf16", 16), ("fp32", 13)])
+def test_grouped_ragged(canopy, dtype, Tp):
+    """Grouped heads (2 q/k heads, 4 value heads) and ragged batches on both trees (padding
+    rows of the previous tree full of NaN, its U past each length unwritten)."""
+    lens_prev, lens = [Tp, 9, 1], [16, 5, 1]
+    prev, new = _pair(3, 4, Tp, 16, dtype, 6200 + Tp, HK=2, lens_prev=lens_prev, lens=lens)
+    _say("grouped ragged", dtype, Tp)
     r = _run(canopy, prev, new, lens_prev=lens_prev, lens=lens)
     _check(r, prev, new, dtype, lens_prev, lens)
 
@@ -165,15 +168,16 @@ def test_binary7_fp32(canopy):
             _check(r, prev, new, "fp32")
 
 
-def test_rejected_paths(canopy):
+@pytest.mark.parametrize("Tp", [30, 12])
+def test_rejected_paths(canopy, Tp):
     """A path that leaves the tree, a path_len past the tree and a bad tree_len: status as in
     the commit, NaN state and NaN outputs for those sequences only."""
     B, H = 4, 4
-    lens_prev = [30, 30, 30, 0]
-    prev, new = _pair(B, H, 30, 12, "bf16", 6400, lens_prev=[30, 30, 30, 30])
+    lens_prev = [Tp, Tp, Tp, 0]
+    prev, new = _pair(B, H, Tp, 12, "bf16", 6400 + Tp, lens_prev=[Tp, Tp, Tp, Tp])
     prev["path"][1, 1] = prev["path"][1, 0]  # position 1 is not a child of position 0
     prev["path_len"][1] = max(prev["path_len"][1], 2)
-    prev["path_len"][2] = 31  # longer than the tree
+    prev["path_len"][2] = Tp + 1  # longer than the tree
     _say("rejected paths")
     r = _run(canopy, prev, new, lens_prev=lens_prev)
     S_ref, pst_ref, _ = _oracle(prev, new, lens_prev)

@@ -17,33 +17,39 @@
 //
 // The fused variant first commits the previous tree's accepted path into the wave's 128 x 16
 // slice of the state ("Design decisions / What the commit kernel stores"): S = P_a S0 +
-// sum_t w_t k_t u_t^T as fp32 MFMA products over path positions, four per instruction, the key
+// sum_t w_t k_t u_t^T as fp32 MFMA products, four path positions per instruction, the key
 // rows permuted so that the result lands in the B-operand placement of S0 that the
-// projections read. The slice is written out as the new state and the verify runs from it
-// without another pass over memory.
+// projections read. The path is requested first, then its nodes' operands; the slice is
+// written out as the new state and the verify runs from it without another pass over memory.
 #include "canopy_device.hpp"
 #include "canopy_kernels.hpp"
 #include <limits.h>
 
 namespace canopy {
 
-// Fused commit: one path position's operands for the rank-update product. Lane (g, r) takes
-// the node of its position (g within the group of four) and loads the key values at the rows
-// R(t, r) = 32 (t / 2) + 8 (r / 4) + 4 (t % 2) + r % 4 of the 8 output tiles t, and U at column
-// col0 + r. With A[r][g] = k[R(t, r)] the product's lane (g, r) receives rows R(t, 4g + e),
-// i.e. rows 32 ks + 8 g + e' of the S0 fragment (ks = t / 2, e' = 4 (t % 2) + e).
+// Fused commit: one node's operands for the rank-update product. Lane (g, r) holds the node of
+// its reduction index g and loads the key values at the rows R(t, r) = 32 (r % 4) + 8 (r / 4) + t
+// of the 8 output tiles t (8 adjacent rows: one 16-byte load for bf16), and U at column col0 + r.
+// With A[r][g] = k[R(t, r)], the product's lane (g, r) receives rows R(t, 4g + e) = 32 e + 8 g + t:
+// value t of the S0 fragment's slice ks = e.
 template <bool BF>
 __device__ __forceinline__ void prev_operands(const PrevCommitArgs &c, size_t kbase, size_t krs,
                                               size_t ubase, size_t urs, int node, int lr,
                                               float (&ka)[8], float &u) {
-    const size_t ko = kbase + static_cast<size_t>(node) * krs + 8 * (lr >> 2) + (lr & 3);
+    const size_t ko = kbase + static_cast<size_t>(node) * krs + 32 * (lr & 3) + 8 * (lr >> 2);
+    if constexpr (BF) {
+        const uint4 w = *reinterpret_cast<const uint4 *>(static_cast<const uint16_t *>(c.k) + ko);
+        const uint32_t ww[4] = {w.x, w.y, w.z, w.w};
 #pragma unroll
-    for (int t = 0; t < 8; ++t) {
-        const size_t o = ko + 32 * (t >> 1) + 4 * (t & 1);
-        if constexpr (BF)
-            ka[t] = bf16_to_f32(static_cast<const uint16_t *>(c.k)[o]);
-        else
-            ka[t] = static_cast<const float *>(c.k)[o];
+        for (int q = 0; q < 4; ++q) {
+            ka[2 * q] = __uint_as_float(ww[q] << 16);
+            ka[2 * q + 1] = __uint_as_float(ww[q] & 0xFFFF0000u);
+        }
+    } else {
+        const float4 f0 = *reinterpret_cast<const float4 *>(static_cast<const float *>(c.k) + ko);
+        const float4 f1 = *reinterpret_cast<const float4 *>(static_cast<const float *>(c.k) + ko + 4);
+        ka[0] = f0.x; ka[1] = f0.y; ka[2] = f0.z; ka[3] = f0.w;
+        ka[4] = f1.x; ka[5] = f1.y; ka[6] = f1.z; ka[7] = f1.w;
     }
     u = c.U[ubase + static_cast<size_t>(node) * urs];
 }
@@ -108,24 +114,24 @@ __global__ __launch_bounds__(64 * NWV) void verify_small_kernel(VerifyArgs a, Pr
     for (int e = 0; e < 4; ++e)
         vraw[e] = Op::load_raw(a.v, base + static_cast<size_t>(min(4 * lg + e, T - 1)) * rs + col0 + lr);
 
-    // ---- fused commit, second request: the path nodes' parents and gates, and the operands
-    // of path positions 0..3 (all that a short accepted path has). Positions past the path take
-    // node 0 (a real node of any previous tree), whose finite values meet a zero weight.
-    int pndc = 0, ppar = -1, pmv = 0;
-    bool plenok = false;
+    // ---- fused commit, second request: the path nodes' parents and gates (lane = position)
+    // and the operands of positions 0..3 (all that a short accepted path has). Positions past
+    // the path take node 0 (a real node of any previous tree), whose finite values meet a zero
+    // weight.
+    int ppar = -1, pmv = 0;
     SeqLen psl{1, false};
-    float pal = 1.f, ka0[8], ub0 = 0.f;
+    float pal = 1.f, ka[8], ub = 0.f;
     const size_t pkbase = FUSE ? qk_base(b, h, H, a.HK, c.T) : 0;
     const size_t pubase = (static_cast<size_t>(b) * (FUSE ? c.T : 0) * H + h) * D + col0 + lr;
     if constexpr (FUSE) {
         psl = seq_len(c.tree_len, b, c.T);
-        plenok = !psl.bad && pm >= 0 && pm <= psl.n;
+        const bool plenok = !psl.bad && pm >= 0 && pm <= psl.n;
         pmv = plenok ? pm : 0;
-        pndc = min(max(pnd, 0), c.T - 1);
-        ppar = c.parent[static_cast<size_t>(b) * c.T + pndc];
-        pal = c.alpha[(static_cast<size_t>(b) * c.T + pndc) * H + h];
-        const int sn = __shfl(pndc, lg, 64);
-        prev_operands<BF>(c, pkbase, qkrs, pubase, rs, lg < pmv ? sn : 0, lr, ka0, ub0);
+        const int nsel = min(max(pnd, 0), c.T - 1);
+        ppar = c.parent[static_cast<size_t>(b) * c.T + nsel];
+        pal = c.alpha[(static_cast<size_t>(b) * c.T + nsel) * H + h];
+        const int sn = __shfl(nsel, lg, 64);
+        prev_operands<BF>(c, pkbase, qkrs, pubase, rs, lg < pmv ? sn : 0, lr, ka, ub);
     }
 
     // ---- prep: validation, then pointer jumping across lanes. A malformed tree is computed
@@ -173,10 +179,12 @@ __global__ __launch_bounds__(64 * NWV) void verify_small_kernel(VerifyArgs a, Pr
     // rank update on MFMA, then the new state in place of the S0 fragment
     if constexpr (FUSE) {
         const bool inp = lane < pmv;
+        const int ndc = min(max(pnd, 0), c.T - 1);
         const int up = __shfl_up(pnd, 1, 64);
         const int prevn = lane == 0 ? -1 : up;
         const bool ok = !inp || (pnd >= 0 && pnd < psl.n && ppar == prevn);
         const unsigned long long pbad = __ballot(!ok);
+        const bool plenok = !psl.bad && pm >= 0 && pm <= psl.n;
         // -1 for a length out of range, else 1 + the first bad position
         const int pst = !plenok ? -1 : (pbad ? __ffsll(static_cast<unsigned long long>(pbad)) : 0);
         const double la = inp ? static_cast<double>(__builtin_amdgcn_logf(pal)) : 0.0;
@@ -201,30 +209,30 @@ __global__ __launch_bounds__(64 * NWV) void verify_small_kernel(VerifyArgs a, Pr
         for (int t = 0; t < 8; ++t) dS[t] = f32x4{0.f, 0.f, 0.f, 0.f};
         {
             const float wv = __shfl(w, lg, 64);
-            const float bu = lg < pmv ? wv * ub0 : 0.f;
-#pragma unroll
-            for (int t = 0; t < 8; ++t) dS[t] = mfma_f32(ka0[t], bu, dS[t]);
-        }
-        for (int p0 = 4; p0 < pmv; p0 += 4) {  // paths longer than 4 nodes
-            const int pos = min(p0 + lg, 63);
-            const int sn = __shfl(pndc, pos, 64);
-            float ka[8], uu;
-            prev_operands<BF>(c, pkbase, qkrs, pubase, rs, p0 + lg < pmv ? sn : 0, lr, ka, uu);
-            const float wv = __shfl(w, pos, 64);
-            const float bu = p0 + lg < pmv ? wv * uu : 0.f;
+            const float bu = lg < pmv ? wv * ub : 0.f;
 #pragma unroll
             for (int t = 0; t < 8; ++t) dS[t] = mfma_f32(ka[t], bu, dS[t]);
         }
+        for (int p0 = 4; p0 < pmv; p0 += 4) {  // paths longer than 4 nodes
+            const int pos = min(p0 + lg, 63);
+            const int sn = __shfl(ndc, pos, 64);
+            float kx[8], ux;
+            prev_operands<BF>(c, pkbase, qkrs, pubase, rs, p0 + lg < pmv ? sn : 0, lr, kx, ux);
+            const float wv = __shfl(w, pos, 64);
+            const float bu = p0 + lg < pmv ? wv * ux : 0.f;
+#pragma unroll
+            for (int t = 0; t < 8; ++t) dS[t] = mfma_f32(kx[t], bu, dS[t]);
+        }
         const float qnan = __builtin_nanf("");
+#pragma unroll
+        for (int ks = 0; ks < 4; ++ks)
+#pragma unroll
+            for (int e = 0; e < 8; ++e) s0v[ks][e] = pst != 0 ? qnan : Pa * s0v[ks][e] + dS[e][ks];
         float *Sn = c.S_new + static_cast<size_t>(bh) * D * D + col0 + lr;
 #pragma unroll
         for (int ks = 0; ks < 4; ++ks)
 #pragma unroll
-            for (int e = 0; e < 8; ++e) {
-                const float x = pst != 0 ? qnan : Pa * s0v[ks][e] + dS[2 * ks + (e >> 2)][e & 3];
-                s0v[ks][e] = x;
-                store_nt(Sn + static_cast<size_t>(32 * ks + 8 * lg + e) * D, x);
-            }
+            for (int e = 0; e < 8; ++e) store_nt(Sn + static_cast<size_t>(32 * ks + 8 * lg + e) * D, s0v[ks][e]);
         if (c.path_status && tile == 0 && h == 0 && lane == 0) c.path_status[b] = pst;
     }
 
