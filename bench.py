@@ -1,14 +1,17 @@
 #!/usr/bin/env python3
 """Benchmark: tree-structured verification of one Gated DeltaNet layer on one MI355X.
 
-A step is one pass of the hot path over one layer's synthetic batch: canopy_tree_verify (tree
-preprocessing, S0 projections, masked Gram matrices, triangular solve, read-out) followed by
-canopy_commit of a random root-to-leaf path. The serial fork baseline is timed beside it.
-Inputs are resident in HBM before the timed region; the timed region holds exactly --steps
-steps between two stream synchronisations, timed with HIP events on the launch stream. The
-steps are captured once into a HIP graph and the timed region is one replay of it (the kernels
-are short enough at B=1 that launching them one by one from Python would time the host);
---eager launches them one by one instead.
+A step is one pass of the hot path over one layer's synthetic batch, as a decode loop runs it:
+canopy_commit_verify commits the previous round's accepted path (a random root-to-leaf path of
+the tree) into the state the loop carries, then verifies the tree from the committed state
+(tree preprocessing, S0 projections, masked Gram matrices, triangular solve, read-out). For
+trees of at most 16 nodes that is one launch; otherwise the commit kernel and the verify kernel.
+The same work as two separate calls (canopy_tree_verify, then canopy_commit) is timed beside
+it, and so is the serial fork baseline. Inputs are resident in HBM before the timed region; the
+timed region holds exactly --steps steps between two stream synchronisations, timed with HIP
+events on the launch stream. The steps are captured once into a HIP graph and the timed region
+is one replay of it (the kernels are short enough at B=1 that launching them one by one from
+Python would time the host); --eager launches them one by one instead.
 
 Prints one JSON line. The default workload is the 9B-shaped layer: B=1, H=32, d=128, T=16
 top-k tree (root, 3 children, 4 children each), bf16 q/k/v, fp32 state.
@@ -82,6 +85,24 @@ def commit_bytes(B, H, m_total):
     return B * H * 2 * 128 * 128 * 4 + m_total * H * (128 * 2 + 128 * 4 + 4) + m_total * 8
 
 
+def fused_step_bytes(B, H, T, dtype, m_total, HK=None, nodes=None):
+    """Algorithmic HBM bytes of the one-launch decode step: the verify's bytes plus the commit's,
+    with S0 read once for both (the committed state goes from registers into the verify)."""
+    return verify_bytes(B, H, T, dtype, HK=HK, nodes=nodes) + commit_bytes(B, H, m_total) - B * H * 128 * 128 * 4
+
+
+def one_launch_step(T, solver):
+    """Whether canopy_commit_verify runs the step as one launch (trees of at most 16 nodes after
+    trees of at most 64, AUTO or NEUMANN)."""
+    return T <= 16 and solver in ("auto", "neumann")
+
+
+def fused_kernel_name(dtype="bf16", waves=0):
+    """The one-launch step's kernel as the profiler names it."""
+    return "canopy::verify_small_kernel<%s, %d, true>" % ("true" if dtype == "bf16" else "false",
+                                                         waves if waves else 1)
+
+
 def verify_flops_ragged(H, lens):
     """verify_flops summed over sequences of their own node counts."""
     return sum(verify_flops(1, H, int(n)) for n in lens)
@@ -120,9 +141,10 @@ def kernel_digest():
     return h.hexdigest()[:16]
 
 
-def measured_traffic(workload, solver, waves):
-    """HBM bytes per verify launch from the committed counter summary, or None if there is
-    none for this configuration or the kernels have changed since it was taken."""
+def measured_traffic(workload, solver, waves, role="verify"):
+    """HBM bytes per launch of the verify, commit or one-launch step ("fused") kernel from the
+    committed counter summary, or None if there is none for this configuration or the kernels
+    have changed since it was taken."""
     try:
         with open(TRAFFIC_FILE) as fh:
             data = json.load(fh)
@@ -131,7 +153,9 @@ def measured_traffic(workload, solver, waves):
     if data.get("kernel_digest") != kernel_digest():
         return None
     ent = data.get("workloads", {}).get(f"{workload}:{solver}:{waves}")
-    return None if ent is None else ent["verify"]["hbm_bytes_per_launch"]
+    if ent is None or role not in ent:
+        return None
+    return ent[role]["hbm_bytes_per_launch"]
 
 
 def pmc_summary(run_dir, out_path):
@@ -167,15 +191,24 @@ def pmc_summary(run_dir, out_path):
         fscale = probe / 1024.0 / max(f["__amd_rocclr_copyBuffer"])
         wscale = probe / 1024.0 / max(w["__amd_rocclr_copyBuffer"])
         ent = {"config": rec["config"], "fetch_scale": round(fscale, 4), "write_scale": round(wscale, 4)}
-        for prefix, role in (("canopy::verify", "verify"), ("canopy::commit_kernel<", "commit")):
-            kf = [k for k in f if k.startswith("void " + prefix)]
+        def is_fused(k):
+            return k.startswith("void canopy::verify_small_kernel<") and ", true>(" in k
+        roles = (("verify", lambda k: k.startswith("void canopy::verify") and not is_fused(k), True),
+                 ("commit", lambda k: k.startswith("void canopy::commit_kernel<"), True),
+                 ("fused", is_fused, False))
+        for role, match, required in roles:
+            kf = [k for k in f if match(k)]
+            if not kf and not required:
+                continue
             if len(kf) != 1:
-                raise RuntimeError(f"{tag}: expected one {prefix} kernel in the counters, found {kf}")
+                raise RuntimeError(f"{tag}: expected one {role} kernel in the counters, found {kf}")
             fk = sum(f[kf[0]]) / len(f[kf[0]])
             wk = sum(w[kf[0]]) / len(w[kf[0]])
             ent[role] = {"kernel": kf[0], "fetch_kib": round(fk, 1), "write_kib": round(wk, 1),
                          "hbm_bytes_per_launch": int(round(fk * 1024 * fscale + wk * 1024 * wscale))}
-        ent["verify"]["algorithmic_bytes"] = rec["roofline"]["algorithmic_bytes"]
+        ent["verify"]["algorithmic_bytes"] = rec["verify_algorithmic_bytes"]
+        if "fused" in ent:
+            ent["fused"]["algorithmic_bytes"] = rec["roofline"]["algorithmic_bytes"]
         key = f"{rec['config']['workload_key']}:{rec['config']['solver']}:{rec['config']['waves']}"
         out["workloads"][key] = ent
     with open(out_path, "w") as fh:
@@ -871,32 +904,76 @@ def main(argv=None):
         tsv.commit(d["S0"], d["k"], U, d["alpha"], d["parent"], d["path"], d["path_len"], out=S_new,
                    tree_len=d["tree_len"])
 
-    def step():
+    def separate_step():
         verify()
         commit()
 
+    # The decode loop's step: commit the previous round's path (its U from the previous step)
+    # into the carried state S_run, then verify the tree from it; U is carried in one buffer.
+    S_run = d["S0"].clone()
+    O_run = torch.empty_like(O)
+    U_run = torch.empty_like(O)
+    ell_run = torch.empty_like(ell)
+
+    def step():
+        tsv.commit_verify(S_run, d["k"], U_run, d["alpha"], d["parent"], d["path"], d["path_len"],
+                          d["q"], d["k"], d["v"], d["alpha"], d["beta"], d["parent"],
+                          solver=args.solver, waves=args.waves, out=(O_run, U_run, ell_run),
+                          S_out=S_run, tree_len_prev=d["tree_len"], tree_len=d["tree_len"])
+
+    for _ in range(args.warmup):
+        separate_step()
+    torch.cuda.synchronize()
+    ref_O, ref_U, ref_S = O.clone(), U.clone(), S_new.clone()
+    tsv.tree_verify(d["q"], d["k"], d["v"], d["alpha"], d["beta"], S_run, d["parent"],
+                    solver=args.solver, waves=args.waves, out=(O_run, U_run, ell_run),
+                    tree_len=d["tree_len"])
     for _ in range(args.warmup):
         step()
     torch.cuda.synchronize()
-    ref_O, ref_U, ref_S = O.clone(), U.clone(), S_new.clone()
     if args.eager:
         us_step = time_eager(step, args.steps, 0)
+        us_sep = time_eager(separate_step, args.steps, 0)
         us_verify = time_eager(verify, args.steps, 5)
         us_commit = time_eager(commit, args.steps, 5)
     else:
-        # Timed region: one replay of a graph holding exactly `steps` steps.
-        g_step = graph_of(step, args.steps)
+        # Timed region: one replay of a graph holding exactly `steps` steps. The loop carries
+        # its state, so the replay is checked against the same steps run eagerly from the same
+        # starting state, bit for bit.
+        start = (S_run.clone(), U_run.clone())
+        for _ in range(args.steps):
+            step()
+        torch.cuda.synchronize()
+        eager_end = (S_run.clone(), U_run.clone(), O_run.clone())
+        g_step = torch.cuda.CUDAGraph()
+        with torch.cuda.graph(g_step):
+            for _ in range(args.steps):
+                step()
+        torch.cuda.synchronize()
+        S_run.copy_(start[0])
+        U_run.copy_(start[1])
+        torch.cuda.synchronize()
+        g_step.replay()
+        torch.cuda.synchronize()
+        if not (torch.equal(S_run, eager_end[0]) and torch.equal(U_run, eager_end[1])
+                and torch.equal(O_run, eager_end[2])):
+            raise RuntimeError("graph replay of the decode steps differs from the eager run")
         us_step = time_graph(g_step, args.steps)
+        del g_step, start, eager_end
+        g_sep = graph_of(separate_step, args.steps)
+        us_sep = time_graph(g_sep, args.steps)
         # The replayed kernels must reproduce the eager results bit for bit.
         if not (torch.equal(O, ref_O) and torch.equal(U, ref_U) and torch.equal(S_new, ref_S)):
             raise RuntimeError("graph replay differs from the eager run")
-        del g_step
+        del g_sep
         g_v = graph_of(verify, args.steps)
         us_verify = time_graph(g_v, args.steps)
         del g_v
         g_c = graph_of(commit, args.steps)
         us_commit = time_graph(g_c, args.steps)
         del g_c
+    if not bool(torch.isfinite(S_run).all()):
+        raise RuntimeError("the carried state is not finite")
     us_serial = us_hybrid = None
     if not args.no_serial:
         snaps = torch.empty((B, T, H, 128, 128), device="cuda")
@@ -934,9 +1011,21 @@ def main(argv=None):
     lens = inp["tree_len"] if inp.get("tree_len") is not None else np.full(B, T)
     nodes = int(lens.sum())
     vbytes = verify_bytes(B, H, T, dt, HK=HK, nodes=nodes)
-    achieved = vbytes / (us_verify * 1e-6) / 1e9
     vflops = verify_flops_ragged(H, lens)
-    tflops = vflops / (us_verify * 1e-6) / 1e12
+    one = one_launch_step(T, args.solver)
+    if one:
+        # the dominant (only) kernel of the step: commit + verify in one launch per step
+        m_total = int(inp["path_len"].sum())
+        rbytes = fused_step_bytes(B, H, T, dt, m_total, HK=HK, nodes=nodes)
+        rflops = vflops + H * 2 * 128 * 128 * m_total
+        r_us, r_kernel, r_role = us_step, fused_kernel_name(dt, args.waves), "fused"
+        r_note = "one launch per step (commit + verify): algorithmic bytes and flops of both"
+    else:
+        rbytes, rflops, r_us, r_role = vbytes, vflops, us_verify, "verify"
+        r_kernel = verify_kernel_name(T, args.solver, B * H, args.waves, dt)
+        r_note = "algorithmic dense-triangle flops of the verify launch"
+    achieved = rbytes / (r_us * 1e-6) / 1e9
+    tflops = rflops / (r_us * 1e-6) / 1e12
     out = {
         "metric": METRIC,
         "value": round(us_step, 3),
@@ -953,23 +1042,28 @@ def main(argv=None):
         "config": {"workload": wl["desc"], "workload_key": args.workload, "B": B, "H": H, "T": T,
                    "q_k_heads": HK, "nodes": nodes, "dk": 128, "dv": 128, "tree": wl["tree"],
                    "solver": args.solver,
-                   "waves": args.waves, "step": "verify + commit of a random root-to-leaf path",
+                   "waves": args.waves,
+                   "step": ("commit of the previous round's accepted path (a random root-to-leaf "
+                            "path) into the carried state, then verify of the tree from it "
+                            "(canopy_commit_verify, %s)" % ("one launch" if one else "two launches")),
                    "launch": "eager" if args.eager else "hip graph of all timed steps",
                    "copy_probe_bytes": args.copy_probe},
         "nodes_per_s": round(nodes / (us_step * 1e-6), 1),
+        "separate_step_us": round(us_sep, 3),
         "verify_us": round(us_verify, 3),
         "verify_nodes_per_s": round(nodes / (us_verify * 1e-6), 1),
         "commit_us": round(us_commit, 3),
         "serial_verify_us": None if us_serial is None else round(us_serial, 3),
         "hybrid_verify_us": None if us_hybrid is None else round(us_hybrid, 3),
-        "roofline": {"bound": "hbm", "kernel": verify_kernel_name(T, args.solver, B * H, args.waves, dt),
+        "roofline": {"bound": "hbm", "kernel": r_kernel,
                      "achieved": round(achieved, 2), "peak": HBM_PEAK_GBS, "unit": "GB/s",
                      "frac": round(achieved / HBM_PEAK_GBS, 5),
-                     "traffic": measured_traffic(args.workload, args.solver, args.waves),
-                     "algorithmic_bytes": vbytes},
-        "mfma": {"flops_per_launch": vflops, "achieved_tflops": round(tflops, 2),
+                     "traffic": measured_traffic(args.workload, args.solver, args.waves, r_role),
+                     "algorithmic_bytes": rbytes, "launch_us": round(r_us, 3)},
+        "verify_algorithmic_bytes": vbytes,
+        "mfma": {"flops_per_launch": rflops, "achieved_tflops": round(tflops, 2),
                  "peak_tflops": BF16_PEAK_TFLOPS, "frac": round(tflops / BF16_PEAK_TFLOPS, 5),
-                 "note": "algorithmic dense-triangle flops of the verify launch"},
+                 "note": r_note},
         "kernel_digest": kernel_digest(),
     }
     if not args.no_cpu:

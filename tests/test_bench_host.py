@@ -44,6 +44,24 @@ def test_commit_bytes_c2():
     assert bench.commit_bytes(1, 32, 3) == 4_268_440
 
 
+def test_fused_step_bytes_c2():
+    # One-launch step at C2 with a 3-node path: the verify's 3.02 MB and the commit's 4.27 MB
+    # with S0 (2.10 MB) read once for both
+    assert bench.fused_step_bytes(1, 32, 16, "bf16", 3) == 3_020_864 + 4_268_440 - 2_097_152
+    assert bench.fused_step_bytes(1, 32, 16, "bf16", 3) == 5_192_152
+
+
+@pytest.mark.parametrize("T,solver,one", [(16, "auto", True), (7, "neumann", True), (16, "fwdsub", False),
+                                          (16, "level", False), (17, "auto", False), (256, "auto", False)])
+def test_one_launch_step_follows_the_dispatch(T, solver, one):
+    assert bench.one_launch_step(T, solver) == one
+
+
+def test_fused_kernel_name():
+    assert bench.fused_kernel_name("bf16", 0) == "canopy::verify_small_kernel<true, 1, true>"
+    assert bench.fused_kernel_name("fp32", 8) == "canopy::verify_small_kernel<false, 8, true>"
+
+
 def test_verify_flops_dense_tile():
     assert bench.verify_flops(1, 32, 16) == 37_748_736            # C2: 37.7 MFLOP
     assert bench.verify_flops(16, 32, 256) == 25_769_803_776      # C4: 25.8 GFLOP
@@ -74,6 +92,7 @@ def test_traffic_gated_by_digest(tmp_path, monkeypatch):
     monkeypatch.setattr(bench, "TRAFFIC_FILE", str(path))
     assert bench.measured_traffic("topk16_b1", "auto", 0) == 123
     assert bench.measured_traffic("topk16_b1", "auto", 8) is None
+    assert bench.measured_traffic("topk16_b1", "auto", 0, "fused") is None
     path.write_text(json.dumps({"kernel_digest": "0" * 16, "workloads": {"topk16_b1:auto:0": entry}}))
     assert bench.measured_traffic("topk16_b1", "auto", 0) is None
 
