@@ -5,9 +5,10 @@ by its per-path verify, and against the two separate calls.
 Tolerances as for the separate calls: max per-(batch, head) relative error 2e-3 for bf16 q/k/v
 (1e-5 for fp32) for O, U and the committed state against the oracle; mask, depth and both
 statuses bit-exact. Covered: the one-launch form (new trees of at most 16 nodes after previous
-trees of at most 64) at the 1+3+12 top-k shape, paths of 0, 1..4 and more than 4 positions,
-grouped heads and ragged batches, fp32 inputs, rejected paths, the state committed in place and
-one U buffer for both trees; and the two-launch form for larger trees."""
+trees of at most 64) at the 1+3+12 top-k shape and for 17-64-node trees with narrow
+workgroups, paths of 0, 1..4 and more than 4 positions, grouped heads and ragged batches, fp32
+inputs, rejected paths, the state committed in place and one U buffer for both trees; and the
+two-launch form for the other shapes."""
 from __future__ import annotations
 
 import numpy as np
@@ -197,10 +198,48 @@ def test_in_place_and_shared_U(canopy):
         assert np.array_equal(a[name], b[name], equal_nan=True), name
 
 
-@pytest.mark.parametrize("Tp,T", [(100, 16), (16, 40), (64, 130)])
-def test_two_launch_form(canopy, Tp, T):
-    """Shapes outside the one-launch form: the commit kernel, then the verify kernel."""
-    prev, new = _pair(2, 4, Tp, T, "bf16", 6600 + Tp + T)
-    _say("two launches", Tp, T)
+@pytest.mark.parametrize("B,H,Tp,T", [(2, 4, 100, 16), (2, 4, 64, 130), (3, 16, 16, 40), (2, 48, 30, 64),
+                                     (2, 4, 100, 40)])
+def test_two_launch_form(canopy, B, H, Tp, T):
+    """Shapes outside the one-launch forms (a previous tree past 64 nodes, a new tree past 64,
+    17-64-node trees with wide workgroups): the commit kernel, then the verify kernel."""
+    prev, new = _pair(B, H, Tp, T, "bf16", 6600 + Tp + T + H)
+    _say("two launches", B, H, Tp, T)
     r = _run(canopy, prev, new)
     _check(r, prev, new, "bf16")
+
+
+@pytest.mark.parametrize("T,Tp,plen,dtype", [(17, 16, 3, "bf16"), (40, 16, 16, "bf16"), (64, 64, 0, "bf16"),
+                                             (64, 64, 7, "bf16"), (33, 64, 64, "bf16"), (48, 40, 13, "fp32"),
+                                             (64, 12, 5, "fp32")])
+def test_mid_one_launch(canopy, T, Tp, plen, dtype):
+    """The one-launch form for new trees of 17 to 64 nodes (narrow workgroups, B * H <= 32):
+    chains before random trees, paths of every length class."""
+    B, H = 2, 4
+    prev, new = _pair(B, H, Tp, T, dtype, 6700 + T + Tp + plen, tree_prev="chain")
+    prev["path"][:] = -1
+    prev["path"][:, :plen] = np.arange(plen)
+    prev["path_len"][:] = plen
+    _say("17-64 one launch", T, Tp, plen, dtype)
+    r = _run(canopy, prev, new)
+    _check(r, prev, new, dtype)
+    if plen == 0:
+        assert np.array_equal(r["S"], prev["S0"].astype(np.float32)), "an empty path must keep S0"
+    s = _separate(canopy, r)
+    for name in ("S", "O", "U"):
+        err = np.max(np.abs(r[name] - s[name])) / max(1e-30, np.max(np.abs(s[name])))
+        assert err < 1e-5, f"{name}: fused and separate differ by {err:.2e}"
+
+
+@pytest.mark.parametrize("dtype", ["bf16", "fp32"])
+def test_mid_grouped_ragged_rejected(canopy, dtype):
+    """The 17-64 one-launch form with grouped heads, ragged batches on both trees and a rejected
+    path (sequence 1) and a bad length (sequence 2)."""
+    lens_prev, lens = [50, 20, 0], [40, 17, 1]
+    prev, new = _pair(3, 4, 50, 40, dtype, 6800, HK=2, lens_prev=[50, 20, 1], lens=lens)
+    prev["path"][1, 1] = prev["path"][1, 0]
+    prev["path_len"][1] = max(prev["path_len"][1], 2)
+    _say("17-64 grouped ragged rejected", dtype)
+    r = _run(canopy, prev, new, lens_prev=lens_prev, lens=lens)
+    assert r["pst"][0] == 0 and r["pst"][1] == 2 and r["pst"][2] == -1
+    _check(r, prev, new, dtype, lens_prev, lens)

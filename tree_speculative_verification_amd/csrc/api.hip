@@ -144,10 +144,14 @@ canopy_status canopy_commit_verify(const float *S0, const void *k_prev, const fl
         solver != CANOPY_SOLVE_NEUMANN && solver != CANOPY_SOLVE_LEVEL)
         return CANOPY_ERR_UNSUPPORTED;
     if (waves != 0 && waves != 1 && waves != 2 && waves != 4 && waves != 8) return CANOPY_ERR_UNSUPPORTED;
-    // A tree of at most 16 nodes after a previous tree of at most 64 (one path position per
-    // lane): one launch, the committed state kept in registers for the verify. Otherwise the
-    // commit kernel, then the verify kernel on the committed state.
-    if (T <= 16 && T_prev <= 64 && (solver == CANOPY_SOLVE_AUTO || solver == CANOPY_SOLVE_NEUMANN)) {
+    // After a previous tree of at most 64 nodes (one path position per lane): one launch, the
+    // committed state kept in registers for the verify, for new trees of at most 16 nodes (AUTO,
+    // NEUMANN) and for 17 to 64 nodes where the 17-64 kernel's threads hold at most 2 state
+    // pairs (narrow workgroups: up to 32 heads, or 64 at 49-64 nodes). Otherwise the commit
+    // kernel, then the verify kernel on the committed state.
+    const bool small = T <= 16 && (solver == CANOPY_SOLVE_AUTO || solver == CANOPY_SOLVE_NEUMANN);
+    const bool mid = T > 16 && T <= 64 && solver != CANOPY_SOLVE_LEVEL;
+    if (T_prev <= 64 && (small || mid)) {
         VerifyArgs a{};
         a.q = q; a.k = k; a.v = v;
         a.alpha = alpha; a.beta = beta; a.S0 = S0; a.parent = parent; a.tree_len = tree_len;
@@ -158,7 +162,10 @@ canopy_status canopy_commit_verify(const float *S0, const void *k_prev, const fl
         a.anc_mask = anc_mask; a.depth = depth; a.tree_status = tree_status;
         const PrevCommitArgs c{k_prev, U_prev, alpha_prev, parent_prev, tree_len_prev, path,
                                path_len, T_prev, S_new, path_status};
-        return from_hip(launch_commit_verify_small(a, c, waves, stream));
+        if (small) return from_hip(launch_commit_verify_small(a, c, waves, stream));
+        const int col_tiles = waves == 8 ? 4 : waves;
+        if (commit_verify_mid_fits(a, col_tiles))
+            return from_hip(launch_commit_verify_mid(a, c, col_tiles, stream));
     }
     const canopy_status st = canopy_commit(S0, k_prev, in_dtype, U_prev, alpha_prev, parent_prev,
                                            tree_len_prev, path, path_len, B, H, HV, T_prev, S_new,

@@ -141,6 +141,9 @@ hipError_t launch_verify_small(const VerifyArgs &a, int waves, hipStream_t strea
 hipError_t launch_commit_verify_small(const VerifyArgs &a, const PrevCommitArgs &c, int waves,
                                       hipStream_t stream);
 hipError_t launch_verify_mid(const VerifyArgs &a, int col_tiles, hipStream_t stream);
+bool commit_verify_mid_fits(const VerifyArgs &a, int col_tiles);
+hipError_t launch_commit_verify_mid(const VerifyArgs &a, const PrevCommitArgs &c, int col_tiles,
+                                    hipStream_t stream);
 hipError_t launch_verify_wide(const VerifyArgs &a, int col_tiles, hipStream_t stream);
 hipError_t launch_prep(const PrepArgs &a, hipStream_t stream);
 hipError_t launch_commit(const CommitArgs &a, hipStream_t stream);

@@ -26,6 +26,13 @@
 // tiles of a workgroup share the Gram tiles and the inverse powers and run their solves as
 // independent MFMA chains. Decay ratios are powers of two of fp64 differences of log2 sums
 // (v_exp_f32), so no cancellation of long path sums enters them.
+//
+// The fused variant (FUSE) first commits the previous tree's accepted path into the S0 values
+// each thread holds ("Design decisions / What the commit kernel stores"): S = P_a S0 +
+// sum_t w_t k_t u_t^T on the VALU, four path positions per round of requests (each position's
+// 8 key values of the thread's row chunk and the U entry of its column), then writes the new
+// state and stages it for the verify in place of S0. Only for shapes whose threads hold at
+// most 2 (column, row chunk) pairs, so that a round's operands fit in registers.
 #include "canopy_device.hpp"
 #include "canopy_kernels.hpp"
 #include <limits.h>
@@ -58,8 +65,44 @@ __device__ __forceinline__ void wait_lds_flag(int *flag) {
     }
 }
 
-template <bool BF, int NSB, int NCT>
-__global__ __launch_bounds__(64 * NSB) void verify_mid_kernel(VerifyArgs a) {
+// Fused commit: for path positions first .. first+CG-1 (node 0 past the path, whose finite
+// values meet a zero weight), the key values at rows 8kc .. 8kc+7 and the U entry at column cc
+// of each (column, row chunk) pair m of this thread.
+template <bool BF, int PPT, int CG>
+__device__ __forceinline__ void mid_prev_group(const PrevCommitArgs &c, size_t kbase, size_t krs,
+                                               size_t ubase, size_t urs, int nsel, int first, int pmv,
+                                               const int (&kc)[PPT], const int (&cc)[PPT],
+                                               float (&ck)[CG][PPT][8], float (&cu)[CG][PPT]) {
+#pragma unroll
+    for (int tt = 0; tt < CG; ++tt) {
+        const int t = first + tt;
+        const int nr = __builtin_amdgcn_readlane(nsel, min(t, 63));
+        const int node = t < pmv ? nr : 0;
+        const size_t ko = kbase + static_cast<size_t>(node) * krs;
+        const size_t uo = ubase + static_cast<size_t>(node) * urs;
+#pragma unroll
+        for (int m = 0; m < PPT; ++m) {
+            if constexpr (BF) {
+                const uint4 w = *reinterpret_cast<const uint4 *>(static_cast<const uint16_t *>(c.k) + ko + 8 * kc[m]);
+                const uint32_t ww[4] = {w.x, w.y, w.z, w.w};
+#pragma unroll
+                for (int q = 0; q < 4; ++q) {
+                    ck[tt][m][2 * q] = __uint_as_float(ww[q] << 16);
+                    ck[tt][m][2 * q + 1] = __uint_as_float(ww[q] & 0xFFFF0000u);
+                }
+            } else {
+                const float4 f0 = *reinterpret_cast<const float4 *>(static_cast<const float *>(c.k) + ko + 8 * kc[m]);
+                const float4 f1 = *reinterpret_cast<const float4 *>(static_cast<const float *>(c.k) + ko + 8 * kc[m] + 4);
+                ck[tt][m][0] = f0.x; ck[tt][m][1] = f0.y; ck[tt][m][2] = f0.z; ck[tt][m][3] = f0.w;
+                ck[tt][m][4] = f1.x; ck[tt][m][5] = f1.y; ck[tt][m][6] = f1.z; ck[tt][m][7] = f1.w;
+            }
+            cu[tt][m] = c.U[uo + cc[m]];
+        }
+    }
+}
+
+template <bool BF, int NSB, int NCT, bool FUSE>
+__global__ __launch_bounds__(64 * NSB) void verify_mid_kernel(VerifyArgs a, PrevCommitArgs c) {
     using Op = Ops<BF>;
     using In = typename Op::In;
     using Sp = typename Op::Sp;
@@ -85,6 +128,13 @@ __global__ __launch_bounds__(64 * NSB) void verify_mid_kernel(VerifyArgs a) {
     const SeqLen sl = seq_len(a.tree_len, b, T);
     const int Tb = sl.n;  // this sequence's node count
     const bool writer = grp == 0 && p == 0;  // this head's wave for the per-node outputs
+
+    // ---- fused commit, first request: the accepted path (lane = path position)
+    int pm = 0, pnd = -1;
+    if constexpr (FUSE) {
+        pm = c.path_len[b];
+        pnd = c.path[static_cast<size_t>(b) * c.T + min(lane, c.T - 1)];
+    }
 
     // ---- every load up front, unconditional (rows and nodes past T read row or node T-1;
     // rows and nodes past Tb are padding, dropped by selects later): tree and gates (lane = node), the wave's own K and Q rows, the
@@ -125,6 +175,32 @@ __global__ __launch_bounds__(64 * NSB) void verify_mid_kernel(VerifyArgs a) {
         for (int e = 0; e < 4; ++e)
             vraw[ct][e] = Op::load_raw(a.v, base + static_cast<size_t>(min(16 * p + 4 * lg + e, T - 1)) * rs +
                                                 colw + 16 * ct + lr);
+
+    // ---- fused commit, second request: the path nodes' parents and gates (lane = position) and
+    // the operands of path positions 0..3 for this thread's (column, row chunk) pairs
+    constexpr int CG = 4;
+    constexpr int CGF = FUSE ? CG : 1;
+    int pmv = 0, nsel = 0, ppar = -1;
+    SeqLen psl{1, false};
+    float pal = 1.f, ck[CGF][PPT][8], cu[CGF][PPT];
+    int pkc[PPT], pcc[PPT];
+#pragma unroll
+    for (int m = 0; m < PPT; ++m) {
+        const int x = min(tid + m * NT, NPAIR - 1);
+        pcc[m] = x % (16 * NCT);
+        pkc[m] = x / (16 * NCT);
+    }
+    const size_t pkbase = FUSE ? qk_base(b, h, H, a.HK, c.T) : 0;
+    const size_t pubase = (static_cast<size_t>(b) * (FUSE ? c.T : 0) * H + h) * D + colw;
+    if constexpr (FUSE) {
+        psl = seq_len(c.tree_len, b, c.T);
+        const bool plenok = !psl.bad && pm >= 0 && pm <= psl.n;
+        pmv = plenok ? pm : 0;
+        nsel = min(max(pnd, 0), c.T - 1);
+        ppar = c.parent[static_cast<size_t>(b) * c.T + nsel];
+        pal = c.alpha[(static_cast<size_t>(b) * c.T + nsel) * H + h];
+        mid_prev_group<BF, PPT, CGF>(c, pkbase, qkrs, pubase, rs, nsel, 0, pmv, pkc, pcc, ck, cu);
+    }
 
     // ---- prep over the wave's lanes. A malformed tree is computed through like a forest (bad
     // parents read as -1) and replaced by NaN at the stores.
@@ -174,6 +250,62 @@ __global__ __launch_bounds__(64 * NSB) void verify_mid_kernel(VerifyArgs a) {
 #pragma unroll
     for (int bit = 5; bit >= 0; --bit)
         if (__any(depth >= (dtree | (1 << bit)))) dtree |= 1 << bit;
+
+    // ---- fused commit: path check (each node a child of the one before, inside the previous
+    // tree), suffix sums of log2 alpha in fp64, w_t = 2^(suffix after t), P_a = 2^(total); the
+    // rank update of this thread's S0 values, written out as the new state
+    if constexpr (FUSE) {
+        const bool inp = lane < pmv;
+        const int up = __shfl_up(pnd, 1, 64);
+        const int prevn = lane == 0 ? -1 : up;
+        const bool ok = !inp || (pnd >= 0 && pnd < psl.n && ppar == prevn);
+        const unsigned long long pbad = __ballot(!ok);
+        const bool plenok = !psl.bad && pm >= 0 && pm <= psl.n;
+        // -1 for a length out of range, else 1 + the first bad position
+        const int pst = !plenok ? -1 : (pbad ? __ffsll(static_cast<unsigned long long>(pbad)) : 0);
+        const double la = inp ? static_cast<double>(__builtin_amdgcn_logf(pal)) : 0.0;
+        double sv = la;  // lanes at or past the path hold 0
+#pragma unroll
+        for (int off = 1; off < 64; off <<= 1) {
+            const double tv = __shfl_down(sv, off, 64);
+            sv = lane + off < 64 ? sv + tv : sv;
+        }
+        const float Pa = __builtin_amdgcn_exp2f(static_cast<float>(__shfl(sv, 0, 64)));
+        const float w = __builtin_amdgcn_exp2f(static_cast<float>(sv - la));  // decay after t
+        float acc[PPT][8];
+#pragma unroll
+        for (int m = 0; m < PPT; ++m)
+#pragma unroll
+            for (int e = 0; e < 8; ++e) acc[m][e] = 0.f;
+        for (int g0 = 0; g0 < max(pmv, 1); g0 += CG) {
+            if (g0 > 0) mid_prev_group<BF, PPT, CGF>(c, pkbase, qkrs, pubase, rs, nsel, g0, pmv, pkc, pcc, ck, cu);
+#pragma unroll
+            for (int tt = 0; tt < CG; ++tt) {
+                const int t = g0 + tt;
+                const float wr = __int_as_float(__builtin_amdgcn_readlane(__float_as_int(w), min(t, 63)));
+                const float wt = t < pmv ? wr : 0.f;
+#pragma unroll
+                for (int m = 0; m < PPT; ++m) {
+                    const float wu = wt * cu[tt][m];
+#pragma unroll
+                    for (int e = 0; e < 8; ++e) acc[m][e] += wu * ck[tt][m][e];
+                }
+            }
+        }
+        const float qnan = __builtin_nanf("");
+        float *Sn = c.S_new + static_cast<size_t>(bh) * D * D + colw;
+#pragma unroll
+        for (int m = 0; m < PPT; ++m) {
+#pragma unroll
+            for (int e = 0; e < 8; ++e) s0v[m][e] = pst != 0 ? qnan : Pa * s0v[m][e] + acc[m][e];
+            if (tid + m * NT < NPAIR) {
+#pragma unroll
+                for (int e = 0; e < 8; ++e)
+                    store_nt(Sn + static_cast<size_t>(8 * pkc[m] + e) * D + pcc[m], s0v[m][e]);
+            }
+        }
+        if (c.path_status && grp == 0 && h == 0 && tid == 0) c.path_status[b] = pst;
+    }
 
     // ---- stage: the per-node table (private to the wave), this wave's keys, the S0 columns
     sm.lam[p][lane] = lam;
@@ -433,37 +565,67 @@ __global__ __launch_bounds__(64 * NSB) void verify_mid_kernel(VerifyArgs a) {
         }
 }
 
-template <bool BF, int NSB>
-static void launch_mid_nct(const VerifyArgs &a, int nct, hipStream_t stream) {
-    const unsigned heads = static_cast<unsigned>(a.B * a.H);
-    const dim3 block(64 * NSB);
-    switch (nct) {
-        case 1: hipLaunchKernelGGL((verify_mid_kernel<BF, NSB, 1>), dim3(heads * 8), block, 0, stream, a); break;
-        case 2: hipLaunchKernelGGL((verify_mid_kernel<BF, NSB, 2>), dim3(heads * 4), block, 0, stream, a); break;
-        default: hipLaunchKernelGGL((verify_mid_kernel<BF, NSB, 4>), dim3(heads * 2), block, 0, stream, a); break;
+// The fused variant exists only where each thread holds at most 2 (column, row chunk) pairs.
+template <bool BF, int NSB, int NCT, bool FUSE>
+static void launch_mid_one(const VerifyArgs &a, const PrevCommitArgs &c, hipStream_t stream) {
+    if constexpr (!FUSE || 4 * NCT <= 2 * NSB) {
+        const unsigned heads = static_cast<unsigned>(a.B * a.H);
+        hipLaunchKernelGGL((verify_mid_kernel<BF, NSB, NCT, FUSE>), dim3(heads * (8 / NCT)), dim3(64 * NSB), 0,
+                           stream, a, c);
     }
 }
 
-template <bool BF>
-static void launch_mid_dtype(const VerifyArgs &a, int nct, hipStream_t stream) {
-    switch ((a.T + 15) / 16) {
-        case 2: launch_mid_nct<BF, 2>(a, nct, stream); break;
-        case 3: launch_mid_nct<BF, 3>(a, nct, stream); break;
-        default: launch_mid_nct<BF, 4>(a, nct, stream); break;
+template <bool BF, int NSB, bool FUSE>
+static void launch_mid_nct(const VerifyArgs &a, const PrevCommitArgs &c, int nct, hipStream_t stream) {
+    switch (nct) {
+        case 1: launch_mid_one<BF, NSB, 1, FUSE>(a, c, stream); break;
+        case 2: launch_mid_one<BF, NSB, 2, FUSE>(a, c, stream); break;
+        default: launch_mid_one<BF, NSB, 4, FUSE>(a, c, stream); break;
     }
+}
+
+template <bool BF, bool FUSE>
+static void launch_mid_dtype(const VerifyArgs &a, const PrevCommitArgs &c, int nct, hipStream_t stream) {
+    switch ((a.T + 15) / 16) {
+        case 2: launch_mid_nct<BF, 2, FUSE>(a, c, nct, stream); break;
+        case 3: launch_mid_nct<BF, 3, FUSE>(a, c, nct, stream); break;
+        default: launch_mid_nct<BF, 4, FUSE>(a, c, nct, stream); break;
+    }
+}
+
+static int mid_col_tiles(const VerifyArgs &a, int col_tiles) {
+    if (col_tiles != 0) return col_tiles;
+    const long long heads = static_cast<long long>(a.B) * a.H;
+    return heads <= 32 ? 1 : (heads <= 64 ? 2 : 4);
 }
 
 // col_tiles: 16-column tiles per workgroup (1, 2 or 4); 0 picks by the number of heads.
 hipError_t launch_verify_mid(const VerifyArgs &a, int col_tiles, hipStream_t stream) {
-    int nct = col_tiles;
-    if (nct == 0) {
-        const long long heads = static_cast<long long>(a.B) * a.H;
-        nct = heads <= 32 ? 1 : (heads <= 64 ? 2 : 4);
-    }
+    const int nct = mid_col_tiles(a, col_tiles);
+    const PrevCommitArgs none{};
     if (a.bf16)
-        launch_mid_dtype<true>(a, nct, stream);
+        launch_mid_dtype<true, false>(a, none, nct, stream);
     else
-        launch_mid_dtype<false>(a, nct, stream);
+        launch_mid_dtype<false, false>(a, none, nct, stream);
+    return hipGetLastError();
+}
+
+// Whether the fused commit fits this shape: each thread holds at most 2 (column, row chunk)
+// pairs of S0, i.e. 4 * tiles <= 2 * sub-blocks.
+bool commit_verify_mid_fits(const VerifyArgs &a, int col_tiles) {
+    const int nsb = (a.T + 15) / 16, nct = mid_col_tiles(a, col_tiles);
+    return a.T > 16 && a.T <= 64 && 4 * nct <= 2 * nsb;
+}
+
+// The commit of the previous tree's path (c.T <= 64: one path position per lane) fused in front
+// of the verify of a tree of 17 to 64 nodes; a.S0 is the state before the commit.
+hipError_t launch_commit_verify_mid(const VerifyArgs &a, const PrevCommitArgs &c, int col_tiles,
+                                    hipStream_t stream) {
+    const int nct = mid_col_tiles(a, col_tiles);
+    if (a.bf16)
+        launch_mid_dtype<true, true>(a, c, nct, stream);
+    else
+        launch_mid_dtype<false, true>(a, c, nct, stream);
     return hipGetLastError();
 }
 
