@@ -5,7 +5,8 @@ A step is one pass of the hot path over one layer's synthetic batch, as a decode
 canopy_commit_verify commits the previous round's accepted path (a random root-to-leaf path of
 the tree) into the state the loop carries, then verifies the tree from the committed state
 (tree preprocessing, S0 projections, masked Gram matrices, triangular solve, read-out). For
-trees of at most 16 nodes that is one launch; otherwise the commit kernel and the verify kernel.
+trees of at most 16 nodes, and of 17 to 64 at small batch, that is one launch; otherwise the
+commit kernel and the verify kernel.
 The same work as two separate calls (canopy_tree_verify, then canopy_commit) is timed beside
 it, and so is the serial fork baseline. Inputs are resident in HBM before the timed region; the
 timed region holds exactly --steps steps between two stream synchronisations, timed with HIP
@@ -91,16 +92,30 @@ def fused_step_bytes(B, H, T, dtype, m_total, HK=None, nodes=None):
     return verify_bytes(B, H, T, dtype, HK=HK, nodes=nodes) + commit_bytes(B, H, m_total) - B * H * 128 * 128 * 4
 
 
-def one_launch_step(T, solver):
-    """Whether canopy_commit_verify runs the step as one launch (trees of at most 16 nodes after
-    trees of at most 64, AUTO or NEUMANN)."""
-    return T <= 16 and solver in ("auto", "neumann")
+def _mid_col_tiles(heads, waves):
+    """The 17-64-node kernel's 16-column tiles per workgroup, as the library picks them."""
+    if waves:
+        return 4 if waves == 8 else waves
+    return 1 if heads <= 32 else (2 if heads <= 64 else 4)
 
 
-def fused_kernel_name(dtype="bf16", waves=0):
+def one_launch_step(T, solver, heads=32, waves=0):
+    """Whether canopy_commit_verify runs the step as one launch (after previous trees of at most
+    64 nodes): trees of at most 16 nodes (AUTO, NEUMANN), and trees of 17 to 64 nodes (not
+    LEVEL) whose workgroups hold at most 2 state pairs per thread (4 * tiles <= 2 * sub-blocks)."""
+    if T <= 16:
+        return solver in ("auto", "neumann")
+    if T <= 64 and solver != "level":
+        return 4 * _mid_col_tiles(heads, waves) <= 2 * ((T + 15) // 16)
+    return False
+
+
+def fused_kernel_name(T, dtype="bf16", heads=32, waves=0):
     """The one-launch step's kernel as the profiler names it."""
-    return "canopy::verify_small_kernel<%s, %d, true>" % ("true" if dtype == "bf16" else "false",
-                                                         waves if waves else 1)
+    bf = "true" if dtype == "bf16" else "false"
+    if T <= 16:
+        return "canopy::verify_small_kernel<%s, %d, true>" % (bf, waves if waves else 1)
+    return "canopy::verify_mid_kernel<%s, %d, %d, true>" % (bf, (T + 15) // 16, _mid_col_tiles(heads, waves))
 
 
 def verify_flops_ragged(H, lens):
@@ -192,7 +207,7 @@ def pmc_summary(run_dir, out_path):
         wscale = probe / 1024.0 / max(w["__amd_rocclr_copyBuffer"])
         ent = {"config": rec["config"], "fetch_scale": round(fscale, 4), "write_scale": round(wscale, 4)}
         def is_fused(k):
-            return k.startswith("void canopy::verify_small_kernel<") and ", true>(" in k
+            return k.startswith("void canopy::verify") and ", true>(" in k
         roles = (("verify", lambda k: k.startswith("void canopy::verify") and not is_fused(k), True),
                  ("commit", lambda k: k.startswith("void canopy::commit_kernel<"), True),
                  ("fused", is_fused, False))
@@ -1012,13 +1027,13 @@ def main(argv=None):
     nodes = int(lens.sum())
     vbytes = verify_bytes(B, H, T, dt, HK=HK, nodes=nodes)
     vflops = verify_flops_ragged(H, lens)
-    one = one_launch_step(T, args.solver)
+    one = one_launch_step(T, args.solver, B * H, args.waves)
     if one:
         # the dominant (only) kernel of the step: commit + verify in one launch per step
         m_total = int(inp["path_len"].sum())
         rbytes = fused_step_bytes(B, H, T, dt, m_total, HK=HK, nodes=nodes)
         rflops = vflops + H * 2 * 128 * 128 * m_total
-        r_us, r_kernel, r_role = us_step, fused_kernel_name(dt, args.waves), "fused"
+        r_us, r_kernel, r_role = us_step, fused_kernel_name(T, dt, B * H, args.waves), "fused"
         r_note = "one launch per step (commit + verify): algorithmic bytes and flops of both"
     else:
         rbytes, rflops, r_us, r_role = vbytes, vflops, us_verify, "verify"
