@@ -173,10 +173,12 @@ canopy_status canopy_commit(const float *S0, const void *k, canopy_dtype in_dtyp
  * One decode step of a layer: commit the previous tree's accepted path, then verify the new
  * draft tree from the committed state. The result equals canopy_commit followed by
  * canopy_tree_verify with S0 = S_new (the commit of "What the commit kernel stores" and the
- * closed form of "The tree closed form"; the two steps are only ordered, not changed). For a
- * new tree of at most 16 nodes after a previous tree of at most 64 (AUTO or NEUMANN) both run
- * in one launch and the committed state goes from registers straight into the projections;
- * otherwise the two kernels run one after the other on the stream.
+ * closed form of "The tree closed form"; the two steps are only ordered, not changed). After a
+ * previous tree of at most 64 nodes, both run in one launch and the committed state goes from
+ * registers straight into the verify for new trees of at most 16 nodes (AUTO or NEUMANN) and
+ * for 17 to 64 nodes (not LEVEL) when the 17-64 kernel's workgroups are narrow (B*HV <= 32, or
+ * <= 64 at 49-64 nodes, with waves 0; or waves 1, or 2 at 49-64 nodes); otherwise the two
+ * kernels run one after the other on the stream.
  *   S0, k_prev, U_prev, alpha_prev, parent_prev, tree_len_prev, path, path_len: as S0, k, U,
  *               alpha, parent, tree_len, path and path_len of canopy_commit, for the previous
  *               tree of T_prev nodes (k_prev [B,T_prev,H,128] in in_dtype).
