@@ -1,8 +1,9 @@
 """The entry points captured in a HIP graph: every replay gives bit for bit what eager calls give
 on the inputs the static buffers hold at that replay.
 
-Each case captures one step (verify + commit; the hybrid and the serial fork with their
-commits; the convolution + its commit; the layered commit) with preallocated outputs, then
+Each case captures one step (verify + commit; the decode step of canopy_commit_verify; the
+hybrid and the serial fork with their commits; the convolution + its commit; the layered
+commit) with preallocated outputs, then
 replays it four times. Before each replay the static inputs are overwritten with one of two
 seeded input sets and the outputs with NaN, and unrelated eager work runs between replays;
 after each replay the outputs must equal those of eager calls on the same input set. The first
@@ -311,4 +312,61 @@ def test_commit_layers_graph(canopy):
         for l in range(L):
             _same(f"S_new layer {l}", _np(outs[l]), eager[src][l])
         _same("path status", _np(pst), eager[src][L])
+    del g
+
+
+@pytest.mark.parametrize("B,H,Tp,T", [(1, 32, 16, 16), (1, 8, 64, 64), (2, 4, 30, 40), (2, 4, 64, 130)])
+def test_commit_verify_graph(canopy, B, H, Tp, T):
+    """The decode step (commit of the previous tree's path, then the verify) in one launch (the
+    first three shapes) and in two (the last), the state committed in place."""
+    import torch
+    sets = []
+    for s in range(2):
+        prev = synth.make_inputs(B, H, Tp, tree="random", dtype="bf16", seed=5500 + 10 * s + T)
+        new = synth.make_inputs(B, H, T, tree="random", dtype="bf16", seed=5501 + 10 * s + T)
+        dp, dn = to_device(prev), to_device(new)
+        U_prev = canopy.tree_verify(dp["q"], dp["k"], dp["v"], dp["alpha"], dp["beta"], dp["S0"],
+                                    dp["parent"])[1]
+        sets.append((dp, dn, U_prev))
+    torch.cuda.synchronize()
+    st = [{n: t.clone() for n, t in d.items()} for d in sets[0][:2]] + [sets[0][2].clone()]
+    S = st[0]["S0"]
+    O = torch.empty((B, T, H, 128), device="cuda")
+    U = torch.empty_like(O)
+    ell = torch.empty((B, T, H), device="cuda")
+
+    def step(dp, dn, U_prev, S_io, outs):
+        _, pst, _, _, _ = canopy.commit_verify(S_io, dp["k"], U_prev, dp["alpha"], dp["parent"], dp["path"],
+                                               dp["path_len"], dn["q"], dn["k"], dn["v"], dn["alpha"],
+                                               dn["beta"], dn["parent"], out=outs, S_out=S_io)
+        return pst
+
+    eager = []
+    for dp, dn, U_prev in sets:
+        S_e = dp["S0"].clone()
+        outs = (_nan_like(O), _nan_like(U), _nan_like(ell))
+        pst = step(dp, dn, U_prev, S_e, outs)
+        torch.cuda.synchronize()
+        eager.append([_np(S_e), _np(pst)] + [_np(t) for t in outs])
+    torch.cuda.synchronize()
+    _say("capture commit_verify", B, H, Tp, T)
+    g = torch.cuda.CUDAGraph()
+    with torch.cuda.graph(g):
+        pst = step(st[0], st[1], st[2], S, (O, U, ell))
+    for r in range(REPLAYS):
+        src = r % 2
+        for dst, srcd in zip(st[:2], sets[src][:2]):
+            for n, t in dst.items():
+                t.copy_(srcd[n])
+        st[2].copy_(sets[src][2])
+        for t in (O, U, ell):
+            t.fill_(float("nan"))
+        _noise(canopy, sets[1 - src][1])
+        torch.cuda.synchronize()
+        g.replay()
+        torch.cuda.synchronize()
+        _say("replay", r, "input set", src)
+        for name, x, y in zip(("S_new", "path status", "O", "U", "ell"),
+                              [_np(S), _np(pst), _np(O), _np(U), _np(ell)], eager[src]):
+            _same(name, x, y)
     del g
