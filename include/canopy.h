@@ -92,6 +92,20 @@ typedef enum {
 /* Library version, major * 10000 + minor * 100 + patch. */
 int canopy_version(void);
 
+/*
+ * Test hook for failure handling (not part of the method). Some kernels hand results from one
+ * wave to another inside a workgroup: the 17-64-node verify and the 65-256-node
+ * wave-per-sub-block verify (solved sub-blocks of U), and canopy_hybrid_verify (fork
+ * snapshots). A waiting wave sleeps between checks and gives up after `sleeps` sleeps; the
+ * default, 2^24, is never reached (every publisher is resident and waits on nothing later).
+ * A wave that gives up writes NaN for every output row it computes, passes the loss on to the
+ * waves that wait for it in turn, and sets tree_status[b] = -2. Bound 0 makes every such wait
+ * give up at once, so the whole path of a lost hand-off can be checked from the host with every
+ * kernel still ending normally. sleeps < 0 restores the default. Applies to launches enqueued
+ * after the call, in this process (one process-wide value); returns the previous bound.
+ */
+int canopy_set_wait_bound(int sleeps);
+
 /* Text for a status code (static storage). */
 const char *canopy_status_string(canopy_status s);
 
@@ -108,7 +122,11 @@ const char *canopy_status_string(canopy_status s);
  *               parent counting 0, summed in fp64 and rounded once.
  *   tree_status [B] int32, out, may be NULL: 0; -1 for a tree_len outside 1..T; else 1 + the
  *               first node i whose parent is not in -1..i-1 (then mask and depth rows are 0
- *               and ell is NaN).
+ *               and ell is NaN). The verify calls also report -2 when a wave gave up waiting
+ *               for another wave's result (see canopy_set_wait_bound; the rows computed from it
+ *               are NaN). The status of a valid tree is stored right after the tree
+ *               preprocessing and a wait gives up only after its full bound, so -2 is the value
+ *               left in place.
  */
 canopy_status canopy_tree_prep(const int32_t *parent, const int32_t *tree_len, const float *alpha,
                                int B, int HV, int T, uint32_t *anc_mask, int32_t *depth, float *ell,

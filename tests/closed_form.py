@@ -1,86 +1,88 @@
-"""NumPy prototype of the tree closed form, used by the tests only.
+"""The tree closed form in NumPy, for the tests only.
 
-It states the algebra that the HIP library implements, written from the canopy project page
-("The tree closed form" and "Design decisions / Two solve strategies"), so that the tests can
-(1) pin the oracle against an independent formula and (2) check every solve strategy against
-the oracle before any kernel runs. It is not the oracle and not the product: it imports
-neither.
+It restates, per node, the algebra that the HIP library implements (the canopy project page,
+"The tree closed form" and "Design decisions / Two solve strategies"), so that the tests can
+(1) pin the oracle against a second formulation that shares nothing with it and (2) check every
+solve strategy against the oracle before any kernel runs. It is neither the oracle nor the
+product, and imports neither.
 
-For one (batch, head) with T nodes (parents before children):
-  l_i = log alpha_i + l_parent(i)                 (0 for a root's parent)
-  Gamma_ij = exp(l_i - l_j) for j in path(i), else 0
-  G_ij = beta_i Gamma_ij k_i.k_j for j a strict ancestor of i, else 0
-  R_i = beta_i (v_i - exp(l_i) S0^T k_i)
-  (I + G) U = R
-  C_ij = Gamma_ij q_i.k_j for j in path(i), else 0
-  O = diag(exp l) Q S0 + C U
-  S_a = exp(l_a) S0 + sum_{j in path(a)} Gamma_aj k_j u_j^T
+The matrices are built entry by entry from each node's root path: node i's row holds one entry
+per node j on path(i), weighted by the decay accumulated strictly below j on that path
+(exp(l_i - l_j), with l the running sum of log alpha from the root). The G row leaves out i
+itself and carries beta_i; the C row keeps it. The right-hand side subtracts the decayed
+initial state's read of k_i, and the output starts from its read of q_i. The commit replays the
+accepted path's updates, S <- alpha_n S + k_n u_n^T, root first.
 """
 from __future__ import annotations
 
 import numpy as np
 
 
-def ancestor_masks(parent):
-    """Strict and inclusive ancestor masks (bool [T,T]) by walking parents."""
-    T = len(parent)
-    Mp = np.zeros((T, T), dtype=bool)
-    for i in range(T):
-        n = i
-        while n >= 0:
-            Mp[i, n] = True
-            n = parent[n]
-    Mm = Mp & ~np.eye(T, dtype=bool)
-    return Mm, Mp
+def root_paths(parent):
+    """path(i) for every node, as a list of node ids from the root down to i (a node's list is
+    its parent's list with itself appended)."""
+    paths = []
+    for i, p in enumerate(np.asarray(parent)):
+        paths.append((paths[p] + [i]) if p >= 0 else [i])
+    return paths
 
 
 def depth_of(parent):
-    Mm, _ = ancestor_masks(parent)
-    return Mm.sum(1)
+    """|A(i)|: the length of each node's root path, minus the node."""
+    return np.array([len(p) - 1 for p in root_paths(parent)], dtype=int)
 
 
 def log_decay(parent, alpha, dtype=np.float64):
+    """l_i: log alpha summed along path(i), root first, in ``dtype``."""
     la = np.log(np.asarray(alpha, dtype=dtype))
-    ell = np.zeros(len(parent), dtype=dtype)
-    for i in range(len(parent)):
-        ell[i] = la[i] + (ell[parent[i]] if parent[i] >= 0 else dtype(0))
+    ell = np.empty(len(parent), dtype=dtype)
+    for i, path in enumerate(root_paths(parent)):
+        acc = dtype(0)
+        for n in path:
+            acc = acc + la[n]
+        ell[i] = acc
     return ell
 
 
 def build_system(parent, q, k, v, alpha, beta, S0, dtype=np.float64, naive_ratio=False,
                  drop=None):
-    """G, C, R, the output's first term and ell for one (batch, head).
+    """G, C, R, the output's first term and l for one (batch, head), each row from the node's
+    root path.
 
-    ``naive_ratio`` forms Gamma as P_i / P_j instead of exp(l_i - l_j) (a negative control).
-    ``drop`` plants one of the feature-drop mistakes used by the control tests:
-    "causal" (lower triangle instead of the ancestor mask), "gamma" (no decay ratio in G, C),
-    "strict_c" (C without its diagonal), "chain" (the tree read as a chain)."""
+    ``naive_ratio`` weighs an entry by the ratio of cumulative decays P_i / P_j instead of
+    exp(l_i - l_j) (a negative control). ``drop`` plants one of the mistakes of the
+    feature-drop controls: "causal" (every earlier node counted as an ancestor, the causal
+    triangle), "gamma" (no decay weight), "strict_c" (C without the node's own entry), "chain"
+    (the tree read as a chain)."""
     q, k, v = (np.asarray(x, dtype=dtype) for x in (q, k, v))
     beta = np.asarray(beta, dtype=dtype)
     S0 = np.asarray(S0, dtype=dtype)
-    par = np.asarray(parent)
-    if drop == "chain":
-        par = np.arange(-1, len(par) - 1)
-    Mm, Mp = ancestor_masks(par)
-    if drop == "causal":
-        T = len(par)
-        Mp = np.tril(np.ones((T, T), dtype=bool))
-        Mm = Mp & ~np.eye(T, dtype=bool)
+    T = len(parent)
+    par = np.arange(-1, T - 1) if drop == "chain" else np.asarray(parent)
     ell = log_decay(par, alpha, dtype)
     P = np.exp(ell)
-    if naive_ratio:
-        with np.errstate(all="ignore"):
-            Gam = np.where(Mp, P[:, None] / P[None, :], 0.0).astype(dtype)
-    else:
-        diff = np.where(Mp, ell[:, None] - ell[None, :], 0.0)
-        Gam = np.where(Mp, np.exp(diff), 0.0).astype(dtype)
-    if drop == "gamma":
-        Gam = Mp.astype(dtype)
-    G = beta[:, None] * Gam * (k @ k.T) * Mm
-    Mc = Mm if drop == "strict_c" else Mp
-    C = Gam * (q @ k.T) * Mc
-    R = beta[:, None] * (v - P[:, None] * (k @ S0))
-    O0 = P[:, None] * (q @ S0)
+    rows = [list(range(i + 1)) for i in range(T)] if drop == "causal" else root_paths(par)
+    G = np.zeros((T, T), dtype=dtype)
+    C = np.zeros((T, T), dtype=dtype)
+    one = dtype(1)
+    with np.errstate(all="ignore"):
+        for i in range(T):
+            for j in rows[i]:
+                if drop == "gamma":
+                    w = one
+                elif naive_ratio:
+                    w = P[i] / P[j]
+                else:
+                    w = np.exp(ell[i] - ell[j])
+                if j != i:
+                    G[i, j] = beta[i] * w * np.dot(k[i], k[j])
+                if j != i or drop != "strict_c":
+                    C[i, j] = w * np.dot(q[i], k[j])
+    R = np.empty((T, v.shape[1]), dtype=dtype)
+    O0 = np.empty((T, S0.shape[1]), dtype=dtype)
+    for i in range(T):
+        R[i] = beta[i] * (v[i] - P[i] * (S0.T @ k[i]))
+        O0[i] = P[i] * (S0.T @ q[i])
     return G, C, R, O0, ell
 
 
@@ -169,16 +171,14 @@ def closed_form(parent, q, k, v, alpha, beta, S0, solver="dense", dtype=np.float
 
 
 def commit_formula(parent, a, k, alpha, U, S0, dtype=np.float64):
-    """S_a = exp(l_a) S0 + sum_{j in path(a)} Gamma_aj k_j u_j^T (a < 0: S0)."""
-    S0 = np.asarray(S0, dtype=dtype)
+    """The state after accepting node a, from the pseudo-values U: the updates of path(a)
+    replayed root first, S <- alpha_n S + k_n u_n^T (a < 0: S0 unchanged). Unrolled, this is
+    P_a S0 plus each path node's k_j u_j^T decayed by the gates below it."""
+    S = np.array(S0, dtype=dtype, copy=True)
     if a < 0:
-        return S0.copy()
-    ell = log_decay(parent, alpha, dtype)
-    S = np.exp(ell[a]) * S0
-    j = a
-    while j >= 0:
-        S = S + np.exp(ell[a] - ell[j]) * np.outer(np.asarray(k[j], dtype), np.asarray(U[j], dtype))
-        j = parent[j]
+        return S
+    for n in root_paths(parent)[a]:
+        S = dtype(alpha[n]) * S + np.outer(np.asarray(k[n], dtype), np.asarray(U[n], dtype))
     return S
 
 

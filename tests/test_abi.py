@@ -89,3 +89,27 @@ def test_conv_host_checks_need_no_gpu():
     assert call(16, 5) == 1
     assert call(16, 1) == 1
     assert call(16, 4, x=nul) == 1
+
+
+def test_binding_refuses_other_head_dims():
+    """Every kernel is built for d_k = d_v = 128: the binding refuses any other width before a
+    pointer reaches the library (checked first, so CPU tensors show it without a GPU)."""
+    import pytest
+    import torch
+    import tree_speculative_verification_amd as canopy
+    B, T, H, d = 1, 4, 2, 64
+    q = torch.zeros((B, T, H, d), dtype=torch.bfloat16)
+    a = torch.ones((B, T, H))
+    S0 = torch.zeros((B, H, d, d))
+    par = torch.tensor([[-1, 0, 0, 1]], dtype=torch.int32)
+    with pytest.raises(ValueError, match="head dimension 64"):
+        canopy.tree_verify(q, q, q, a, a, S0, par)
+    with pytest.raises(ValueError, match="head dimension 64"):
+        canopy.commit(S0, q, torch.zeros((B, T, H, d)), a, par, par, torch.ones(1, dtype=torch.int32))
+    with pytest.raises(ValueError, match="head dimension 64"):
+        canopy.serial_verify(q, q, q, a, a, S0, par)
+    with pytest.raises(ValueError, match="head dimension 64"):
+        canopy.hybrid_verify(q, q, q, a, a, S0, par)
+    with pytest.raises(ValueError, match="head dimension 64"):
+        canopy.commit_verify(S0, q, torch.zeros((B, T, H, d)), a, par, par,
+                             torch.ones(1, dtype=torch.int32), q, q, q, a, a, par)

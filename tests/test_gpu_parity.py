@@ -123,58 +123,63 @@ def test_tile_edges(canopy, T, dtype):
 
 @pytest.mark.parametrize("B", [1, 2, 4, 8, 16])
 def test_config_skewed64_batch_sweep(canopy, B):
-    """B in {1..16}, H=32, T=64 skewed trees (independent per sequence), bf16, both solvers
-    and the serial baseline; oracle on sampled (b, h) pairs."""
+    """B in {1..16}, H=32, T=64 skewed trees (independent per sequence), bf16, every solver and
+    the serial baseline; every (b, h) pair against the oracle (about 0.1 s of oracle at B=16 on
+    16 host cores)."""
+    import time
     import torch
     inp = synth.make_inputs(B, 32, 64, tree="skewed", dtype="bf16", seed=200 + B)
     d = to_device(inp)
-    bsel = sorted(set([0, B - 1, B // 2]))
-    hsel = [0, 7, 31]
-    ref = run_oracle(slice_inputs(inp, bsel, hsel))
+    t0 = time.perf_counter()
+    ref = run_oracle(inp)
+    _say("skewed64 B", B, "oracle over the full grid: %.2f s" % (time.perf_counter() - t0))
     for solver in ("fwdsub", "neumann", "level", "auto"):
         _say("skewed64 B", B, solver)
         O, U, ell, mask, depth, st = _verify(canopy, d, solver=solver)
-        assert_close_heads("O", O[bsel][:, :, hsel], ref["O"], TOL["bf16"])
-        assert_close_heads("U", U[bsel][:, :, hsel], ref["U"], TOL["bf16"])
-        assert_ell(ell[bsel][:, :, hsel], ref["ell"])
+        assert_close_heads("O", O, ref["O"], TOL["bf16"])
+        assert_close_heads("U", U, ref["U"], TOL["bf16"])
+        assert_ell(ell, ref["ell"])
         _check_structure(inp, mask, depth, st)
     _say("skewed64 serial B", B)
     O, U, snap, st = canopy.serial_verify(d["q"], d["k"], d["v"], d["alpha"], d["beta"], d["S0"], d["parent"])
     torch.cuda.synchronize()
     O, U = O.cpu().numpy(), U.cpu().numpy()
     del snap
-    assert_close_heads("serial O", O[bsel][:, :, hsel], ref["O"], TOL["bf16"])
-    assert_close_heads("serial U", U[bsel][:, :, hsel], ref["U"], TOL["bf16"])
+    assert_close_heads("serial O", O, ref["O"], TOL["bf16"])
+    assert_close_heads("serial U", U, ref["U"], TOL["bf16"])
 
 
 def test_config_random256_b16(canopy):
     """The large tree at full size, in the launch configuration the benchmark uses: B=16 H=32
-    T=256 random recursive trees, bf16; oracle on sampled (b, h) pairs; commit of random
-    leaves."""
+    T=256 random recursive trees, bf16; every (b, h) pair of verify (every solver) and commit of
+    random leaves against the oracle (about 1 s of oracle on 16 host cores)."""
+    import time
     import torch
     inp = synth.make_inputs(16, 32, 256, tree="random", dtype="bf16", seed=300)
     d = to_device(inp)
-    bsel, hsel = [0, 5, 15], [0, 13, 31]
-    sub = slice_inputs(inp, bsel, hsel)
-    ref = run_oracle(sub)
+    t0 = time.perf_counter()
+    ref = run_oracle(inp)
+    _say("random256 B16 oracle over the full grid: %.2f s" % (time.perf_counter() - t0))
     for solver in ("fwdsub", "neumann", "level"):
         _say("random256 B16 verify", solver)
         O, U, ell, mask, depth, st = _verify(canopy, d, solver=solver)
-        assert_close_heads("O", O[bsel][:, :, hsel], ref["O"], TOL["bf16"])
-        assert_close_heads("U", U[bsel][:, :, hsel], ref["U"], TOL["bf16"])
+        assert_close_heads("O", O, ref["O"], TOL["bf16"])
+        assert_close_heads("U", U, ref["U"], TOL["bf16"])
     _say("random256 B16 verify auto")
     O, U, ell, mask, depth, st = _verify(canopy, d)
-    assert_close_heads("O", O[bsel][:, :, hsel], ref["O"], TOL["bf16"])
-    assert_close_heads("U", U[bsel][:, :, hsel], ref["U"], TOL["bf16"])
-    assert_ell(ell[bsel][:, :, hsel], ref["ell"])
+    assert_close_heads("O", O, ref["O"], TOL["bf16"])
+    assert_close_heads("U", U, ref["U"], TOL["bf16"])
+    assert_ell(ell, ref["ell"])
     _check_structure(inp, mask, depth, st)
     _say("random256 B16 commit")
     Sn, pst = canopy.commit(d["S0"], d["k"], torch.from_numpy(U).cuda(), d["alpha"], d["parent"],
                             d["path"], d["path_len"])
     torch.cuda.synchronize()
-    S_or, st_or = oracle_commit(sub)
-    assert np.array_equal(pst.cpu().numpy()[bsel], st_or)
-    assert_close_state("S_new", Sn.cpu().numpy()[bsel][:, hsel], S_or, TOL["bf16"])
+    t0 = time.perf_counter()
+    S_or, st_or = oracle_commit(inp)
+    _say("random256 B16 oracle commit over the full grid: %.2f s" % (time.perf_counter() - t0))
+    assert np.array_equal(pst.cpu().numpy(), st_or)
+    assert_close_state("S_new", Sn.cpu().numpy(), S_or, TOL["bf16"])
 
 
 def test_serial_snapshots_match_oracle_states(canopy):

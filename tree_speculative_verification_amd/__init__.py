@@ -21,7 +21,7 @@ import os
 import torch  # loaded first so that libcanopy binds to the HIP runtime torch uses
 
 __all__ = ["load", "lib_path", "tree_prep", "tree_verify", "commit", "serial_verify",
-           "serial_commit", "CanopyError", "SOLVERS"]
+           "serial_commit", "set_wait_bound", "CanopyError", "SOLVERS"]
 
 _HERE = os.path.dirname(os.path.abspath(__file__))
 _LIB_PATH = os.path.join(_HERE, "libcanopy.so")
@@ -50,6 +50,8 @@ def load():
     lib = ctypes.CDLL(_LIB_PATH)
     P, i, u64 = ctypes.c_void_p, ctypes.c_int, ctypes.c_void_p
     lib.canopy_version.restype = i
+    lib.canopy_set_wait_bound.argtypes = [i]
+    lib.canopy_set_wait_bound.restype = i
     lib.canopy_status_string.argtypes = [i]
     lib.canopy_status_string.restype = ctypes.c_char_p
     lib.canopy_tree_prep.argtypes = [P, P, P, i, i, i, P, P, P, P, u64]
@@ -108,6 +110,35 @@ def _req(t, name, dtype=None, shape=None):
     return t
 
 
+D = 128  # d_k = d_v: every kernel is built for 128-wide heads
+
+
+def _head_dim(d, name):
+    """Every kernel reads and writes 128-wide key and value rows; any other width is refused
+    before anything reaches the GPU."""
+    if d != D:
+        raise ValueError(f"{name} has head dimension {d}; libcanopy supports d_k = d_v = {D} only")
+
+
+def _outs(out, B, T, HV, dev):
+    """Preallocated (O, U, ell) for a verify: fp32 [B,T,HV,128] twice and fp32 [B,T,HV], on the
+    inputs' device and contiguous; new tensors when ``out`` is None."""
+    if out is None:
+        return (torch.empty((B, T, HV, D), dtype=torch.float32, device=dev),
+                torch.empty((B, T, HV, D), dtype=torch.float32, device=dev),
+                torch.empty((B, T, HV), dtype=torch.float32, device=dev))
+    if len(out) != 3:
+        raise ValueError("out must be a tuple (O, U, ell)")
+    O, U, ell = out
+    _req(O, "out O", torch.float32, (B, T, HV, D))
+    _req(U, "out U", torch.float32, (B, T, HV, D))
+    _req(ell, "out ell", torch.float32, (B, T, HV))
+    for name, t in (("out O", O), ("out U", U), ("out ell", ell)):
+        if t.device != dev:
+            raise ValueError(f"{name} is on {t.device}, the inputs on {dev}")
+    return O, U, ell
+
+
 def _tree_len(tree_len, B):
     return None if tree_len is None else _req(tree_len, "tree_len", torch.int32, (B,))
 
@@ -126,6 +157,13 @@ def _in_dtype(q):
     if q.dtype == torch.float32:
         return _FP32
     raise TypeError(f"q, k, v must be bfloat16 or float32, got {q.dtype}")
+
+
+def set_wait_bound(sleeps: int) -> int:
+    """Test hook: the bound (in sleeps) after which a wave stops waiting for another wave's
+    result in later launches of this process (negative: the default); returns the previous
+    bound. A wave that gives up writes NaN rows and tree status -2."""
+    return int(load().canopy_set_wait_bound(int(sleeps)))
 
 
 def tree_prep(parent, alpha, tree_len=None):
@@ -156,6 +194,7 @@ def tree_verify(q, k, v, alpha, beta, S0, parent, solver="auto", waves=0, struct
     count are left unwritten. With ``structure=True`` also returns the ancestor bitmask, depth
     and tree status. ``out`` may pass preallocated (O, U, ell)."""
     B, T, H, d = q.shape
+    _head_dim(d, "q")
     dt = _in_dtype(q)
     H, HV = _heads(q, v)
     for name, t in (("q", q), ("k", k)):
@@ -167,12 +206,7 @@ def tree_verify(q, k, v, alpha, beta, S0, parent, solver="auto", waves=0, struct
     _req(parent, "parent", torch.int32, (B, T))
     tl = _tree_len(tree_len, B)
     dev = q.device
-    if out is None:
-        O = torch.empty((B, T, HV, d), dtype=torch.float32, device=dev)
-        U = torch.empty((B, T, HV, d), dtype=torch.float32, device=dev)
-        ell = torch.empty((B, T, HV), dtype=torch.float32, device=dev)
-    else:
-        O, U, ell = out
+    O, U, ell = _outs(out, B, T, HV, dev)
     mask = depth = status = None
     if structure:
         mask = torch.empty((B, T, (T + 31) // 32), dtype=torch.int32, device=dev)
@@ -192,6 +226,7 @@ def commit(S0, k, U, alpha, parent, path, path_len, out=None, tree_len=None):
     an in-place commit) and the path status [B]. k is [B,T,H,128] with H dividing U's head
     count HV; ``tree_len`` as in ``tree_verify``."""
     B, T, H, d = k.shape
+    _head_dim(d, "k")
     dt = _in_dtype(k)
     H, HV = _heads(k, U)
     _req(S0, "S0", torch.float32, (B, HV, d, d))
@@ -219,6 +254,7 @@ def commit_verify(S0, k_prev, U_prev, alpha_prev, parent_prev, path, path_len, q
     also the ancestor bitmask, depth and tree status. ``S_out`` may be S0 (in place); ``out``
     may pass preallocated (O, U, ell), whose U may be U_prev when both trees have T rows."""
     B, T, H, d = q.shape
+    _head_dim(d, "q")
     Tp = k_prev.shape[1]
     dt = _in_dtype(q)
     H, HV = _heads(q, v)
@@ -240,12 +276,7 @@ def commit_verify(S0, k_prev, U_prev, alpha_prev, parent_prev, path, path_len, q
     dev = q.device
     S_new = torch.empty_like(S0) if S_out is None else _req(S_out, "S_out", torch.float32, (B, HV, d, d))
     pstatus = torch.empty((B,), dtype=torch.int32, device=dev)
-    if out is None:
-        O = torch.empty((B, T, HV, d), dtype=torch.float32, device=dev)
-        U = torch.empty((B, T, HV, d), dtype=torch.float32, device=dev)
-        ell = torch.empty((B, T, HV), dtype=torch.float32, device=dev)
-    else:
-        O, U, ell = out
+    O, U, ell = _outs(out, B, T, HV, dev)
     mask = depth = status = None
     if structure:
         mask = torch.empty((B, T, (T + 31) // 32), dtype=torch.int32, device=dev)
@@ -266,6 +297,7 @@ def serial_verify(q, k, v, alpha, beta, S0, parent, snapshots=None, tree_len=Non
     """The serial fork baseline: O, U [B,T,HV,128], every node's state snapshot
     [B,T,HV,128,128] and the tree status [B]. Heads and ``tree_len`` as in ``tree_verify``."""
     B, T, H, d = q.shape
+    _head_dim(d, "q")
     dt = _in_dtype(q)
     H, HV = _heads(q, v)
     for name, t in (("q", q), ("k", k)):
@@ -294,6 +326,7 @@ def hybrid_verify(q, k, v, alpha, beta, S0, parent, snapshots=None, tree_len=Non
     """The chain-decomposed hybrid: O, U [B,T,HV,128], the snapshot buffer [B,T,HV,128,128]
     (only fork nodes' rows written) and the tree status [B]. Arguments as ``serial_verify``."""
     B, T, H, d = q.shape
+    _head_dim(d, "q")
     dt = _in_dtype(q)
     H, HV = _heads(q, v)
     for name, t in (("q", q), ("k", k)):
@@ -322,6 +355,7 @@ def serial_commit(snapshots, S0, parent, path, path_len, out=None, tree_len=None
     """Serial baseline commit: the snapshot of each sequence's accepted node becomes S_new
     (``out`` may be S0 for an in-place commit); returns (S_new, path_status)."""
     B, T, H, d, _ = snapshots.shape
+    _head_dim(d, "snapshots")
     _req(snapshots, "snapshots", torch.float32, (B, T, H, d, d))
     _req(S0, "S0", torch.float32, (B, H, d, d))
     _req(parent, "parent", torch.int32, (B, T))
@@ -388,6 +422,7 @@ def commit_layers(S0s, ks, Us, alphas, parent, path, path_len, outs=None, tree_l
     assert len(ks) == len(Us) == len(alphas) == L
     k0 = ks[0]
     B, T, H, d = k0.shape
+    _head_dim(d, "k")
     dt = _in_dtype(k0)
     H, HV = _heads(k0, Us[0])
     for l in range(L):
@@ -415,6 +450,7 @@ def serial_commit_layers(snapshots, S0s, parent, path, path_len, outs=None, tree
     """``serial_commit`` for L layers in one launch; returns (list of S_new, path status)."""
     L = len(S0s)
     B, T, H, d, _ = snapshots[0].shape
+    _head_dim(d, "snapshots")
     for l in range(L):
         _req(snapshots[l], "snapshots", torch.float32, (B, T, H, d, d))
         _req(S0s[l], "S0", torch.float32, (B, H, d, d))
@@ -424,6 +460,8 @@ def serial_commit_layers(snapshots, S0s, parent, path, path_len, outs=None, tree
     tl = _tree_len(tree_len, B)
     if outs is None:
         outs = [torch.empty_like(s) for s in S0s]
+    for o in outs:
+        _req(o, "out", torch.float32, (B, H, d, d))
     status = torch.empty((B,), dtype=torch.int32, device=parent.device)
     _check(load().canopy_serial_commit_layers(L, _ptr_array(snapshots), _ptr_array(S0s), _ptr(parent),
                                               _ptr(tl), _ptr(path), _ptr(path_len), B, H, T,

@@ -1,5 +1,7 @@
 // The C ABI of libcanopy (declared in include/canopy.h): host-side argument checks, the launch
 // configuration, and nothing else. Every call only enqueues kernels on the caller's stream.
+#include <atomic>
+
 #include "canopy_device.hpp"
 #include "canopy_kernels.hpp"
 
@@ -16,6 +18,9 @@ bool sizes_ok(int B, int H, int T) {
 
 // q/k heads H and value heads HV: each q/k head serves HV / H value heads.
 bool heads_ok(int H, int HV) { return H >= 1 && HV >= H && HV % H == 0; }
+
+// Bound of the waits of one wave for another wave's result (see canopy_set_wait_bound).
+std::atomic<int> g_wait_bound{kWaitBound};
 
 canopy_status from_hip(hipError_t e) { return e == hipSuccess ? CANOPY_OK : CANOPY_ERR_HIP; }
 
@@ -37,7 +42,11 @@ constexpr long long kWideMaxHeads = 64;
 
 extern "C" {
 
-int canopy_version(void) { return 100; }
+int canopy_version(void) { return 200; }
+
+int canopy_set_wait_bound(int sleeps) {
+    return g_wait_bound.exchange(sleeps < 0 ? kWaitBound : sleeps, std::memory_order_relaxed);
+}
 
 const char *canopy_status_string(canopy_status s) {
     switch (s) {
@@ -81,6 +90,7 @@ canopy_status canopy_tree_verify(const void *q, const void *k, const void *v,
     a.solver = solver;
     a.O = O; a.U = U; a.ell = ell;
     a.anc_mask = anc_mask; a.depth = depth; a.tree_status = tree_status;
+    a.wait_bound = g_wait_bound.load(std::memory_order_relaxed);
     // Trees of at most 16 nodes fit one MFMA tile: AUTO and NEUMANN run the single-wave
     // register kernel (Neumann series in registers). Trees of 17 to 64 nodes run the
     // wave-per-sub-block kernel for AUTO, FWDSUB and NEUMANN. Everything else (LEVEL, and
@@ -160,6 +170,7 @@ canopy_status canopy_commit_verify(const float *S0, const void *k_prev, const fl
         a.solver = solver;
         a.O = O; a.U = U; a.ell = ell;
         a.anc_mask = anc_mask; a.depth = depth; a.tree_status = tree_status;
+        a.wait_bound = g_wait_bound.load(std::memory_order_relaxed);
         const PrevCommitArgs c{k_prev, U_prev, alpha_prev, parent_prev, tree_len_prev, path,
                                path_len, T_prev, S_new, path_status};
         if (small) return from_hip(launch_commit_verify_small(a, c, waves, stream));
@@ -215,7 +226,7 @@ canopy_status canopy_serial_verify(const void *q, const void *k, const void *v,
         return CANOPY_ERR_ARG;
     if (in_dtype != CANOPY_FP32 && in_dtype != CANOPY_BF16) return CANOPY_ERR_UNSUPPORTED;
     SerialArgs a{q, k, v, alpha, beta, S0, parent, tree_len, B, HV, H, T, in_dtype == CANOPY_BF16,
-                 O, U, snapshots, tree_status};
+                 O, U, snapshots, tree_status, g_wait_bound.load(std::memory_order_relaxed)};
     return from_hip(launch_serial(a, stream));
 }
 
@@ -231,7 +242,7 @@ canopy_status canopy_hybrid_verify(const void *q, const void *k, const void *v,
         return CANOPY_ERR_ARG;
     if (in_dtype != CANOPY_FP32 && in_dtype != CANOPY_BF16) return CANOPY_ERR_UNSUPPORTED;
     SerialArgs a{q, k, v, alpha, beta, S0, parent, tree_len, B, HV, H, T, in_dtype == CANOPY_BF16,
-                 O, U, snapshots, tree_status};
+                 O, U, snapshots, tree_status, g_wait_bound.load(std::memory_order_relaxed)};
     return from_hip(launch_hybrid(a, stream));
 }
 

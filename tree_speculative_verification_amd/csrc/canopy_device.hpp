@@ -50,6 +50,36 @@ __device__ __forceinline__ int wave_max(int x) {
     return x;
 }
 
+// Tree status of a sequence in which a wave gave up waiting for a result that another wave of
+// its workgroup publishes (never expected: see wait_flag).
+constexpr int kStatusHandoffLost = -2;
+// Default bound, in sleeps, of such a wait.
+constexpr int kWaitBound = 1 << 24;
+
+// Wait for a flag that another wave of the workgroup sets with a release store: 1 when its
+// result is published, 2 when the publisher itself computed from a lost hand-off. Every wave
+// of a workgroup is resident and no publisher waits for a wave that waits for it, so the flag
+// is always set; the bound (in sleeps) only guarantees that the wait ends. Returns the flag, or
+// 0 when the bound ran out; the value is the same in every lane (the acquire load reads one
+// LDS word for the whole wave).
+__device__ __forceinline__ int wait_flag(int *flag, int bound) {
+    for (int n = 0; n < bound; ++n) {
+        const int v = __builtin_amdgcn_readfirstlane(
+            __hip_atomic_load(flag, __ATOMIC_ACQUIRE, __HIP_MEMORY_SCOPE_WORKGROUP));
+        if (v != 0) return v;
+        __builtin_amdgcn_s_sleep(1);
+    }
+    return 0;
+}
+
+// Record a lost hand-off of sequence b in tree_status (if given). The sequence's own status
+// store (0 for a valid tree) comes right after its tree preprocessing; a lost hand-off is only
+// known after a full wait bound, so this store lands after it.
+__device__ __forceinline__ void report_lost(int32_t *tree_status, int b) {
+    if (tree_status)
+        __hip_atomic_store(tree_status + b, kStatusHandoffLost, __ATOMIC_RELAXED, __HIP_MEMORY_SCOPE_AGENT);
+}
+
 // Blocks of a launch are spread round-robin over the 8 XCDs (each with its own L2). Map the
 // hardware block id so that consecutive logical ids run on one XCD: logical ids that share a
 // (batch, head) then share that XCD's L2 copy of its keys and queries.

@@ -19,6 +19,7 @@ struct VerifyArgs {
     float *O, *U, *ell;
     uint32_t *anc_mask;
     int32_t *depth, *tree_status;
+    int wait_bound;  // sleeps before a wave gives up waiting for another wave's result
 };
 
 struct PrepArgs {
@@ -62,6 +63,7 @@ struct SerialArgs {
     int bf16;
     float *O, *U, *snap;
     int32_t *tree_status;
+    int wait_bound;  // as in VerifyArgs
 };
 
 struct SerialCommitArgs {

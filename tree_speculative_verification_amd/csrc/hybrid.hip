@@ -20,17 +20,6 @@ namespace canopy {
 
 constexpr int HMAXT = 256;
 
-// Spin (with sleeps) until another wave of the workgroup has published `flag` with a release
-// store; the acquire makes that wave's earlier stores visible. Every wave of a workgroup is
-// resident and the publisher never waits on this wave, so the wait ends; the bound only
-// guarantees exit.
-__device__ __forceinline__ void wait_ready(int *flag) {
-    for (int n = 0; n < (1 << 24); ++n) {
-        if (__hip_atomic_load(flag, __ATOMIC_ACQUIRE, __HIP_MEMORY_SCOPE_WORKGROUP) != 0) return;
-        __builtin_amdgcn_s_sleep(1);
-    }
-}
-
 template <bool BF, int NW>
 __global__ __launch_bounds__(NW * 64) void hybrid_kernel(SerialArgs a) {
     constexpr int NT = NW * 64, TILES = D / 16;
@@ -151,7 +140,10 @@ __global__ __launch_bounds__(NW * 64) void hybrid_kernel(SerialArgs a) {
         load_node<BF>(cur, a.q, a.k, qkbase + static_cast<size_t>(node) * qkrs, rg, a.v,
                       base + static_cast<size_t>(node) * rs + col, a.alpha, a.beta,
                       sbase + static_cast<size_t>(node) * H);
-        if (p >= 0) wait_ready(&s_ready[p]);
+        // a chain whose starting snapshot never came (or came from such a chain) is lost: its
+        // nodes get NaN outputs and its forks pass the loss on
+        const bool lost = p >= 0 && wait_flag(&s_ready[p], a.wait_bound) != 1;
+        if (lost && lane == 0) report_lost(a.tree_status, b);
         // ---- one chain from head: state from the parent's snapshot (or S0)
         const float *src = (p < 0) ? a.S0 + static_cast<size_t>(bh) * SS
                                    : a.snap + ((static_cast<size_t>(b) * T + p) * H + h) * SS;
@@ -171,15 +163,17 @@ __global__ __launch_bounds__(NW * 64) void hybrid_kernel(SerialArgs a) {
             gdn_step(S, cur, o, u);
             const size_t nodeo = base + static_cast<size_t>(node) * rs + col;
             if (rg == 0) {
-                reinterpret_cast<float4 *>(a.O + nodeo)[0] = o;
-                reinterpret_cast<float4 *>(a.U + nodeo)[0] = u;
+                const float qnan = __builtin_nanf("");
+                const float4 nan4 = make_float4(qnan, qnan, qnan, qnan);
+                reinterpret_cast<float4 *>(a.O + nodeo)[0] = lost ? nan4 : o;
+                reinterpret_cast<float4 *>(a.U + nodeo)[0] = lost ? nan4 : u;
             }
             if (s_nch[node] >= 2) {  // a fork: light chains start from this state
                 float *dst = a.snap + ((static_cast<size_t>(b) * T + node) * H + h) * SS;
 #pragma unroll
                 for (int m = 0; m < 8; ++m) reinterpret_cast<float4 *>(dst + (rg + 16 * m) * D + col)[0] = S[m];
                 // the snapshot is written before the flag that lets other waves read it
-                __hip_atomic_store(&s_ready[node], 1, __ATOMIC_RELEASE, __HIP_MEMORY_SCOPE_WORKGROUP);
+                __hip_atomic_store(&s_ready[node], lost ? 2 : 1, __ATOMIC_RELEASE, __HIP_MEMORY_SCOPE_WORKGROUP);
             }
             cur = nin;
             node = nxt;

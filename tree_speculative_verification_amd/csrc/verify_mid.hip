@@ -56,15 +56,6 @@ struct MidSmem {
     int ready[NSB];  // forward substitution: U_s is in x[0][s]
 };
 
-// Spin (with sleeps) until another wave of the workgroup has published `flag`. Every wave of a
-// workgroup is resident, so the publisher always progresses; the bound only guarantees exit.
-__device__ __forceinline__ void wait_lds_flag(int *flag) {
-    for (int n = 0; n < (1 << 24); ++n) {
-        if (__hip_atomic_load(flag, __ATOMIC_ACQUIRE, __HIP_MEMORY_SCOPE_WORKGROUP) != 0) return;
-        __builtin_amdgcn_s_sleep(1);
-    }
-}
-
 // Fused commit: for path positions first .. first+CG-1 (node 0 past the path, whose finite
 // values meet a zero weight), the key values at rows 8kc .. 8kc+7 and the U entry at column cc
 // of each (column, row chunk) pair m of this thread.
@@ -432,6 +423,7 @@ __global__ __launch_bounds__(64 * NSB) void verify_mid_kernel(VerifyArgs a, Prev
 
     const float qnan = __builtin_nanf("");
     float u[NCT][4];
+    bool lost = false;  // a result this wave waited for never came (or came from a lost wait)
     if (a.solver != CANOPY_SOLVE_NEUMANN) {
         // ---- a4, forward substitution. The diagonal inverse (I + G_pp)^-1 in the A placement,
         // as the product of the ceil(log2(dp + 1)) factors (I + N^(2^s)), N = -G_pp: each power
@@ -473,7 +465,7 @@ __global__ __launch_bounds__(64 * NSB) void verify_mid_kernel(VerifyArgs a, Prev
 #pragma unroll
         for (int s = 0; s < NSB; ++s) {
             if (s >= p) break;
-            wait_lds_flag(&sm.ready[s]);
+            lost |= wait_flag(&sm.ready[s], a.wait_bound) != 1;
 #pragma unroll
             for (int ct = 0; ct < NCT; ++ct) {
                 const float4 t = sm.u.x[0][s][ct][lane];
@@ -490,7 +482,7 @@ __global__ __launch_bounds__(64 * NSB) void verify_mid_kernel(VerifyArgs a, Prev
             for (int e = 0; e < 4; ++e) u[ct][e] = y[e];
             sm.u.x[0][p][ct][lane] = make_float4(u[ct][0], u[ct][1], u[ct][2], u[ct][3]);
         }
-        __hip_atomic_store(&sm.ready[p], 1, __ATOMIC_RELEASE, __HIP_MEMORY_SCOPE_WORKGROUP);
+        __hip_atomic_store(&sm.ready[p], lost ? 2 : 1, __ATOMIC_RELEASE, __HIP_MEMORY_SCOPE_WORKGROUP);
 #pragma unroll
         for (int ct = 0; ct < NCT; ++ct) {
             oacc[ct] = mma16f(cdiag, u[ct], oacc[ct]);
@@ -551,7 +543,9 @@ __global__ __launch_bounds__(64 * NSB) void verify_mid_kernel(VerifyArgs a, Prev
         }
     }
 
-    // ---- a6: outputs (NaN for a malformed tree)
+    // ---- a6: outputs (NaN for a malformed tree and for rows computed from a lost hand-off)
+    if (lost && lane == 0) report_lost(a.tree_status, b);
+    const bool nanout = bad || lost;
 #pragma unroll
     for (int ct = 0; ct < NCT; ++ct)
 #pragma unroll
@@ -559,8 +553,8 @@ __global__ __launch_bounds__(64 * NSB) void verify_mid_kernel(VerifyArgs a, Prev
             const int i = 16 * p + 4 * lg + e;
             if (i < Tb) {
                 const size_t o = base + static_cast<size_t>(i) * rs + colw + 16 * ct + lr;
-                a.U[o] = bad ? qnan : u[ct][e];
-                store_nt(a.O + o, bad ? qnan : oacc[ct][e]);
+                a.U[o] = nanout ? qnan : u[ct][e];
+                store_nt(a.O + o, nanout ? qnan : oacc[ct][e]);
             }
         }
 }

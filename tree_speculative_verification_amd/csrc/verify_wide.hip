@@ -45,13 +45,6 @@ struct WideSmem {
     int bad;
 };
 
-__device__ __forceinline__ void wide_wait_flag(int *flag) {
-    for (int n = 0; n < (1 << 24); ++n) {
-        if (__hip_atomic_load(flag, __ATOMIC_ACQUIRE, __HIP_MEMORY_SCOPE_WORKGROUP) != 0) return;
-        __builtin_amdgcn_s_sleep(1);
-    }
-}
-
 // One Gram tile (p, c): lane (lg, lr) gets row i = 16p + lr and columns j = 16c + 4lg + e of
 // -G (strict ancestors) and C (path), from K_c (A operand, LDS) and the wave's K_p, Q_p.
 template <int NCT>
@@ -336,6 +329,7 @@ __global__ __launch_bounds__(1024) void verify_wide_kernel(VerifyArgs a) {
             for (int e = 0; e < 4; ++e) minv[e] = mi[e];
         }
     }
+    bool lost = false;  // a result this wave waited for never came (or came from a lost wait)
     // The tile needed last, (p, p-1), first; then the others in the order the U_s arrive.
     float glast[4] = {0.f, 0.f, 0.f, 0.f}, clast[4] = {0.f, 0.f, 0.f, 0.f};
     if (p >= 1) {
@@ -354,7 +348,7 @@ __global__ __launch_bounds__(1024) void verify_wide_kernel(VerifyArgs a) {
                 cm[e] = clast[e];
             }
         }
-        wide_wait_flag(&sm.ready[s]);
+        lost |= wait_flag(&sm.ready[s], a.wait_bound) != 1;
 #pragma unroll
         for (int ct = 0; ct < NCT; ++ct) {
             const float4 t = sm.u.x[s][ct][lane];
@@ -373,7 +367,7 @@ __global__ __launch_bounds__(1024) void verify_wide_kernel(VerifyArgs a) {
         for (int e = 0; e < 4; ++e) u[ct][e] = y[e];
         sm.u.x[p][ct][lane] = make_float4(u[ct][0], u[ct][1], u[ct][2], u[ct][3]);
     }
-    __hip_atomic_store(&sm.ready[p], 1, __ATOMIC_RELEASE, __HIP_MEMORY_SCOPE_WORKGROUP);
+    __hip_atomic_store(&sm.ready[p], lost ? 2 : 1, __ATOMIC_RELEASE, __HIP_MEMORY_SCOPE_WORKGROUP);
     // ---- a5: the read-out terms left: the last incoming tile and the wave's own
 #pragma unroll
     for (int ct = 0; ct < NCT; ++ct) {
@@ -385,8 +379,10 @@ __global__ __launch_bounds__(1024) void verify_wide_kernel(VerifyArgs a) {
         oacc[ct] = mma16f(cdiag, u[ct], oacc[ct]);
     }
 
-    // ---- a6: outputs (NaN for a malformed tree)
+    // ---- a6: outputs (NaN for a malformed tree and for rows computed from a lost hand-off)
     const float qnan = __builtin_nanf("");
+    if (lost && lane == 0) report_lost(a.tree_status, b);
+    const bool nanout = bad || lost;
 #pragma unroll
     for (int ct = 0; ct < NCT; ++ct)
 #pragma unroll
@@ -394,8 +390,8 @@ __global__ __launch_bounds__(1024) void verify_wide_kernel(VerifyArgs a) {
             const int i = 16 * p + 4 * lg + e;
             if (i < Tb) {
                 const size_t o = base + static_cast<size_t>(i) * rs + colw + 16 * ct + lr;
-                a.U[o] = bad ? qnan : u[ct][e];
-                store_nt(a.O + o, bad ? qnan : oacc[ct][e]);
+                a.U[o] = nanout ? qnan : u[ct][e];
+                store_nt(a.O + o, nanout ? qnan : oacc[ct][e]);
             }
         }
     (void)nsb;
