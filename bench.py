@@ -49,6 +49,11 @@ WORKLOADS = {
     "random256_b16": dict(B=16, H=32, T=256, tree="random", dtype="bf16", seed=3,
                           desc="B=16 H=32 T=256 random recursive trees, bf16 q/k/v, fp32 S0"),
 }
+WORKLOADS["topk16_b16"] = dict(B=16, H=32, T=16, tree="topk", tree_kw={"branching": (3, 4)}, dtype="bf16",
+                              seed=1, desc="B=16 H=32 T=16 top-k trees 1+3+12, bf16 q/k/v, fp32 S0")
+DEFAULT_WORKLOAD = "topk16_b1"
+# Timed beside the default workload in every default run.
+EXTRA_WORKLOADS = ("random256_b16", "topk16_b16")
 # Grouped value heads ("Qwen3.5-9B shapes": 16 q/k heads serving 32 value heads) and a ragged
 # batch (each sequence's own node count, drawn uniformly from the given range).
 WORKLOADS["topk16_b1_hk16"] = dict(B=1, H=32, HK=16, T=16, tree="topk", tree_kw={"branching": (3, 4)},
@@ -103,6 +108,8 @@ def one_launch_step(T, solver, heads=32, waves=0):
     """Whether canopy_commit_verify runs the step as one launch (after previous trees of at most
     64 nodes): trees of at most 16 nodes (AUTO, NEUMANN), and trees of 17 to 64 nodes (not
     LEVEL) whose workgroups hold at most 2 state pairs per thread (4 * tiles <= 2 * sub-blocks)."""
+    if solver in ("series", "squaring", "split"):
+        return False
     if T <= 16:
         return solver in ("auto", "neumann")
     if T <= 64 and solver != "level":
@@ -124,22 +131,55 @@ def verify_flops_ragged(H, lens):
 
 
 def verify_flops(B, H, T):
-    """Algorithmic matrix flops of one verify launch, counting the Gram, solve and read-out
-    matrices as dense lower triangles (a tree's ancestor pattern is sparser): per (sequence,
-    head) the projections K S0 and Q S0 (4 T d^2), the strict and inclusive Gram triangles
-    (2 d T^2 together), the triangular solve and the C U read-out (2 d T^2 together)."""
+    """Dense-triangle matrix flops of one verify launch: the Gram, solve and read-out matrices
+    counted as whole lower triangles, as a tiled kernel issues them (a tree's ancestor pattern
+    is sparser, so this is not the method's count): per (sequence, head) the projections K S0
+    and Q S0 (4 T d^2), the strict and inclusive Gram triangles (2 d T^2 together), the
+    triangular solve and the C U read-out (2 d T^2 together)."""
     d = 128
     return B * H * (4 * T * d * d + 4 * d * T * T)
 
 
+def ancestor_pairs(parent, n=None):
+    """|A| = sum over the first n nodes of |A(i)|, the number of (node, strict ancestor) pairs
+    (depth by the parent walk, parents before children)."""
+    n = len(parent) if n is None else int(n)
+    depth = [0] * n
+    for i in range(n):
+        p = int(parent[i])
+        depth[i] = depth[p] + 1 if p >= 0 else 0
+    return sum(depth)
+
+
+def method_flops(parents, H, lens=None):
+    """The method's own matrix flops for one verify launch, from each tree's ancestor pairs:
+    per (sequence, head) the projections K S0 and Q S0 (4 T d^2), G over strict ancestors
+    (2 |A| d), C over paths (2 (|A| + T) d), the substitution over strict ancestors (2 |A| d)
+    and the read-out over paths (2 (|A| + T) d)."""
+    d = 128
+    tot = 0
+    for b, par in enumerate(parents):
+        n = len(par) if lens is None else int(lens[b])
+        A = ancestor_pairs(par, n)
+        tot += 4 * n * d * d + 8 * A * d + 4 * n * d
+    return H * tot
+
+
+def commit_flops(H, m_total):
+    """Flops of the commit's rank-m update: 2 d^2 per path node and head."""
+    return H * 2 * 128 * 128 * m_total
+
+
 def verify_kernel_name(T, solver, heads=0, waves=0, dtype="bf16"):
     """The kernel canopy_tree_verify launches for this size, solver, head count and width."""
+    if solver in ("series", "squaring", "split"):
+        return "mat_apply_kernel"
     if T <= 16 and solver in ("auto", "neumann"):
         return "verify_small_kernel"
     if 16 < T <= 64 and solver != "level":
         return "verify_mid_kernel"
     if T > 64 and dtype == "bf16" and solver in ("auto", "fwdsub"):
-        if waves in (1, 2) or (waves == 0 and heads <= 64):
+        if waves in (1, 2) or (waves == 0 and heads <= 128):
             return "verify_wide_kernel"
     return "verify_kernel"
 
@@ -276,6 +316,53 @@ def run_solver_sweep(args):
     return 0
 
 
+def run_depth_sweep(args):
+    """The solve strategies across tree depths 1-255 at T = 256 (level trees: a root, then
+    levels of W nodes, depth ceil(255 / W)): verify µs at each of --batches. Solvers: AUTO
+    (forward substitution in the fused kernels), NEUMANN (per 64-node block in the blocked
+    kernel), the whole-tree series, its squaring form and the split design. One JSON line per
+    (depth, B); ``--out`` appends them to a file. (Their bf16 errors against the oracle on the
+    same trees are a GPU test: test_gpu_matrix_solvers.py::test_errors_by_depth.)"""
+    import torch
+    import synth
+    import tree_speculative_verification_amd as tsv
+    tsv.load()
+    T = 256
+    solvers = ("auto", "neumann", "series", "squaring", "split")
+    lines = []
+    for W in (255, 128, 64, 32, 16, 8, 4, 2, 1):
+        par = synth.level_tree(T, W)
+        depth = int(synth.tree_depths(par).max())
+        for B in args.batches:
+            inp = synth.make_inputs(B, 32, T, dtype="bf16", seed=11, parents=par)
+            d = to_device(inp)
+            res = {}
+            for sv in solvers:
+                ws = None
+                if sv in tsv.WORKSPACE_SOLVERS:
+                    ws = torch.empty((tsv.workspace_bytes(B, 32, T, sv),), dtype=torch.uint8, device="cuda")
+                O = torch.empty((B, T, 32, 128), device="cuda")
+                U = torch.empty_like(O)
+                L = torch.empty((B, T, 32), device="cuda")
+                fn = lambda: tsv.tree_verify(d["q"], d["k"], d["v"], d["alpha"], d["beta"], d["S0"],
+                                             d["parent"], solver=sv, out=(O, U, L), workspace=ws)
+                fn()
+                torch.cuda.synchronize()
+                n = max(3, min(args.steps, 20))
+                g = graph_of(fn, n)
+                res[sv] = round(min(time_graph(g, n) for _ in range(2)), 3)
+                del g, ws, O, U, L
+            line = dict(T=T, W=W, depth=depth, B=B, H=32, us=res,
+                        best=min((v, k) for k, v in res.items())[1])
+            print(json.dumps(line), flush=True)
+            lines.append(line)
+    if args.out:
+        with open(args.out, "a") as fh:
+            for line in lines:
+                fh.write(json.dumps(line) + "\n")
+    return 0
+
+
 def run_conv(args):
     """The root-path causal convolution (kernel 4, SiLU) and its state commit on the workload's
     trees, over the channels a GDN layer convolves: q and k of its q/k heads and v of its value
@@ -367,14 +454,23 @@ def graph_of(fn, n):
     return g
 
 
+# Shader clocks of the spin kernel that holds the stream before a timed graph replay (about
+# 80 µs at 2.4 GHz, longer than the host takes to submit a graph of a few hundred launches).
+HOLD_CYCLES = 200_000
+
+
 def time_graph(g, n):
     """Average µs per call of a graph of n calls: one replay between two events on the stream
-    the replay runs on, synchronised on both sides."""
+    the replay runs on, synchronised on both sides. A spin kernel ahead of the first event
+    holds the stream while the host submits the graph's launches, so that the events bracket
+    the n calls running back to back on the GPU and not the host's submission of the first
+    ones (with a graph of 20 steps of about 5 µs, the submission alone added 0.5 µs per step)."""
     import torch
     g.replay()  # warm replay
     torch.cuda.synchronize()
     e0 = torch.cuda.Event(enable_timing=True)
     e1 = torch.cuda.Event(enable_timing=True)
+    torch.cuda._sleep(HOLD_CYCLES)
     e0.record()
     g.replay()
     e1.record()
@@ -839,8 +935,11 @@ def main(argv=None):
     ap.add_argument("--gpus", type=int, default=1)
     ap.add_argument("--steps", type=int, default=200)
     ap.add_argument("--warmup", type=int, default=25)
-    ap.add_argument("--workload", default="topk16_b1", choices=sorted(WORKLOADS))
-    ap.add_argument("--solver", default="auto", choices=["auto", "fwdsub", "neumann", "level"])
+    ap.add_argument("--workload", default=DEFAULT_WORKLOAD, choices=sorted(WORKLOADS))
+    ap.add_argument("--no-extra", action="store_true",
+                    help="the default workload only (without the B=16 workloads beside it)")
+    ap.add_argument("--solver", default="auto",
+                    choices=["auto", "fwdsub", "neumann", "level", "series", "squaring", "split"])
     ap.add_argument("--waves", type=int, default=0)
     ap.add_argument("--no-cpu", action="store_true", help="skip the oracle CPU baseline")
     ap.add_argument("--no-serial", action="store_true", help="skip the serial fork baseline")
@@ -852,6 +951,8 @@ def main(argv=None):
     ap.add_argument("--rounds", type=int, default=100, help="crossover: rounds per cell")
     ap.add_argument("--solver-sweep", action="store_true",
                     help="time every solver on level trees over T, width and --batches")
+    ap.add_argument("--depth-sweep", action="store_true",
+                    help="time and check every solve strategy over tree depths 1-255 at T=256")
     ap.add_argument("--conv", action="store_true",
                     help="time the root-path causal convolution and its commit instead")
     ap.add_argument("--protocol", action="store_true",
@@ -892,28 +993,75 @@ def main(argv=None):
         return run_conv(args)
     if args.solver_sweep:
         return run_solver_sweep(args)
+    if args.depth_sweep:
+        return run_depth_sweep(args)
     if args.protocol:
         return run_protocol(args)
     if args.peaks:
         return run_peaks(args)
 
+    rec = measure(args.workload, args, baselines=not args.no_serial)
+    primary = args.workload == DEFAULT_WORKLOAD and not args.no_extra
+    out = {
+        "metric": METRIC,
+        "value": rec["step_us"],
+        "unit": "us",
+        "n_gpus": 1,
+        "steps": args.steps,
+        "warmup": args.warmup,
+        "ms_per_step": round(rec["step_us"] / 1000.0, 6),
+        "higher_is_better": False,
+        "scaling": "weak",
+        "vs_baseline": None,
+        "dtype": rec.pop("dtype"),
+        "data": "synthetic",
+    }
+    out.update(rec)
+    out["kernel_digest"] = kernel_digest()
+    if primary:
+        # The other workloads the targets name, timed the same way in the same run: the
+        # 256-node trees at B=16 (the MFMA target's configuration) and 16-node trees at B=16
+        # (the HBM target's tree size at a batch that can fill the GPU).
+        out["extra_workloads"] = []
+        for key in EXTRA_WORKLOADS:
+            r = measure(key, args, baselines=False)
+            r.pop("dtype")
+            out["extra_workloads"].append(r)
+    if not args.no_cpu:
+        out["cpu_baseline"] = cpu_baseline(build_inputs(WORKLOADS[args.workload]), args.cpu_budget)
+    print(json.dumps(out), flush=True)
+    return 0
+
+
+def measure(key, args, baselines=True):
+    """Time one workload's decode step (exactly args.steps steps after args.warmup), the same
+    work as separate calls, verify and commit alone and, with ``baselines``, the serial fork and
+    the chain hybrid; returns the record of the bench line for it."""
     import numpy as np
     import torch
     import tree_speculative_verification_amd as tsv
 
-    wl = WORKLOADS[args.workload]
+    wl = WORKLOADS[key]
     B, H, T, dt = wl["B"], wl["H"], wl["T"], wl["dtype"]
     inp = build_inputs(wl)
     d = to_device(inp)
     tsv.load()
+    print(f"[bench] {key}: inputs resident", file=sys.stderr, flush=True)
     O = torch.empty((B, T, H, 128), device="cuda")
     U = torch.empty_like(O)
     ell = torch.empty((B, T, H), device="cuda")
     S_new = torch.empty_like(d["S0"])
 
+    ws_solver = args.solver in tsv.WORKSPACE_SOLVERS
+    ws = None
+    if ws_solver:
+        ws = torch.empty((max(tsv.workspace_bytes(B, H, T, args.solver), 16),), dtype=torch.uint8,
+                         device="cuda")
+
     def verify():
         tsv.tree_verify(d["q"], d["k"], d["v"], d["alpha"], d["beta"], d["S0"], d["parent"],
-                        solver=args.solver, waves=args.waves, out=(O, U, ell), tree_len=d["tree_len"])
+                        solver=args.solver, waves=args.waves, out=(O, U, ell), tree_len=d["tree_len"],
+                        workspace=ws)
 
     def commit():
         tsv.commit(d["S0"], d["k"], U, d["alpha"], d["parent"], d["path"], d["path_len"], out=S_new,
@@ -931,6 +1079,14 @@ def main(argv=None):
     ell_run = torch.empty_like(ell)
 
     def step():
+        if ws_solver:
+            # the matrix forms: the commit, then the verify from the committed state
+            tsv.commit(S_run, d["k"], U_run, d["alpha"], d["parent"], d["path"], d["path_len"],
+                       out=S_run, tree_len=d["tree_len"])
+            tsv.tree_verify(d["q"], d["k"], d["v"], d["alpha"], d["beta"], S_run, d["parent"],
+                            solver=args.solver, out=(O_run, U_run, ell_run), tree_len=d["tree_len"],
+                            workspace=ws)
+            return
         tsv.commit_verify(S_run, d["k"], U_run, d["alpha"], d["parent"], d["path"], d["path_len"],
                           d["q"], d["k"], d["v"], d["alpha"], d["beta"], d["parent"],
                           solver=args.solver, waves=args.waves, out=(O_run, U_run, ell_run),
@@ -942,7 +1098,7 @@ def main(argv=None):
     ref_O, ref_U, ref_S = O.clone(), U.clone(), S_new.clone()
     tsv.tree_verify(d["q"], d["k"], d["v"], d["alpha"], d["beta"], S_run, d["parent"],
                     solver=args.solver, waves=args.waves, out=(O_run, U_run, ell_run),
-                    tree_len=d["tree_len"])
+                    tree_len=d["tree_len"], workspace=ws)
     for _ in range(args.warmup):
         step()
     torch.cuda.synchronize()
@@ -990,7 +1146,7 @@ def main(argv=None):
     if not bool(torch.isfinite(S_run).all()):
         raise RuntimeError("the carried state is not finite")
     us_serial = us_hybrid = None
-    if not args.no_serial:
+    if baselines:
         snaps = torch.empty((B, T, H, 128, 128), device="cuda")
 
         def serial():
@@ -1021,40 +1177,33 @@ def main(argv=None):
         dst.copy_(src)
         torch.cuda.synchronize()
         del src, dst
+    print(f"[bench] {key}: step {us_step:.3f} us", file=sys.stderr, flush=True)
 
     HK = wl.get("HK", H)
     lens = inp["tree_len"] if inp.get("tree_len") is not None else np.full(B, T)
     nodes = int(lens.sum())
+    m_total = int(inp["path_len"].sum())
     vbytes = verify_bytes(B, H, T, dt, HK=HK, nodes=nodes)
-    vflops = verify_flops_ragged(H, lens)
+    vflops = method_flops(inp["parent"], H, lens)
+    vdense = verify_flops_ragged(H, lens)
     one = one_launch_step(T, args.solver, B * H, args.waves)
     if one:
         # the dominant (only) kernel of the step: commit + verify in one launch per step
-        m_total = int(inp["path_len"].sum())
         rbytes = fused_step_bytes(B, H, T, dt, m_total, HK=HK, nodes=nodes)
-        rflops = vflops + H * 2 * 128 * 128 * m_total
+        rflops = vflops + commit_flops(H, m_total)
+        rdense = vdense + commit_flops(H, m_total)
         r_us, r_kernel, r_role = us_step, fused_kernel_name(T, dt, B * H, args.waves), "fused"
-        r_note = "one launch per step (commit + verify): algorithmic bytes and flops of both"
+        r_note = ("one launch per step (commit + verify): the method's flops of both, from the "
+                  "trees' ancestor pairs and the accepted paths")
     else:
-        rbytes, rflops, r_us, r_role = vbytes, vflops, us_verify, "verify"
+        rbytes, rflops, rdense, r_us, r_role = vbytes, vflops, vdense, us_verify, "verify"
         r_kernel = verify_kernel_name(T, args.solver, B * H, args.waves, dt)
-        r_note = "algorithmic dense-triangle flops of the verify launch"
+        r_note = "the verify launch: the method's flops from the trees' ancestor pairs"
     achieved = rbytes / (r_us * 1e-6) / 1e9
     tflops = rflops / (r_us * 1e-6) / 1e12
-    out = {
-        "metric": METRIC,
-        "value": round(us_step, 3),
-        "unit": "us",
-        "n_gpus": 1,
-        "steps": args.steps,
-        "warmup": args.warmup,
-        "ms_per_step": round(us_step / 1000.0, 6),
-        "higher_is_better": False,
-        "scaling": "weak",
-        "vs_baseline": None,
+    return {
         "dtype": "bf16" if dt == "bf16" else "fp32",
-        "data": "synthetic",
-        "config": {"workload": wl["desc"], "workload_key": args.workload, "B": B, "H": H, "T": T,
+        "config": {"workload": wl["desc"], "workload_key": key, "B": B, "H": H, "T": T,
                    "q_k_heads": HK, "nodes": nodes, "dk": 128, "dv": 128, "tree": wl["tree"],
                    "solver": args.solver,
                    "waves": args.waves,
@@ -1063,6 +1212,7 @@ def main(argv=None):
                             "(canopy_commit_verify, %s)" % ("one launch" if one else "two launches")),
                    "launch": "eager" if args.eager else "hip graph of all timed steps",
                    "copy_probe_bytes": args.copy_probe},
+        "step_us": round(us_step, 3),
         "nodes_per_s": round(nodes / (us_step * 1e-6), 1),
         "separate_step_us": round(us_sep, 3),
         "verify_us": round(us_verify, 3),
@@ -1073,18 +1223,15 @@ def main(argv=None):
         "roofline": {"bound": "hbm", "kernel": r_kernel,
                      "achieved": round(achieved, 2), "peak": HBM_PEAK_GBS, "unit": "GB/s",
                      "frac": round(achieved / HBM_PEAK_GBS, 5),
-                     "traffic": measured_traffic(args.workload, args.solver, args.waves, r_role),
+                     "traffic": measured_traffic(key, args.solver, args.waves, r_role),
                      "algorithmic_bytes": rbytes, "launch_us": round(r_us, 3)},
         "verify_algorithmic_bytes": vbytes,
-        "mfma": {"flops_per_launch": rflops, "achieved_tflops": round(tflops, 2),
+        "mfma": {"flops_per_launch": rflops, "achieved_tflops": round(tflops, 3),
                  "peak_tflops": BF16_PEAK_TFLOPS, "frac": round(tflops / BF16_PEAK_TFLOPS, 5),
+                 "issued_dense_flops": rdense,
+                 "issued_dense_frac": round(rdense / (r_us * 1e-6) / 1e12 / BF16_PEAK_TFLOPS, 5),
                  "note": r_note},
-        "kernel_digest": kernel_digest(),
     }
-    if not args.no_cpu:
-        out["cpu_baseline"] = cpu_baseline(inp, args.cpu_budget)
-    print(json.dumps(out), flush=True)
-    return 0
 
 
 if __name__ == "__main__":

@@ -56,6 +56,7 @@ typedef enum {
     CANOPY_OK = 0,
     CANOPY_ERR_ARG = 1,         /* null required pointer or a size out of range */
     CANOPY_ERR_UNSUPPORTED = 2, /* dtype, solver or waves value not supported */
+    CANOPY_ERR_WORKSPACE = 3,   /* workspace missing, misaligned or smaller than required */
     CANOPY_ERR_HIP = 4          /* the HIP runtime reported a launch error */
 } canopy_status;
 
@@ -70,9 +71,9 @@ typedef enum { CANOPY_FP32 = 0, CANOPY_BF16 = 1 } canopy_dtype;
  *    substitute forward over the sub-blocks, each 16 x 16 diagonal inverse formed as the
  *    squaring product (I + N)(I + N^2)(I + N^4)(I + N^8), N = -G_pp, truncated at the
  *    sub-block's depth; NEUMANN sums the whole tree's series, one term per tree level.
- *  - 65 <= T <= 256 with bf16 inputs (AUTO, FWDSUB), for at most 64 (sequence, head) pairs:
+ *  - 65 <= T <= 256 with bf16 inputs (AUTO, FWDSUB), for at most 128 (sequence, head) pairs:
  *    the same wave-per-sub-block forward substitution, with the Gram tiles formed as the
- *    solved tiles arrive.
+ *    solved tiles arrive (16, 32 or 64 value columns per workgroup).
  *  - Otherwise, and for LEVEL: 64-node blocks staged in LDS, the couplings to earlier blocks
  *    applied as matrix-core products; a diagonal block is solved by
  *      FWDSUB   forward substitution over four 16-node sub-blocks on fp32 matrix-core
@@ -81,12 +82,24 @@ typedef enum { CANOPY_FP32 = 0, CANOPY_BF16 = 1 } canopy_dtype;
  *      NEUMANN  the finite series sum_{m=0..d} (-G_bb)^m, d the block's in-block depth;
  *      LEVEL    row-by-row substitution with the rows of equal in-block depth together;
  *      AUTO     NEUMANN for blocks of in-block depth <= 2, FWDSUB otherwise (measured on
- *               level trees: the series wins at depth 0-2, substitution from 3 up). */
+ *               level trees: the series wins at depth 0-2, substitution from 3 up).
+ * Matrix-form solvers for any T (canopy_tree_verify_ws only: they keep T x T operators of each
+ * (sequence, head) in a caller workspace). One launch per (sequence, head) builds N = -G and C
+ * there; the solve then runs per (sequence, head, 16 value columns):
+ *      SERIES   the whole tree's finite Neumann series (Bole's form): Z <- -G Z, U <- U + Z
+ *               for d rounds, d the tree depth (G^(d+1) = 0);
+ *      SQUARING the squaring form of the same series: Z <- (I + N^(2^k)) Z for
+ *               k < ceil(log2(d + 1)), the powers squared once per (sequence, head);
+ *      SPLIT    the split design ("Batch and heads to CTAs"): (I + G)^-1 multiplied out once per
+ *               (sequence, head) as the squaring product, then applied per value tile. */
 typedef enum {
     CANOPY_SOLVE_AUTO = 0,
     CANOPY_SOLVE_FWDSUB = 1,
     CANOPY_SOLVE_NEUMANN = 2,
-    CANOPY_SOLVE_LEVEL = 3
+    CANOPY_SOLVE_LEVEL = 3,
+    CANOPY_SOLVE_SERIES = 4,
+    CANOPY_SOLVE_SQUARING = 5,
+    CANOPY_SOLVE_SPLIT = 6
 } canopy_solver;
 
 /* Library version, major * 10000 + minor * 100 + patch. */
@@ -144,7 +157,8 @@ canopy_status canopy_tree_prep(const int32_t *parent, const int32_t *tree_len, c
  *   O, U        [B,T,HV,128] fp32, out: outputs o_i and pseudo-values u_i.
  *   ell         [B,T,HV] fp32, out: as in canopy_tree_prep.
  *   anc_mask, depth, tree_status: optional outputs (NULL to skip), as in canopy_tree_prep.
- *   solver      AUTO, FWDSUB, NEUMANN or LEVEL (see canopy_solver).
+ *   solver      AUTO, FWDSUB, NEUMANN or LEVEL (see canopy_solver); the matrix forms need a
+ *               workspace and go through canopy_tree_verify_ws (CANOPY_ERR_UNSUPPORTED here).
  *   waves       workgroup width, 1, 2, 4 or 8, or 0 to let the library choose from B, H and T.
  *               T <= 16 (AUTO, NEUMANN): waves per workgroup, each owning 16 value columns.
  *               17 <= T <= 64 (AUTO, FWDSUB, NEUMANN): 16-column tiles per workgroup, whose
@@ -161,6 +175,37 @@ canopy_status canopy_tree_verify(const void *q, const void *k, const void *v,
                                  float *ell, uint32_t *anc_mask, int32_t *depth,
                                  int32_t *tree_status, canopy_solver solver, int waves,
                                  hipStream_t stream);
+
+/*
+ * Bytes of workspace canopy_tree_verify_ws needs for this batch and solver: 0 for the solvers
+ * that need none (AUTO, FWDSUB, NEUMANN, LEVEL); for SERIES, SQUARING and SPLIT one slot per
+ * (sequence, value head) of 64 + n * Tp * Tp * 4 bytes, Tp = T rounded up to 16, n = 3 (SERIES),
+ * max(ceil(log2 T), 1) + 4 (SQUARING) or 11 (SPLIT). Returns 0 for sizes out of range.
+ */
+size_t canopy_workspace_bytes(int B, int HV, int T, canopy_solver solver);
+
+/*
+ * canopy_tree_verify with a caller workspace, for every solver including the matrix forms
+ * (SERIES, SQUARING, SPLIT; see canopy_solver). Arguments and outputs as canopy_tree_verify,
+ * plus:
+ *   workspace        device memory of at least canopy_workspace_bytes(B, HV, T, solver) bytes,
+ *                    16-byte aligned, owned by the caller; its contents are scratch (nothing
+ *                    needs to be cleared before the call, nothing is kept after it). Calls that
+ *                    share a workspace must not overlap in time. May be NULL when the solver
+ *                    needs none.
+ *   workspace_bytes  its size in bytes.
+ *   waves            ignored by the matrix forms.
+ * Errors: as canopy_tree_verify, plus CANOPY_ERR_WORKSPACE for a workspace that is NULL,
+ * misaligned or too small when the solver needs one. The matrix forms take bf16 or fp32 inputs;
+ * a malformed tree gives the status and NaN outputs as the other solvers do.
+ */
+canopy_status canopy_tree_verify_ws(const void *q, const void *k, const void *v,
+                                    const float *alpha, const float *beta, const float *S0,
+                                    const int32_t *parent, const int32_t *tree_len, int B, int H,
+                                    int HV, int T, canopy_dtype in_dtype, float *O, float *U,
+                                    float *ell, uint32_t *anc_mask, int32_t *depth,
+                                    int32_t *tree_status, canopy_solver solver, int waves,
+                                    void *workspace, size_t workspace_bytes, hipStream_t stream);
 
 /*
  * Commit the accepted path: S_new = exp(l_a) S0 + sum_{j in path} exp(l_a - l_j) k_j u_j^T

@@ -113,3 +113,21 @@ def test_binding_refuses_other_head_dims():
     with pytest.raises(ValueError, match="head dimension 64"):
         canopy.commit_verify(S0, q, torch.zeros((B, T, H, d)), a, par, par,
                              torch.ones(1, dtype=torch.int32), q, q, q, a, a, par)
+
+
+def test_workspace_bytes_without_gpu():
+    """The workspace size is host arithmetic: one slot per (sequence, value head) of a 64-byte
+    header plus n fp32 Tp x Tp matrices (Tp = T rounded up to 16): n = 3 for the series,
+    max(ceil(log2 T), 1) + 4 for the squaring form, 11 for the split design; 0 for the fused
+    solvers and for sizes out of range."""
+    lib = ctypes.CDLL(LIB)
+    f = lib.canopy_workspace_bytes
+    f.restype = ctypes.c_size_t
+    f.argtypes = [ctypes.c_int] * 4
+    assert f(1, 32, 16, 0) == 0 and f(1, 32, 16, 3) == 0
+    assert f(2, 32, 256, 4) == 64 * (64 + 3 * 256 * 256 * 4)
+    assert f(1, 1, 256, 5) == 64 + (8 + 4) * 256 * 256 * 4
+    assert f(1, 1, 100, 5) == 64 + (7 + 4) * 112 * 112 * 4
+    assert f(1, 1, 1, 5) == 64 + 5 * 16 * 16 * 4
+    assert f(3, 2, 17, 6) == 6 * (64 + 11 * 32 * 32 * 4)
+    assert f(1, 1, 257, 4) == 0 and f(0, 1, 16, 4) == 0

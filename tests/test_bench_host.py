@@ -80,7 +80,9 @@ def test_verify_flops_dense_tile():
     (17, "auto", 32, 0, "bf16", "verify_mid_kernel"),
     (64, "level", 512, 0, "bf16", "verify_kernel"),
     (128, "auto", 64, 0, "bf16", "verify_wide_kernel"),
-    (128, "auto", 128, 0, "bf16", "verify_kernel"),
+    (128, "auto", 128, 0, "bf16", "verify_wide_kernel"),
+    (128, "auto", 256, 0, "bf16", "verify_kernel"),
+    (100, "split", 512, 0, "bf16", "mat_apply_kernel"),
     (256, "fwdsub", 512, 2, "bf16", "verify_wide_kernel"),
     (256, "auto", 32, 0, "fp32", "verify_kernel"),
     (256, "auto", 32, 8, "bf16", "verify_kernel"),
@@ -145,3 +147,22 @@ def test_protocol_summary_splits_warm_and_cold(tmp_path):
 def test_more_than_one_gpu_is_refused(capsys):
     assert bench.main(["--gpus", "2"]) == 2
     assert "one GPU" in capsys.readouterr().err
+
+
+def test_method_flops_from_ancestor_pairs():
+    """The method's own flops (the MFMA fraction's numerator) follow the trees' ancestor pairs:
+    the 1+3+12 top-k tree has |A| = 3 * 1 + 12 * 2 = 27, so C2 is 34.7 MFLOP (the workload
+    table's algorithmic figure, against 37.7 dense); C4's random trees come to about 9.3 GFLOP
+    (against 25.8 dense); a chain has |A| = T (T - 1) / 2."""
+    import numpy as np
+    import synth
+    par = synth.make_tree("topk", 16, np.random.default_rng(0), branching=(3, 4))
+    assert bench.ancestor_pairs(par) == 27
+    assert bench.method_flops([par], 32) == 34_701_312
+    assert bench.ancestor_pairs(np.arange(-1, 9)) == 45
+    assert bench.ancestor_pairs(np.arange(-1, 9), n=4) == 6
+    inp = bench.build_inputs(bench.WORKLOADS["random256_b16"])
+    f = bench.method_flops(inp["parent"], 32)
+    assert 9.0e9 < f < 9.6e9, f
+    assert f < bench.verify_flops(16, 32, 256) / 2.5
+    assert bench.commit_flops(32, 3) == 32 * 2 * 128 * 128 * 3

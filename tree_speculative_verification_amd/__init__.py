@@ -21,13 +21,15 @@ import os
 import torch  # loaded first so that libcanopy binds to the HIP runtime torch uses
 
 __all__ = ["load", "lib_path", "tree_prep", "tree_verify", "commit", "serial_verify",
-           "serial_commit", "set_wait_bound", "CanopyError", "SOLVERS"]
+           "serial_commit", "set_wait_bound", "workspace_bytes", "CanopyError", "SOLVERS"]
 
 _HERE = os.path.dirname(os.path.abspath(__file__))
 _LIB_PATH = os.path.join(_HERE, "libcanopy.so")
 _lib = None
 
-SOLVERS = {"auto": 0, "fwdsub": 1, "neumann": 2, "level": 3}
+SOLVERS = {"auto": 0, "fwdsub": 1, "neumann": 2, "level": 3, "series": 4, "squaring": 5, "split": 6}
+# Solvers that keep T x T operators per (sequence, head) in a workspace (canopy_tree_verify_ws).
+WORKSPACE_SOLVERS = ("series", "squaring", "split")
 _FP32, _BF16 = 0, 1
 
 
@@ -59,6 +61,11 @@ def load():
     lib.canopy_tree_verify.argtypes = [P, P, P, P, P, P, P, P, i, i, i, i, i, P, P, P, P, P, P, i, i,
                                        u64]
     lib.canopy_tree_verify.restype = i
+    lib.canopy_tree_verify_ws.argtypes = [P, P, P, P, P, P, P, P, i, i, i, i, i, P, P, P, P, P, P, i,
+                                          i, P, ctypes.c_size_t, u64]
+    lib.canopy_tree_verify_ws.restype = i
+    lib.canopy_workspace_bytes.argtypes = [i, i, i, i]
+    lib.canopy_workspace_bytes.restype = ctypes.c_size_t
     lib.canopy_commit.argtypes = [P, P, i, P, P, P, P, P, P, i, i, i, i, P, P, u64]
     lib.canopy_commit.restype = i
     lib.canopy_commit_verify.argtypes = [P, P, P, P, P, P, P, P, i, P, P, P, P, P, P, P, i, i, i, i, i,
@@ -186,13 +193,20 @@ def tree_prep(parent, alpha, tree_len=None):
     return mask, depth, ell, status
 
 
+def workspace_bytes(B, HV, T, solver):
+    """Bytes of workspace the solver needs for this batch (0 for the fused solvers)."""
+    return int(load().canopy_workspace_bytes(int(B), int(HV), int(T), SOLVERS[solver]))
+
+
 def tree_verify(q, k, v, alpha, beta, S0, parent, solver="auto", waves=0, structure=False,
-                out=None, tree_len=None):
+                out=None, tree_len=None, workspace=None):
     """Every node's output O and pseudo-value U ([B,T,HV,128] fp32) and ell ([B,T,HV] fp32).
     q and k are [B,T,H,128] with H dividing v's head count HV (value head j reads q/k head
     j // (HV // H)). ``tree_len`` ([B] int32) gives ragged node counts; rows past a sequence's
     count are left unwritten. With ``structure=True`` also returns the ancestor bitmask, depth
-    and tree status. ``out`` may pass preallocated (O, U, ell)."""
+    and tree status. ``out`` may pass preallocated (O, U, ell). The matrix-form solvers
+    ("series", "squaring", "split") run through canopy_tree_verify_ws with ``workspace`` (a
+    uint8 tensor of at least ``workspace_bytes`` bytes), allocated here when not given."""
     B, T, H, d = q.shape
     _head_dim(d, "q")
     dt = _in_dtype(q)
@@ -212,10 +226,21 @@ def tree_verify(q, k, v, alpha, beta, S0, parent, solver="auto", waves=0, struct
         mask = torch.empty((B, T, (T + 31) // 32), dtype=torch.int32, device=dev)
         depth = torch.empty((B, T), dtype=torch.int32, device=dev)
         status = torch.empty((B,), dtype=torch.int32, device=dev)
-    _check(load().canopy_tree_verify(_ptr(q), _ptr(k), _ptr(v), _ptr(alpha), _ptr(beta),
-                                     _ptr(S0), _ptr(parent), _ptr(tl), B, H, HV, T, dt, _ptr(O),
-                                     _ptr(U), _ptr(ell), _ptr(mask), _ptr(depth), _ptr(status),
-                                     SOLVERS[solver], int(waves), _stream()))
+    if solver in WORKSPACE_SOLVERS:
+        need = workspace_bytes(B, HV, T, solver)
+        if workspace is None:
+            workspace = torch.empty((max(need, 16),), dtype=torch.uint8, device=dev)
+        _req(workspace, "workspace", torch.uint8)
+        _check(load().canopy_tree_verify_ws(_ptr(q), _ptr(k), _ptr(v), _ptr(alpha), _ptr(beta),
+                                            _ptr(S0), _ptr(parent), _ptr(tl), B, H, HV, T, dt,
+                                            _ptr(O), _ptr(U), _ptr(ell), _ptr(mask), _ptr(depth),
+                                            _ptr(status), SOLVERS[solver], int(waves),
+                                            _ptr(workspace), workspace.numel(), _stream()))
+    else:
+        _check(load().canopy_tree_verify(_ptr(q), _ptr(k), _ptr(v), _ptr(alpha), _ptr(beta),
+                                         _ptr(S0), _ptr(parent), _ptr(tl), B, H, HV, T, dt, _ptr(O),
+                                         _ptr(U), _ptr(ell), _ptr(mask), _ptr(depth), _ptr(status),
+                                         SOLVERS[solver], int(waves), _stream()))
     if structure:
         return O, U, ell, mask, depth, status
     return O, U, ell

@@ -34,9 +34,11 @@ bool aligned16(const void *p) { return (reinterpret_cast<uintptr_t>(p) & 15u) ==
 // fp32 inputs stage twice the bytes per block and use 2 waves.
 int pick_waves(canopy_dtype dt) { return dt == CANOPY_BF16 ? 8 : 2; }
 
-// Beyond this many (sequence, head) pairs the blocked kernel's single Gram pass per head wins
-// over the wave-per-sub-block kernel's per-column-tile passes for T > 64.
-constexpr long long kWideMaxHeads = 64;
+// Up to this many (sequence, head) pairs the wave-per-sub-block kernel runs trees of 65 to 256
+// nodes (1, 2 or 4 column tiles per workgroup at up to 32, 64 and 128 pairs); beyond, the
+// blocked kernel's single Gram pass per head wins. Measured on MI355X at B = 4, H = 32: T = 256
+// 45.1 us with 4 column tiles against 55.6 us blocked, T = 128 23.8 against 26.9 us.
+constexpr long long kWideMaxHeads = 128;
 
 }  // namespace
 
@@ -53,6 +55,7 @@ const char *canopy_status_string(canopy_status s) {
         case CANOPY_OK: return "ok";
         case CANOPY_ERR_ARG: return "invalid argument (null pointer or size out of range)";
         case CANOPY_ERR_UNSUPPORTED: return "unsupported dtype, solver or waves value";
+        case CANOPY_ERR_WORKSPACE: return "workspace missing, misaligned or too small";
         case CANOPY_ERR_HIP: return "HIP launch error";
         default: return "unknown status";
     }
@@ -108,10 +111,45 @@ canopy_status canopy_tree_verify(const void *q, const void *k, const void *v,
         if (waves == 1 || waves == 2) return from_hip(launch_verify_wide(a, waves, stream));
         if (waves == 0) {
             const long long heads = static_cast<long long>(B) * HV;
-            if (heads <= kWideMaxHeads) return from_hip(launch_verify_wide(a, heads <= 32 ? 1 : 2, stream));
+            if (heads <= kWideMaxHeads)
+                return from_hip(launch_verify_wide(a, heads <= 32 ? 1 : (heads <= 64 ? 2 : 4), stream));
         }
     }
     return from_hip(launch_verify(a, waves ? waves : pick_waves(in_dtype), stream));
+}
+
+size_t canopy_workspace_bytes(int B, int HV, int T, canopy_solver solver) {
+    if (!sizes_ok(B, HV, T)) return 0;
+    return mat_workspace_bytes(B, HV, T, solver);
+}
+
+canopy_status canopy_tree_verify_ws(const void *q, const void *k, const void *v,
+                                    const float *alpha, const float *beta, const float *S0,
+                                    const int32_t *parent, const int32_t *tree_len, int B, int H,
+                                    int HV, int T, canopy_dtype in_dtype, float *O, float *U,
+                                    float *ell, uint32_t *anc_mask, int32_t *depth,
+                                    int32_t *tree_status, canopy_solver solver, int waves,
+                                    void *workspace, size_t workspace_bytes, hipStream_t stream) {
+    if (solver != CANOPY_SOLVE_SERIES && solver != CANOPY_SOLVE_SQUARING && solver != CANOPY_SOLVE_SPLIT)
+        return canopy_tree_verify(q, k, v, alpha, beta, S0, parent, tree_len, B, H, HV, T, in_dtype, O, U,
+                                  ell, anc_mask, depth, tree_status, solver, waves, stream);
+    if (!q || !k || !v || !alpha || !beta || !S0 || !parent || !O || !U || !ell)
+        return CANOPY_ERR_ARG;
+    if (!sizes_ok(B, HV, T) || !heads_ok(H, HV)) return CANOPY_ERR_ARG;
+    if (!aligned16(q) || !aligned16(k) || !aligned16(v) || !aligned16(S0)) return CANOPY_ERR_ARG;
+    if (in_dtype != CANOPY_FP32 && in_dtype != CANOPY_BF16) return CANOPY_ERR_UNSUPPORTED;
+    if (!workspace || !aligned16(workspace) || workspace_bytes < mat_workspace_bytes(B, HV, T, solver))
+        return CANOPY_ERR_WORKSPACE;
+    VerifyArgs a{};
+    a.q = q; a.k = k; a.v = v;
+    a.alpha = alpha; a.beta = beta; a.S0 = S0; a.parent = parent; a.tree_len = tree_len;
+    a.B = B; a.H = HV; a.HK = H; a.T = T;
+    a.bf16 = in_dtype == CANOPY_BF16;
+    a.solver = solver;
+    a.O = O; a.U = U; a.ell = ell;
+    a.anc_mask = anc_mask; a.depth = depth; a.tree_status = tree_status;
+    a.wait_bound = g_wait_bound.load(std::memory_order_relaxed);
+    return from_hip(launch_verify_matrix(a, workspace, stream));
 }
 
 canopy_status canopy_commit(const float *S0, const void *k, canopy_dtype in_dtype,

@@ -147,6 +147,10 @@ bool commit_verify_mid_fits(const VerifyArgs &a, int col_tiles);
 hipError_t launch_commit_verify_mid(const VerifyArgs &a, const PrevCommitArgs &c, int col_tiles,
                                     hipStream_t stream);
 hipError_t launch_verify_wide(const VerifyArgs &a, int col_tiles, hipStream_t stream);
+// Matrix-form solves (SERIES, SQUARING, SPLIT) with their operators in a workspace of
+// mat_workspace_bytes bytes.
+size_t mat_workspace_bytes(int B, int H, int T, int solver);
+hipError_t launch_verify_matrix(const VerifyArgs &a, void *ws, hipStream_t stream);
 hipError_t launch_prep(const PrepArgs &a, hipStream_t stream);
 hipError_t launch_commit(const CommitArgs &a, hipStream_t stream);
 hipError_t launch_serial(const SerialArgs &a, hipStream_t stream);

@@ -401,7 +401,9 @@ __global__ __launch_bounds__(1024) void verify_wide_kernel(VerifyArgs a) {
 hipError_t launch_verify_wide(const VerifyArgs &a, int col_tiles, hipStream_t stream) {
     const unsigned heads = static_cast<unsigned>(a.B * a.H);
     const dim3 block(64 * ((a.T + 15) / 16));
-    if (col_tiles == 2)
+    if (col_tiles == 4)
+        hipLaunchKernelGGL((verify_wide_kernel<4>), dim3(heads * 2), block, 0, stream, a);
+    else if (col_tiles == 2)
         hipLaunchKernelGGL((verify_wide_kernel<2>), dim3(heads * 4), block, 0, stream, a);
     else
         hipLaunchKernelGGL((verify_wide_kernel<1>), dim3(heads * 8), block, 0, stream, a);
