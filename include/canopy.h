@@ -208,6 +208,25 @@ canopy_status canopy_tree_verify_ws(const void *q, const void *k, const void *v,
                                     void *workspace, size_t workspace_bytes, hipStream_t stream);
 
 /*
+ * canopy_tree_verify_ws for callers that cannot allocate device memory (code under HIP graph
+ * capture, tight serving loops, harnesses that forbid allocation): the same kernels, with the
+ * workspace taken from a device array inside the library (64 MiB per device, created with the
+ * code object and held until the process ends) instead of a caller buffer. Allocates nothing.
+ * Arguments, outputs and errors as canopy_tree_verify_ws without workspace and workspace_bytes;
+ * a batch whose canopy_workspace_bytes exceeds 64 MiB returns CANOPY_ERR_WORKSPACE and launches
+ * nothing (e.g. SPLIT at T = 256 fits 23 (sequence, head) pairs, SERIES at T = 256 fits 85).
+ * Solvers that need no workspace go to canopy_tree_verify. Every call on a device shares that
+ * device's array: calls on one device must not overlap in time (different streams included).
+ */
+canopy_status canopy_tree_verify_static(const void *q, const void *k, const void *v,
+                                        const float *alpha, const float *beta, const float *S0,
+                                        const int32_t *parent, const int32_t *tree_len, int B,
+                                        int H, int HV, int T, canopy_dtype in_dtype, float *O,
+                                        float *U, float *ell, uint32_t *anc_mask, int32_t *depth,
+                                        int32_t *tree_status, canopy_solver solver, int waves,
+                                        hipStream_t stream);
+
+/*
  * Commit the accepted path: S_new = exp(l_a) S0 + sum_{j in path} exp(l_a - l_j) k_j u_j^T
  * with a the path's last node ("What the commit kernel stores"; "M5"). The decay ratios are
  * suffix sums of log alpha along the path (fp64), so no cancellation of large l enters them.

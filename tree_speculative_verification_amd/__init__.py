@@ -64,6 +64,9 @@ def load():
     lib.canopy_tree_verify_ws.argtypes = [P, P, P, P, P, P, P, P, i, i, i, i, i, P, P, P, P, P, P, i,
                                           i, P, ctypes.c_size_t, u64]
     lib.canopy_tree_verify_ws.restype = i
+    lib.canopy_tree_verify_static.argtypes = [P, P, P, P, P, P, P, P, i, i, i, i, i, P, P, P, P, P, P,
+                                              i, i, u64]
+    lib.canopy_tree_verify_static.restype = i
     lib.canopy_workspace_bytes.argtypes = [i, i, i, i]
     lib.canopy_workspace_bytes.restype = ctypes.c_size_t
     lib.canopy_commit.argtypes = [P, P, i, P, P, P, P, P, P, i, i, i, i, P, P, u64]

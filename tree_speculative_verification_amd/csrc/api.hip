@@ -152,6 +152,26 @@ canopy_status canopy_tree_verify_ws(const void *q, const void *k, const void *v,
     return from_hip(launch_verify_matrix(a, workspace, stream));
 }
 
+canopy_status canopy_tree_verify_static(const void *q, const void *k, const void *v,
+                                        const float *alpha, const float *beta, const float *S0,
+                                        const int32_t *parent, const int32_t *tree_len, int B,
+                                        int H, int HV, int T, canopy_dtype in_dtype, float *O,
+                                        float *U, float *ell, uint32_t *anc_mask, int32_t *depth,
+                                        int32_t *tree_status, canopy_solver solver, int waves,
+                                        hipStream_t stream) {
+    if (solver != CANOPY_SOLVE_SERIES && solver != CANOPY_SOLVE_SQUARING && solver != CANOPY_SOLVE_SPLIT)
+        return canopy_tree_verify(q, k, v, alpha, beta, S0, parent, tree_len, B, H, HV, T, in_dtype, O, U,
+                                  ell, anc_mask, depth, tree_status, solver, waves, stream);
+    if (!sizes_ok(B, HV, T)) return CANOPY_ERR_ARG;
+    const size_t need = mat_workspace_bytes(B, HV, T, solver);
+    if (need > kStaticScratchBytes) return CANOPY_ERR_WORKSPACE;
+    void *ws = nullptr;
+    if (mat_static_scratch(&ws) != hipSuccess) return CANOPY_ERR_HIP;
+    return canopy_tree_verify_ws(q, k, v, alpha, beta, S0, parent, tree_len, B, H, HV, T, in_dtype, O, U,
+                                 ell, anc_mask, depth, tree_status, solver, waves, ws, kStaticScratchBytes,
+                                 stream);
+}
+
 canopy_status canopy_commit(const float *S0, const void *k, canopy_dtype in_dtype,
                             const float *U, const float *alpha, const int32_t *parent,
                             const int32_t *tree_len, const int32_t *path, const int32_t *path_len,

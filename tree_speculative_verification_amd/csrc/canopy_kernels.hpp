@@ -151,6 +151,9 @@ hipError_t launch_verify_wide(const VerifyArgs &a, int col_tiles, hipStream_t st
 // mat_workspace_bytes bytes.
 size_t mat_workspace_bytes(int B, int H, int T, int solver);
 hipError_t launch_verify_matrix(const VerifyArgs &a, void *ws, hipStream_t stream);
+// The workspace of canopy_tree_verify_static: a device array of this many bytes per device.
+constexpr size_t kStaticScratchBytes = static_cast<size_t>(64) << 20;
+hipError_t mat_static_scratch(void **ptr);
 hipError_t launch_prep(const PrepArgs &a, hipStream_t stream);
 hipError_t launch_commit(const CommitArgs &a, hipStream_t stream);
 hipError_t launch_serial(const SerialArgs &a, hipStream_t stream);

@@ -17,6 +17,8 @@
 // With bf16 inputs the products run on v_mfma_f32_16x16x32_bf16, fp32 operands split into bf16
 // hi + lo parts (three passes); with fp32 inputs every product runs on fp32 MFMA (exact
 // products), as the other fp32 paths do. Accumulation is fp32.
+#include <mutex>
+
 #include "canopy_kernels.hpp"
 #include "canopy_prep.hpp"
 
@@ -477,6 +479,33 @@ __global__ __launch_bounds__(ANT) void mat_apply_kernel(int solver, int B, int H
             }
         }
     }
+}
+
+// The workspace of canopy_tree_verify_static, for callers that cannot allocate: one array per
+// device, held until the process ends and shared by every call on that device (so calls that
+// overlap on one device race). The matrix-form kernels write every workspace word they read
+// before reading it, so its contents from an earlier call never matter.
+static __device__ __align__(256) uint8_t scratch[kStaticScratchBytes];
+
+// The device address of this device's scratch array, looked up once per device with that
+// device current (host code must not use the symbol itself as an address).
+hipError_t mat_static_scratch(void **ptr) {
+    constexpr int kMaxDevices = 64;
+    static std::mutex mu;
+    static void *dev_ptr[kMaxDevices] = {};
+    int dev = -1;
+    hipError_t e = hipGetDevice(&dev);
+    if (e != hipSuccess) return e;
+    if (dev < 0 || dev >= kMaxDevices) return hipErrorInvalidDevice;
+    std::lock_guard<std::mutex> lock(mu);
+    if (!dev_ptr[dev]) {
+        void *p = nullptr;
+        e = hipGetSymbolAddress(&p, HIP_SYMBOL(scratch));
+        if (e != hipSuccess) return e;
+        dev_ptr[dev] = p;
+    }
+    *ptr = dev_ptr[dev];
+    return hipSuccess;
 }
 
 hipError_t launch_verify_matrix(const VerifyArgs &a, void *ws, hipStream_t stream) {
