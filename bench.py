@@ -454,23 +454,14 @@ def graph_of(fn, n):
     return g
 
 
-# Shader clocks of the spin kernel that holds the stream before a timed graph replay (about
-# 80 µs at 2.4 GHz, longer than the host takes to submit a graph of a few hundred launches).
-HOLD_CYCLES = 200_000
-
-
 def time_graph(g, n):
     """Average µs per call of a graph of n calls: one replay between two events on the stream
-    the replay runs on, synchronised on both sides. A spin kernel ahead of the first event
-    holds the stream while the host submits the graph's launches, so that the events bracket
-    the n calls running back to back on the GPU and not the host's submission of the first
-    ones (with a graph of 20 steps of about 5 µs, the submission alone added 0.5 µs per step)."""
+    the replay runs on, synchronised on both sides."""
     import torch
     g.replay()  # warm replay
     torch.cuda.synchronize()
     e0 = torch.cuda.Event(enable_timing=True)
     e1 = torch.cuda.Event(enable_timing=True)
-    torch.cuda._sleep(HOLD_CYCLES)
     e0.record()
     g.replay()
     e1.record()

@@ -101,13 +101,16 @@ __global__ __launch_bounds__(64 * NWV) void verify_small_kernel(VerifyArgs a, Pr
         kf[ks] = Op::template load_frag<In>(a.k, erow + 32 * ks, true);
         qf[ks] = Op::template load_frag<In>(a.q, erow + 32 * ks, true);
     }
-    float s0v[4][8];
+    // s0t[t][ks] = S0[32ks + 8lg + t][col0 + lr]: row t of the B fragment of reduction slice ks,
+    // grouped by t so that each f32x4 is also the accumulator of the fused commit's rank update
+    // for its 16 x 16 tile t (the key rows of that update are permuted to land there)
+    f32x4 s0t[8];
     {
         const float *S0p = a.S0 + static_cast<size_t>(bh) * D * D + col0 + lr;
 #pragma unroll
         for (int ks = 0; ks < 4; ++ks)
 #pragma unroll
-            for (int e = 0; e < 8; ++e) s0v[ks][e] = S0p[(32 * ks + 8 * lg + e) * D];
+            for (int e = 0; e < 8; ++e) s0t[e][ks] = S0p[(32 * ks + 8 * lg + e) * D];
     }
     typename Op::Raw vraw[4];
 #pragma unroll
@@ -204,14 +207,14 @@ __global__ __launch_bounds__(64 * NWV) void verify_small_kernel(VerifyArgs a, Pr
         }
         const float Pa = __builtin_amdgcn_exp2f(static_cast<float>(__shfl(sv, 0, 64)));
         const float w = __builtin_amdgcn_exp2f(static_cast<float>(sv - la));  // decay after t
-        f32x4 dS[8];
+        // S_new = P_a S0 + sum_t w_t k_t u_t^T, accumulated in place of the S0 fragment
 #pragma unroll
-        for (int t = 0; t < 8; ++t) dS[t] = f32x4{0.f, 0.f, 0.f, 0.f};
+        for (int t = 0; t < 8; ++t) s0t[t] = Pa * s0t[t];
         {
             const float wv = __shfl(w, lg, 64);
             const float bu = lg < pmv ? wv * ub : 0.f;
 #pragma unroll
-            for (int t = 0; t < 8; ++t) dS[t] = mfma_f32(ka[t], bu, dS[t]);
+            for (int t = 0; t < 8; ++t) s0t[t] = mfma_f32(ka[t], bu, s0t[t]);
         }
         for (int p0 = 4; p0 < pmv; p0 += 4) {  // paths longer than 4 nodes
             const int pos = min(p0 + lg, 63);
@@ -221,25 +224,29 @@ __global__ __launch_bounds__(64 * NWV) void verify_small_kernel(VerifyArgs a, Pr
             const float wv = __shfl(w, pos, 64);
             const float bu = p0 + lg < pmv ? wv * ux : 0.f;
 #pragma unroll
-            for (int t = 0; t < 8; ++t) dS[t] = mfma_f32(kx[t], bu, dS[t]);
+            for (int t = 0; t < 8; ++t) s0t[t] = mfma_f32(kx[t], bu, s0t[t]);
         }
         const float qnan = __builtin_nanf("");
 #pragma unroll
-        for (int ks = 0; ks < 4; ++ks)
+        for (int t = 0; t < 8; ++t)
 #pragma unroll
-            for (int e = 0; e < 8; ++e) s0v[ks][e] = pst != 0 ? qnan : Pa * s0v[ks][e] + dS[e][ks];
+            for (int ks = 0; ks < 4; ++ks) s0t[t][ks] = pst != 0 ? qnan : s0t[t][ks];
         float *Sn = c.S_new + static_cast<size_t>(bh) * D * D + col0 + lr;
 #pragma unroll
         for (int ks = 0; ks < 4; ++ks)
 #pragma unroll
-            for (int e = 0; e < 8; ++e) store_nt(Sn + static_cast<size_t>(32 * ks + 8 * lg + e) * D, s0v[ks][e]);
+            for (int e = 0; e < 8; ++e) store_nt(Sn + static_cast<size_t>(32 * ks + 8 * lg + e) * D, s0t[e][ks]);
         if (c.path_status && tile == 0 && h == 0 && lane == 0) c.path_status[b] = pst;
     }
 
     // ---- a2: projections; result order: lane (lg, lr) holds rows 4lg+e of column lr
     Sp s0f[4];
 #pragma unroll
-    for (int ks = 0; ks < 4; ++ks) s0f[ks] = Op::split(s0v[ks]);
+    for (int ks = 0; ks < 4; ++ks) {
+        const float v[8] = {s0t[0][ks], s0t[1][ks], s0t[2][ks], s0t[3][ks],
+                            s0t[4][ks], s0t[5][ks], s0t[6][ks], s0t[7][ks]};
+        s0f[ks] = Op::split(v);
+    }
     f32x4 ak = {0.f, 0.f, 0.f, 0.f}, aq = {0.f, 0.f, 0.f, 0.f};
 #pragma unroll
     for (int ks = 0; ks < 4; ++ks) {
