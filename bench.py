@@ -515,6 +515,45 @@ def cpu_baseline(inp, budget_s=10.0):
                 kind="oracle", sample=f"{len(times)} full layers of this workload, median")
 
 
+def cpu_baseline_threads(inp, wl, reps=5):
+    """The CPU baseline of the timing protocol: the oracle's wall time per layer (µs), median of
+    `reps`, on every host core and on one.
+    Large workloads run a slice of whole (sequence, head) problems, as many heads of sequence 0
+    as there are threads (all cores) or 2 heads (one core), scaled by the number of such
+    problems in the layer; every (sequence, head) problem costs the same up to its tree."""
+    import oracle
+    all_threads = oracle.num_threads()
+    B, H = wl["B"], wl["H"]
+    res = {}
+    for label, threads in (("all_cores", all_threads), ("one_core", 1)):
+        oracle.set_threads(threads)
+        full = B * H * wl["T"] <= 2048
+        hs = H if full else min(H, max(2, threads))
+        if full:
+            sub = dict(inp)
+            scale = 1.0
+        else:
+            sub = {n: inp[n][:1, :, :hs] for n in ("q", "k", "v", "alpha", "beta")}
+            sub["S0"] = inp["S0"][:1, :hs]
+            for n in ("parent", "path"):
+                sub[n] = inp[n][:1]
+            sub["path_len"] = inp["path_len"][:1]
+            scale = (B * H) / hs
+        times = []
+        for rep in range(reps + 1):  # the first call (thread team start-up) is not timed
+            t0 = time.perf_counter()
+            oracle.gdn_tree(sub["parent"], sub["q"], sub["k"], sub["v"], sub["alpha"], sub["beta"], sub["S0"])
+            oracle.commit(sub["parent"], sub["path"], sub["path_len"], sub["k"], sub["v"], sub["alpha"],
+                          sub["beta"], sub["S0"])
+            if rep:
+                times.append((time.perf_counter() - t0) * scale)
+        times.sort()
+        res[label] = {"us_per_layer": round(times[len(times) // 2] * 1e6, 1), "threads": threads,
+                      "sample": "whole layer" if full else f"sequence 0, {hs} heads, scaled x{scale:g}"}
+    oracle.set_threads(all_threads)
+    return res
+
+
 # The workloads of the timing protocol: every configuration of the pages' workload table that
 # fits one GPU, small and large batch.
 PROTOCOL_WORKLOADS = ["binary7_fp32", "topk16_b1", "skewed64_b1", "skewed64_b16", "random256_b1",
@@ -561,44 +600,6 @@ def gpu_state():
             return {k: gpu[k] for k in ("clock", "temperature", "power") if k in gpu} or {"keys": sorted(gpu)[:40]}
         return {"raw": r.stdout[:2000]}
     return None
-
-
-def oracle_timing(inp, wl, reps=5):
-    """The oracle's wall time per layer (µs), median of `reps`, on every host core and on one.
-    Large workloads run a slice of whole (sequence, head) problems, as many heads of sequence 0
-    as there are threads (all cores) or 2 heads (one core), scaled by the number of such
-    problems in the layer; every (sequence, head) problem costs the same up to its tree."""
-    import oracle
-    all_threads = oracle.num_threads()
-    B, H = wl["B"], wl["H"]
-    res = {}
-    for label, threads in (("all_cores", all_threads), ("one_core", 1)):
-        oracle.set_threads(threads)
-        full = B * H * wl["T"] <= 2048
-        hs = H if full else min(H, max(2, threads))
-        if full:
-            sub = dict(inp)
-            scale = 1.0
-        else:
-            sub = {n: inp[n][:1, :, :hs] for n in ("q", "k", "v", "alpha", "beta")}
-            sub["S0"] = inp["S0"][:1, :hs]
-            for n in ("parent", "path"):
-                sub[n] = inp[n][:1]
-            sub["path_len"] = inp["path_len"][:1]
-            scale = (B * H) / hs
-        times = []
-        for rep in range(reps + 1):  # the first call (thread team start-up) is not timed
-            t0 = time.perf_counter()
-            oracle.gdn_tree(sub["parent"], sub["q"], sub["k"], sub["v"], sub["alpha"], sub["beta"], sub["S0"])
-            oracle.commit(sub["parent"], sub["path"], sub["path_len"], sub["k"], sub["v"], sub["alpha"],
-                          sub["beta"], sub["S0"])
-            if rep:
-                times.append((time.perf_counter() - t0) * scale)
-        times.sort()
-        res[label] = {"us_per_layer": round(times[len(times) // 2] * 1e6, 1), "threads": threads,
-                      "sample": "whole layer" if full else f"sequence 0, {hs} heads, scaled x{scale:g}"}
-    oracle.set_threads(all_threads)
-    return res
 
 
 def _stats(xs):
@@ -687,7 +688,7 @@ def run_protocol(args):
         torch.cuda.empty_cache()
         rec = {"workload": name, "desc": wl["desc"], "steps": args.steps, "warmup": args.warmup,
                "stream_time": {"warm": warm, "cold": cold},
-               "oracle": oracle_timing(inp, wl), "kernel_digest": kernel_digest(),
+               "oracle": cpu_baseline_threads(inp, wl), "kernel_digest": kernel_digest(),
                "gpu_state_before": state_before, "gpu_state_after": state_after}
         if name == names[0]:
             rec["environment"] = environment()
@@ -943,7 +944,7 @@ def main(argv=None):
     ap.add_argument("--solver-sweep", action="store_true",
                     help="time every solver on level trees over T, width and --batches")
     ap.add_argument("--depth-sweep", action="store_true",
-                    help="time and check every solve strategy over tree depths 1-255 at T=256")
+                    help="time every solve strategy over tree depths 1-255 at T=256")
     ap.add_argument("--conv", action="store_true",
                     help="time the root-path causal convolution and its commit instead")
     ap.add_argument("--protocol", action="store_true",
