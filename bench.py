@@ -108,7 +108,7 @@ def one_launch_step(T, solver, heads=32, waves=0):
     """Whether canopy_commit_verify runs the step as one launch (after previous trees of at most
     64 nodes): trees of at most 16 nodes (AUTO, NEUMANN), and trees of 17 to 64 nodes (not
     LEVEL) whose workgroups hold at most 2 state pairs per thread (4 * tiles <= 2 * sub-blocks)."""
-    if solver in ("series", "squaring", "split"):
+    if solver in ("series", "squaring", "split", "levelsync"):
         return False
     if T <= 16:
         return solver in ("auto", "neumann")
@@ -174,6 +174,8 @@ def verify_kernel_name(T, solver, heads=0, waves=0, dtype="bf16"):
     """The kernel canopy_tree_verify launches for this size, solver, head count and width."""
     if solver in ("series", "squaring", "split"):
         return "mat_apply_kernel"
+    if solver == "levelsync":
+        return "verify_kernel"
     if T <= 16 and solver in ("auto", "neumann"):
         return "verify_small_kernel"
     if 16 < T <= 64 and solver != "level":
@@ -931,7 +933,7 @@ def main(argv=None):
     ap.add_argument("--no-extra", action="store_true",
                     help="the default workload only (without the B=16 workloads beside it)")
     ap.add_argument("--solver", default="auto",
-                    choices=["auto", "fwdsub", "neumann", "level", "series", "squaring", "split"])
+                    choices=["auto", "fwdsub", "neumann", "level", "series", "squaring", "split", "levelsync"])
     ap.add_argument("--waves", type=int, default=0)
     ap.add_argument("--no-cpu", action="store_true", help="skip the oracle CPU baseline")
     ap.add_argument("--no-serial", action="store_true", help="skip the serial fork baseline")

@@ -83,6 +83,18 @@ typedef enum { CANOPY_FP32 = 0, CANOPY_BF16 = 1 } canopy_dtype;
  *      LEVEL    row-by-row substitution with the rows of equal in-block depth together;
  *      AUTO     NEUMANN for blocks of in-block depth <= 2, FWDSUB otherwise (measured on
  *               level trees: the series wins at depth 0-2, substitution from 3 up).
+ *  - LEVELSYNC (bf16 inputs, any T, one workgroup of 8 waves per (sequence, head)): the
+ *    level-synchronous solve over the whole tree ("The tree closed form": level order, and the
+ *    level-synchronous solve U_L = R_L - G_{L,:} U). Row i of G and C is non-zero only at the
+ *    ancestors of i, so each node gathers over its own ancestor list: LDS tables hold one entry
+ *    per (node, ancestor) pair, G and C of each pair formed on the matrix cores, and the u rows
+ *    of the nodes that have a child. The nodes are taken in level order, 16 at a time (their
+ *    K S0 and Q S0 rows on the matrix cores), every product of the solve and the read-out in
+ *    fp32. Trees of at most 2560 (node, ancestor) pairs (sum of the node depths) and at most
+ *    160 nodes with a child fit the tables; a larger tree runs the blocked solve with AUTO's
+ *    choice for its blocks, so the result is the same system solved either way. Measured on
+ *    MI355X at T = 256 it takes about as long per (sequence, head) as the blocked solve, so
+ *    AUTO does not choose it.
  * Matrix-form solvers for any T (canopy_tree_verify_ws only: they keep T x T operators of each
  * (sequence, head) in a caller workspace). One launch per (sequence, head) builds N = -G and C
  * there; the solve then runs per (sequence, head, 16 value columns):
@@ -99,7 +111,8 @@ typedef enum {
     CANOPY_SOLVE_LEVEL = 3,
     CANOPY_SOLVE_SERIES = 4,
     CANOPY_SOLVE_SQUARING = 5,
-    CANOPY_SOLVE_SPLIT = 6
+    CANOPY_SOLVE_SPLIT = 6,
+    CANOPY_SOLVE_LEVELSYNC = 7
 } canopy_solver;
 
 /* Library version, major * 10000 + minor * 100 + patch. */
@@ -157,8 +170,10 @@ canopy_status canopy_tree_prep(const int32_t *parent, const int32_t *tree_len, c
  *   O, U        [B,T,HV,128] fp32, out: outputs o_i and pseudo-values u_i.
  *   ell         [B,T,HV] fp32, out: as in canopy_tree_prep.
  *   anc_mask, depth, tree_status: optional outputs (NULL to skip), as in canopy_tree_prep.
- *   solver      AUTO, FWDSUB, NEUMANN or LEVEL (see canopy_solver); the matrix forms need a
- *               workspace and go through canopy_tree_verify_ws (CANOPY_ERR_UNSUPPORTED here).
+ *   solver      AUTO, FWDSUB, NEUMANN, LEVEL or LEVELSYNC (see canopy_solver; LEVELSYNC needs
+ *               bf16 inputs and takes waves 0 or 8, else CANOPY_ERR_UNSUPPORTED); the matrix
+ *               forms need a workspace and go through canopy_tree_verify_ws
+ *               (CANOPY_ERR_UNSUPPORTED here).
  *   waves       workgroup width, 1, 2, 4 or 8, or 0 to let the library choose from B, H and T.
  *               T <= 16 (AUTO, NEUMANN): waves per workgroup, each owning 16 value columns.
  *               17 <= T <= 64 (AUTO, FWDSUB, NEUMANN): 16-column tiles per workgroup, whose

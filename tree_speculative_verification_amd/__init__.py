@@ -27,7 +27,8 @@ _HERE = os.path.dirname(os.path.abspath(__file__))
 _LIB_PATH = os.path.join(_HERE, "libcanopy.so")
 _lib = None
 
-SOLVERS = {"auto": 0, "fwdsub": 1, "neumann": 2, "level": 3, "series": 4, "squaring": 5, "split": 6}
+SOLVERS = {"auto": 0, "fwdsub": 1, "neumann": 2, "level": 3, "series": 4, "squaring": 5, "split": 6,
+           "levelsync": 7}
 # Solvers that keep T x T operators per (sequence, head) in a workspace (canopy_tree_verify_ws).
 WORKSPACE_SOLVERS = ("series", "squaring", "split")
 _FP32, _BF16 = 0, 1

@@ -82,9 +82,11 @@ canopy_status canopy_tree_verify(const void *q, const void *k, const void *v,
     if (!aligned16(q) || !aligned16(k) || !aligned16(v) || !aligned16(S0)) return CANOPY_ERR_ARG;
     if (in_dtype != CANOPY_FP32 && in_dtype != CANOPY_BF16) return CANOPY_ERR_UNSUPPORTED;
     if (solver != CANOPY_SOLVE_AUTO && solver != CANOPY_SOLVE_FWDSUB &&
-        solver != CANOPY_SOLVE_NEUMANN && solver != CANOPY_SOLVE_LEVEL)
+        solver != CANOPY_SOLVE_NEUMANN && solver != CANOPY_SOLVE_LEVEL && solver != CANOPY_SOLVE_LEVELSYNC)
         return CANOPY_ERR_UNSUPPORTED;
     if (waves != 0 && waves != 1 && waves != 2 && waves != 4 && waves != 8) return CANOPY_ERR_UNSUPPORTED;
+    if (solver == CANOPY_SOLVE_LEVELSYNC && (in_dtype != CANOPY_BF16 || (waves != 0 && waves != 8)))
+        return CANOPY_ERR_UNSUPPORTED;
     VerifyArgs a{};
     a.q = q; a.k = k; a.v = v;
     a.alpha = alpha; a.beta = beta; a.S0 = S0; a.parent = parent; a.tree_len = tree_len;
@@ -98,6 +100,7 @@ canopy_status canopy_tree_verify(const void *q, const void *k, const void *v,
     // register kernel (Neumann series in registers). Trees of 17 to 64 nodes run the
     // wave-per-sub-block kernel for AUTO, FWDSUB and NEUMANN. Everything else (LEVEL, and
     // FWDSUB at T <= 16) runs the blocked LDS kernel, which serves any T <= 256.
+    if (solver == CANOPY_SOLVE_LEVELSYNC) return from_hip(launch_verify(a, 8, stream));
     if (T <= 16 && (solver == CANOPY_SOLVE_AUTO || solver == CANOPY_SOLVE_NEUMANN))
         return from_hip(launch_verify_small(a, waves, stream));
     if (T > 16 && T <= 64 && solver != CANOPY_SOLVE_LEVEL)
@@ -209,16 +212,18 @@ canopy_status canopy_commit_verify(const float *S0, const void *k_prev, const fl
     if (!aligned16(q) || !aligned16(k) || !aligned16(v)) return CANOPY_ERR_ARG;
     if (in_dtype != CANOPY_FP32 && in_dtype != CANOPY_BF16) return CANOPY_ERR_UNSUPPORTED;
     if (solver != CANOPY_SOLVE_AUTO && solver != CANOPY_SOLVE_FWDSUB &&
-        solver != CANOPY_SOLVE_NEUMANN && solver != CANOPY_SOLVE_LEVEL)
+        solver != CANOPY_SOLVE_NEUMANN && solver != CANOPY_SOLVE_LEVEL && solver != CANOPY_SOLVE_LEVELSYNC)
         return CANOPY_ERR_UNSUPPORTED;
     if (waves != 0 && waves != 1 && waves != 2 && waves != 4 && waves != 8) return CANOPY_ERR_UNSUPPORTED;
+    if (solver == CANOPY_SOLVE_LEVELSYNC && (in_dtype != CANOPY_BF16 || (waves != 0 && waves != 8)))
+        return CANOPY_ERR_UNSUPPORTED;
     // After a previous tree of at most 64 nodes (one path position per lane): one launch, the
     // committed state kept in registers for the verify, for new trees of at most 16 nodes (AUTO,
     // NEUMANN) and for 17 to 64 nodes where the 17-64 kernel's threads hold at most 2 state
     // pairs (narrow workgroups: up to 32 heads, or 64 at 49-64 nodes). Otherwise the commit
     // kernel, then the verify kernel on the committed state.
     const bool small = T <= 16 && (solver == CANOPY_SOLVE_AUTO || solver == CANOPY_SOLVE_NEUMANN);
-    const bool mid = T > 16 && T <= 64 && solver != CANOPY_SOLVE_LEVEL;
+    const bool mid = T > 16 && T <= 64 && solver != CANOPY_SOLVE_LEVEL && solver != CANOPY_SOLVE_LEVELSYNC;
     if (T_prev <= 64 && (small || mid)) {
         VerifyArgs a{};
         a.q = q; a.k = k; a.v = v;

@@ -389,6 +389,19 @@ __device__ __forceinline__ void dma_v(uint8_t *buf, const void *g, size_t base, 
     }
 }
 
+// Buffer resource over the memory at p (32-bit byte offsets from it, no range limit): a base
+// held in scalar registers, so that per-lane addresses are one 32-bit offset. p must be the
+// same in every lane; it is read from the first active lane, which tells the compiler so (a
+// resource it takes for divergent would turn every access into a loop over lanes).
+typedef __amdgpu_buffer_rsrc_t BufRsrc;
+__device__ __forceinline__ BufRsrc buf_rsrc(const void *p) {
+    const uint64_t v = reinterpret_cast<uint64_t>(p);
+    const uint32_t lo = __builtin_amdgcn_readfirstlane(static_cast<uint32_t>(v));
+    const uint32_t hi = __builtin_amdgcn_readfirstlane(static_cast<uint32_t>(v >> 32));
+    void *u = reinterpret_cast<void *>((static_cast<uint64_t>(hi) << 32) | lo);
+    return __builtin_amdgcn_make_buffer_rsrc(u, 0, -1, 0x00020000);
+}
+
 // Wait until this wave's LDS-bound loads (and other vector memory operations) have completed.
 __device__ __forceinline__ void wait_vmem() { asm volatile("s_waitcnt vmcnt(0)" ::: "memory"); }
 

@@ -23,7 +23,10 @@
 // (and K_0) are requested with LDS-bound loads before the current diagonal block is solved,
 // and K_{c+1} before the couplings to K_c; each wave waits for its own requests before the
 // barrier that ends the pair.
+#include <type_traits>
+
 #include "canopy_kernels.hpp"
+#include "canopy_levelsync.hpp"
 #include "canopy_prep.hpp"
 #include "canopy_stage.hpp"
 
@@ -50,15 +53,33 @@ __global__ __launch_bounds__(NW * 64) void verify_kernel(VerifyArgs a) {
     using BC = BlockCopy<BF, NT>;
     constexpr bool kPF = BC::PER <= 4;  // prefetch blocks through registers (wide workgroups)
 
+    // The level-synchronous gather solve (bf16, all 128 columns in one workgroup, on request)
+    // shares its tables' memory with the blocked solve's staging: a workgroup takes one of the two.
+    constexpr bool kLS = BF && NW == 8;
+
+    struct Blocked {
+        Stage<BF> st;
+        alignas(16) float x[NW][16][XS];
+        int list[NW][64];
+        alignas(16) uint8_t v[NW][64 * 16 * Op::ES];  // V rows x 16 columns
+        alignas(16) uint8_t ka[BLK];
+        alignas(16) uint8_t qa[BLK];
+        alignas(16) uint8_t kb[NB > 1 ? BLK : 16];
+    };
+    union Work {
+        Blocked bl;
+        std::conditional_t<kLS, LsSmem<MAXT>, char> ls;
+    };
     __shared__ PrepSmem<MAXT> ps;
     __shared__ float s_beta[MAXT], s_P[MAXT];
-    __shared__ Stage<BF> st;
-    __shared__ __attribute__((aligned(16))) float s_x[NW][16][XS];
-    __shared__ int s_list[NW][64];
-    __shared__ __attribute__((aligned(16))) uint8_t s_v[NW][64 * 16 * Op::ES];  // V rows x 16 columns
-    __shared__ __attribute__((aligned(16))) uint8_t s_ka[BLK];
-    __shared__ __attribute__((aligned(16))) uint8_t s_qa[BLK];
-    __shared__ __attribute__((aligned(16))) uint8_t s_kb[NB > 1 ? BLK : 16];
+    __shared__ Work wk;
+    Stage<BF> &st = wk.bl.st;
+    float(*s_x)[16][XS] = wk.bl.x;
+    int(*s_list)[64] = wk.bl.list;
+    uint8_t(*s_v)[64 * 16 * Op::ES] = wk.bl.v;
+    uint8_t *s_ka = wk.bl.ka;
+    uint8_t *s_qa = wk.bl.qa;
+    uint8_t *s_kb = wk.bl.kb;
 
     const int g = xcd_remap(blockIdx.x, gridDim.x);
     const int tile = g % TILES;
@@ -143,6 +164,28 @@ __global__ __launch_bounds__(NW * 64) void verify_kernel(VerifyArgs a) {
             if (a.anc_mask)
                 for (int w = 0; w < W; ++w)
                     a.anc_mask[(static_cast<size_t>(b) * T + i) * W + w] = ps.mask[i][w];
+        }
+    }
+    if constexpr (kLS) {
+        // LEVELSYNC takes the gather solve whenever the tree fits its tables (and a sequence's
+        // rows span less than 2^31 bytes, for its 32-bit offsets).
+        const bool fits32 = static_cast<size_t>(T) * rs * 4 < (size_t{1} << 31) &&
+                            static_cast<size_t>(T) * qkrs * 2 < (size_t{1} << 31);
+        if (a.solver == CANOPY_SOLVE_LEVELSYNC && fits32) {
+            const int nbatch = ls_build<MAXT, NT>(wk.ls, ps, s_beta, s_P, pin.p[0], Tb, a.k, qkbase, qkrs);
+            if (nbatch > 0) {
+                const uint16_t *qp = static_cast<const uint16_t *>(a.q);
+                const uint16_t *vp = static_cast<const uint16_t *>(a.v);
+                Sp s0f[4];
+#pragma unroll
+                for (int ks = 0; ks < 4; ++ks) s0f[ks] = Op::split(s0v[ks]);
+                ls_project<MAXT>(wk.ls, s_beta, s_P, qp, vp, qkbase, qkrs, base, rs, col0, s0f, Tb, a.U, a.O);
+                ls_gram<MAXT, NW>(wk.ls, ps, s_beta, qp, qkbase, qkrs, Tb);
+                wait_vmem();      // the parked projections are written, and
+                __syncthreads();  // the pair entries are complete and the staged k is no longer read
+                ls_levels<MAXT, NW>(wk.ls, base, rs, Tb, nbatch, a.U, a.O);
+                return;
+            }
         }
     }
     if constexpr (kPF) {
