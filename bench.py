@@ -1021,10 +1021,38 @@ def main(argv=None):
             r = measure(key, args, baselines=False)
             r.pop("dtype")
             out["extra_workloads"].append(r)
+    if primary:
+        # The streaming copy rate of this GPU, measured in the same run: the practical HBM
+        # ceiling next to the published 8 TB/s (each roofline also gives its share of it).
+        out["copy_gbs"] = copy_rate_gbs()
+        for r in [out] + out["extra_workloads"]:
+            if r.get("roofline", {}).get("unit") == "GB/s":
+                r["roofline"]["copy_frac"] = round(r["roofline"]["achieved"] / out["copy_gbs"], 4)
     if not args.no_cpu:
         out["cpu_baseline"] = cpu_baseline(build_inputs(WORKLOADS[args.workload]), args.cpu_budget)
     print(json.dumps(out), flush=True)
     return 0
+
+
+def copy_rate_gbs(nbytes=2 ** 31, reps=10):
+    """Device-to-device copy of nbytes (fp32, far past the 256 MB Infinity Cache), bytes read
+    plus written per second, in GB/s."""
+    import torch
+    a = torch.empty(nbytes // 4, dtype=torch.float32, device="cuda").fill_(1.0)
+    b = torch.empty_like(a)
+    b.copy_(a)
+    e0 = torch.cuda.Event(enable_timing=True)
+    e1 = torch.cuda.Event(enable_timing=True)
+    torch.cuda.synchronize()
+    e0.record()
+    for _ in range(reps):
+        b.copy_(a)
+    e1.record()
+    torch.cuda.synchronize()
+    t = e0.elapsed_time(e1) / 1000.0 / reps
+    del a, b
+    torch.cuda.empty_cache()
+    return round(2 * nbytes / t / 1e9, 1)
 
 
 def measure(key, args, baselines=True):
