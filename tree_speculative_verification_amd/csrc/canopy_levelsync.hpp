@@ -266,149 +266,170 @@ __device__ void ls_gram(LsSmem<MAXT> &s, const PrepSmem<MAXT> &ps, const float *
 
 // The projections of every node, in index order, for this wave's 16 value columns col0 ..
 // col0+15: r_i = beta_i (v_i - P_i S0^T k_i) into U and P_i S0^T q_i into O, the two values the
-// level loop then completes. k_i from the staged k, q_i and v_i from global memory requested
-// four tiles ahead into a fixed ring of registers. The tile loop has a fixed trip count (MAXT /
-// 16) and fully unrolled, so that the waits for the loads in flight are exact; rows past the
-// tree repeat node n - 1, whose values they then store again unchanged. s0f: the wave's S0
-// columns as split B operands. The caller waits for the stores before the level loop reads
-// them back.
-template <int MAXT>
-__device__ void ls_project(const LsSmem<MAXT> &s, const float *s_beta, const float *s_P, const uint16_t *qp,
+// level loop then completes. k_i from the staged k; q_i through a two-slot ring in LDS that
+// waves 0-3 fill one 16-node tile at a time (each 1 KB of it, requested four tiles ahead into
+// registers), so that every q row is fetched once per workgroup rather than once per wave; v_i
+// from global memory four tiles ahead. The tile loop has a fixed trip count (MAXT / 16), fully
+// unrolled so that the waits for the loads in flight are exact, with a workgroup barrier per
+// tile; rows past the tree repeat node n - 1, whose values they then store again unchanged.
+// s0f: the wave's S0 columns as split B operands. All threads of the workgroup call it. The
+// caller waits for the stores before the level loop reads them back.
+template <int MAXT, int NT>
+__device__ void ls_project(LsSmem<MAXT> &s, const float *s_beta, const float *s_P, const uint16_t *qp,
                            const uint16_t *vp, size_t qkbase, size_t qkrs, size_t base, size_t rs, int col0,
                            const Ops<true>::Sp (&s0f)[4], int n, float *Uo, float *Oo) {
     constexpr int BLK = 64 * Ops<true>::ROWB;
+    constexpr int TILEB = 16 * Ops<true>::ROWB;  // one 16-row tile of q in LDS (4 KB)
     constexpr int NTILE = MAXT / 16;
     constexpr int DIST = 4;
-    const int lane = threadIdx.x & 63;
+    static_assert(static_cast<int>(sizeof(s.utab)) - MAXT * Ops<true>::ROWB >= 2 * TILEB, "room for the q ring");
+    const int lane = threadIdx.x & 63, wave = threadIdx.x >> 6;
     const int lr = lane & 15, lg = lane >> 4;
     const int col = col0 + lr;
+    uint8_t *ring = s.kst + MAXT * Ops<true>::ROWB;  // two q tiles, in the U table's spare memory
     const BufRsrc rq = buf_rsrc(qp + qkbase), rv = buf_rsrc(vp + base);
     const BufRsrc ru = buf_rsrc(Uo + base), ro = buf_rsrc(Oo + base);
     const uint32_t qkb = static_cast<uint32_t>(qkrs) * 2;
     const uint32_t vrs = static_cast<uint32_t>(rs);
-    struct Tile {
-        bf16x8 qa[4];
-        uint16_t v[4];
+    const bool filler = wave < 4;  // waves 0-3 carry the q tiles, 1 KB each
+    // the LDS offset this lane fills within a tile, and the swizzled global chunk that goes there
+    const int fo = 1024 * (wave & 3) + 16 * lane;
+    const int frow = fo / Ops<true>::ROWB, fch = ((fo % Ops<true>::ROWB) >> 4) ^ (frow & 15);
+    auto qload = [&](int t) {
+        const int row = min(16 * t + frow, n - 1);
+        return __builtin_amdgcn_raw_buffer_load_b128(rq, static_cast<uint32_t>(row) * qkb + 16u * fch, 0, 0);
     };
-    auto fetch = [&](int t, Tile &x) {
-        const int ra = min(16 * t + lr, n - 1);
-        const uint32_t vo = static_cast<uint32_t>(ra) * qkb + 16u * lg;
-#pragma unroll
-        for (int ks = 0; ks < 4; ++ks)
-            x.qa[ks] = __builtin_bit_cast(bf16x8, __builtin_amdgcn_raw_buffer_load_b128(rq, vo, 64 * ks, 0));
+    auto qstore = [&](int t, u32x4 x) { *reinterpret_cast<u32x4 *>(ring + (t & 1) * TILEB + fo) = x; };
+    auto vload = [&](int t, uint16_t (&v)[4]) {
 #pragma unroll
         for (int e = 0; e < 4; ++e) {
             const int i = min(16 * t + 4 * lg + e, n - 1);
-            x.v[e] = __builtin_amdgcn_raw_buffer_load_b16(rv, (static_cast<uint32_t>(i) * vrs + col) * 2, 0, 0);
+            v[e] = __builtin_amdgcn_raw_buffer_load_b16(rv, (static_cast<uint32_t>(i) * vrs + col) * 2, 0, 0);
         }
     };
-    auto work = [&](int t, const Tile &x) {
+    auto work = [&](int t, const uint16_t (&v)[4]) {
         const int ra = min(16 * t + lr, n - 1);
         f32x4 ksum = {0.f, 0.f, 0.f, 0.f}, qsum = {0.f, 0.f, 0.f, 0.f};
         f32x4 klo = {0.f, 0.f, 0.f, 0.f}, qlo = {0.f, 0.f, 0.f, 0.f};
 #pragma unroll
         for (int ks = 0; ks < 4; ++ks) {
             const bf16x8 ka = Ops<true>::lds_frag(s.kst + (ra >> 6) * BLK, ra & 63, 4 * ks + lg).x;
+            const bf16x8 qa = Ops<true>::lds_frag(ring + (t & 1) * TILEB, lr, 4 * ks + lg).x;
             ksum = mfma_bf16(ka, s0f[ks].hi, ksum);
             klo = mfma_bf16(ka, s0f[ks].lo, klo);
-            qsum = mfma_bf16(x.qa[ks], s0f[ks].hi, qsum);
-            qlo = mfma_bf16(x.qa[ks], s0f[ks].lo, qlo);
+            qsum = mfma_bf16(qa, s0f[ks].hi, qsum);
+            qlo = mfma_bf16(qa, s0f[ks].lo, qlo);
         }
 #pragma unroll
         for (int e = 0; e < 4; ++e) {
             const int i = min(16 * t + 4 * lg + e, n - 1);
             const float P = s_P[i];
-            const float r = s_beta[i] * (bf16_to_f32(x.v[e]) - P * (ksum[e] + klo[e]));
+            const float r = s_beta[i] * (bf16_to_f32(v[e]) - P * (ksum[e] + klo[e]));
             const float o = P * (qsum[e] + qlo[e]);
             const uint32_t go = (static_cast<uint32_t>(i) * vrs + col) * 4;
             __builtin_amdgcn_raw_buffer_store_b32(__float_as_uint(r), ru, go, 0, 0);
             __builtin_amdgcn_raw_buffer_store_b32(__float_as_uint(o), ro, go, 0, 0);
         }
     };
-    Tile ring[DIST];
+    u32x4 qr[DIST];
+    uint16_t vr[DIST][4];
 #pragma unroll
-    for (int t = 0; t < DIST && t < NTILE; ++t) fetch(t, ring[t]);
+    for (int t = 0; t < DIST && t < NTILE; ++t) {
+        if (filler) qr[t] = qload(t);
+        vload(t, vr[t]);
+    }
+    if (filler) qstore(0, qr[0]);
 #pragma unroll
     for (int t = 0; t < NTILE; ++t) {
-        work(t, ring[t % DIST]);
-        if (t + DIST < NTILE) fetch(t + DIST, ring[t % DIST]);
+        // tile t is in its slot, and every wave is done with tile t - 1, whose slot takes t + 1
+        lds_barrier();
+        if (filler) {
+            if (t + 1 < NTILE) qstore(t + 1, qr[(t + 1) % DIST]);
+            if (t + 1 + DIST - 1 < NTILE) qr[(t + DIST) % DIST] = qload(t + DIST);
+        }
+        work(t, vr[t % DIST]);
+        if (t + DIST < NTILE) vload(t + DIST, vr[t % DIST]);
     }
 }
 
 // The level loop. The levels are taken in order, a workgroup barrier after each (a level reads
 // the u rows of the levels before it); inside a level the waves take its nodes round-robin by
-// level-order position, one node per wave at a time, two value columns per lane. A node's u_i
-// and o_i are completed from the projections (read back from U and O) by the gathers over its
+// level-order position, two nodes per wave at a time (both of depth L, so their gather loops
+// run in step and their LDS round trips overlap), two value columns per lane. A node's u_i and
+// o_i are completed from the projections (read back from U and O) by the gathers over its
 // ancestor entries in fp32: the entries are read once (one lane each) and handed to the whole
-// wave by readlane, so that the LDS traffic is the u rows alone. The projections of the wave's
-// next node are requested while the current one is worked on (two fixed register slots).
-// Global accesses go through buffer resources with 32-bit offsets (the caller checks that one
+// wave by readlane, so that the LDS traffic is the u rows alone. A missing second node reads
+// the entry for a missing row (zero pairs, the spare U-table row) and stores nothing. Global
+// accesses go through buffer resources with 32-bit offsets (the caller checks that one
 // sequence's rows span less than 2^31 bytes).
 template <int MAXT, int NW>
 __device__ void ls_levels(LsSmem<MAXT> &s, size_t base, size_t rs, int n, int nbatch, float *Uo, float *Oo) {
+    using S = LsSmem<MAXT>;
     const int lane = threadIdx.x & 63, wave = threadIdx.x >> 6;
     const BufRsrc ru = buf_rsrc(Uo + base), ro = buf_rsrc(Oo + base);
-    const uint32_t vrs = static_cast<uint32_t>(rs);  // U/O node stride (elements)
+    const uint32_t vrs = static_cast<uint32_t>(rs);
     const int nlev = static_cast<int>(s.batch[nbatch - 1] >> 14) + 1;
     struct Nd {
+        LsNode rd;
         float r0, r1, o0, o1;
+        LsPair pe;
     };
-    auto fetch = [&](int p, Nd &x) {
-        const int i = p < n ? s.rec[p].node : 0;
-        const uint32_t go = (static_cast<uint32_t>(i) * vrs + 2 * lane) * 4;
+    auto open = [&](int p, bool ok, int L, Nd &x) {
+        x.rd = s.rec[ok ? p : MAXT];
+        const uint32_t go = (static_cast<uint32_t>(x.rd.node) * vrs + 2 * lane) * 4;
         x.r0 = __uint_as_float(__builtin_amdgcn_raw_buffer_load_b32(ru, go, 0, 0));
         x.r1 = __uint_as_float(__builtin_amdgcn_raw_buffer_load_b32(ru, go, 4, 0));
         x.o0 = __uint_as_float(__builtin_amdgcn_raw_buffer_load_b32(ro, go, 0, 0));
         x.o1 = __uint_as_float(__builtin_amdgcn_raw_buffer_load_b32(ro, go, 4, 0));
+        x.pe = LsPair{0.f, 0.f, S::NI * S::UST, 0u};
+        if (ok && lane < L) x.pe = s.pairs[x.rd.off + lane];
     };
-    // node at level-order position p (depth L), from its projections x
-    auto node = [&](int p, int L, const Nd &x) {
-        const LsNode rd = s.rec[p];
-        const int off = __builtin_amdgcn_readfirstlane(rd.off);
-        float r0 = x.r0, r1 = x.r1, o0 = x.o0, o1 = x.o1;
-        for (int a0 = 0; a0 < L; a0 += 64) {
-            LsPair pe = {0.f, 0.f, 0, 0u};
-            if (a0 + lane < L) pe = s.pairs[off + a0 + lane];
-            const int na = min(64, L - a0);
-            for (int a = 0; a < na; ++a) {
-                const float g = __int_as_float(__builtin_amdgcn_readlane(__float_as_int(pe.g), a));
-                const float c = __int_as_float(__builtin_amdgcn_readlane(__float_as_int(pe.c), a));
-                const int uo = __builtin_amdgcn_readlane(pe.uoff, a);
-                const float2 ua = *reinterpret_cast<const float2 *>(&s.utab[uo + 2 * lane]);
-                r0 = fmaf(g, ua.x, r0);
-                r1 = fmaf(g, ua.y, r1);
-                o0 = fmaf(c, ua.x, o0);
-                o1 = fmaf(c, ua.y, o1);
-            }
+    auto step = [&](Nd &x, int a) {
+        const float g = __int_as_float(__builtin_amdgcn_readlane(__float_as_int(x.pe.g), a));
+        const float c = __int_as_float(__builtin_amdgcn_readlane(__float_as_int(x.pe.c), a));
+        const int uo = __builtin_amdgcn_readlane(x.pe.uoff, a);
+        const float2 ua = *reinterpret_cast<const float2 *>(&s.utab[uo + 2 * lane]);
+        x.r0 = fmaf(g, ua.x, x.r0);
+        x.r1 = fmaf(g, ua.y, x.r1);
+        x.o0 = fmaf(c, ua.x, x.o0);
+        x.o1 = fmaf(c, ua.y, x.o1);
+    };
+    auto close = [&](Nd &x, bool ok) {
+        x.o0 = fmaf(x.rd.cdiag, x.r0, x.o0);
+        x.o1 = fmaf(x.rd.cdiag, x.r1, x.o1);
+        *reinterpret_cast<float2 *>(&s.utab[x.rd.uoff + 2 * lane]) = make_float2(x.r0, x.r1);
+        if (ok) {
+            const uint32_t go = (static_cast<uint32_t>(x.rd.node) * vrs + 2 * lane) * 4;
+            __builtin_amdgcn_raw_buffer_store_b32(__float_as_uint(x.r0), ru, go, 0, 0);
+            __builtin_amdgcn_raw_buffer_store_b32(__float_as_uint(x.r1), ru, go, 4, 0);
+            __builtin_amdgcn_raw_buffer_store_b32(__float_as_uint(x.o0), ro, go, 0, 2);
+            __builtin_amdgcn_raw_buffer_store_b32(__float_as_uint(x.o1), ro, go, 4, 2);
         }
-        const float cd = rd.cdiag;
-        o0 = fmaf(cd, r0, o0);
-        o1 = fmaf(cd, r1, o1);
-        *reinterpret_cast<float2 *>(&s.utab[rd.uoff + 2 * lane]) = make_float2(r0, r1);
-        const uint32_t go = (static_cast<uint32_t>(rd.node) * vrs + 2 * lane) * 4;
-        __builtin_amdgcn_raw_buffer_store_b32(__float_as_uint(r0), ru, go, 0, 0);
-        __builtin_amdgcn_raw_buffer_store_b32(__float_as_uint(r1), ru, go, 4, 0);
-        // streaming (nt) stores: nothing on the path reads O again
-        __builtin_amdgcn_raw_buffer_store_b32(__float_as_uint(o0), ro, go, 0, 2);
-        __builtin_amdgcn_raw_buffer_store_b32(__float_as_uint(o1), ro, go, 4, 2);
     };
-    Nd xa, xb;
-    int p = wave;
-    fetch(p, xa);
-    fetch(p + NW, xb);
-    bool useb = false;
     for (int L = 0; L < nlev; ++L) {
-        const int end = L + 1 < nlev ? s.lstart[L + 1] : n;  // first position past level L
-        while (p < end) {
-            if (!useb) {
-                node(p, L, xa);
-                fetch(p + 2 * NW, xa);
-            } else {
-                node(p, L, xb);
-                fetch(p + 2 * NW, xb);
+        const int end = L + 1 < nlev ? s.lstart[L + 1] : n;
+        for (int p = s.lstart[L] + wave; p < end; p += 2 * NW) {
+            const bool ok2 = p + NW < end;
+            Nd x, y;
+            open(p, true, L, x);
+            open(p + NW, ok2, L, y);
+            for (int a0 = 0; a0 < L; a0 += 64) {
+                if (a0 > 0) {
+                    x.pe = LsPair{0.f, 0.f, S::NI * S::UST, 0u};
+                    y.pe = x.pe;
+                    if (a0 + lane < L) {
+                        x.pe = s.pairs[x.rd.off + a0 + lane];
+                        if (ok2) y.pe = s.pairs[y.rd.off + a0 + lane];
+                    }
+                }
+                const int na = min(64, L - a0);
+                for (int a = 0; a < na; ++a) {
+                    step(x, a);
+                    step(y, a);
+                }
             }
-            useb = !useb;
-            p += NW;
+            close(x, true);
+            close(y, ok2);
         }
         lds_barrier();
     }

@@ -179,7 +179,7 @@ __global__ __launch_bounds__(NW * 64) void verify_kernel(VerifyArgs a) {
                 Sp s0f[4];
 #pragma unroll
                 for (int ks = 0; ks < 4; ++ks) s0f[ks] = Op::split(s0v[ks]);
-                ls_project<MAXT>(wk.ls, s_beta, s_P, qp, vp, qkbase, qkrs, base, rs, col0, s0f, Tb, a.U, a.O);
+                ls_project<MAXT, NT>(wk.ls, s_beta, s_P, qp, vp, qkbase, qkrs, base, rs, col0, s0f, Tb, a.U, a.O);
                 ls_gram<MAXT, NW>(wk.ls, ps, s_beta, qp, qkbase, qkrs, Tb);
                 wait_vmem();      // the parked projections are written, and
                 __syncthreads();  // the pair entries are complete and the staged k is no longer read
