@@ -40,7 +40,9 @@ constexpr int XS = 68;  // column stride (floats) of the per-wave 64-row x 16-co
 // is never the fastest.
 constexpr int kNeumannMaxDepth = 2;
 
-template <int NW, bool BF, int NB>
+// LS: the instantiation that LEVELSYNC launches, with the gather solve; the others hold the
+// blocked solve alone (so that its code and registers are not shaped by the gather path).
+template <int NW, bool BF, int NB, bool LS>
 __global__ __launch_bounds__(NW * 64) void verify_kernel(VerifyArgs a) {
     using Op = Ops<BF>;
     using In = typename Op::In;
@@ -55,7 +57,7 @@ __global__ __launch_bounds__(NW * 64) void verify_kernel(VerifyArgs a) {
 
     // The level-synchronous gather solve (bf16, all 128 columns in one workgroup, on request)
     // shares its tables' memory with the blocked solve's staging: a workgroup takes one of the two.
-    constexpr bool kLS = BF && NW == 8;
+    constexpr bool kLS = LS && BF && NW == 8;
 
     struct Blocked {
         Stage<BF> st;
@@ -497,7 +499,13 @@ template <int NW, bool BF, int NB>
 static hipError_t launch_nb(const VerifyArgs &a, hipStream_t stream) {
     const int tiles = D / (16 * NW);
     const dim3 grid(static_cast<unsigned>(a.B * a.H * tiles));
-    hipLaunchKernelGGL((verify_kernel<NW, BF, NB>), grid, dim3(NW * 64), 0, stream, a);
+    if constexpr (BF && NW == 8) {
+        if (a.solver == CANOPY_SOLVE_LEVELSYNC) {
+            hipLaunchKernelGGL((verify_kernel<NW, BF, NB, true>), grid, dim3(NW * 64), 0, stream, a);
+            return hipGetLastError();
+        }
+    }
+    hipLaunchKernelGGL((verify_kernel<NW, BF, NB, false>), grid, dim3(NW * 64), 0, stream, a);
     return hipGetLastError();
 }
 
