@@ -163,10 +163,12 @@ __global__ __launch_bounds__(NW * 64) void hybrid_kernel(SerialArgs a) {
             gdn_step(S, cur, o, u);
             const size_t nodeo = base + static_cast<size_t>(node) * rs + col;
             if (rg == 0) {
+                // selected per component: a select of whole float4 values goes through scratch
                 const float qnan = __builtin_nanf("");
-                const float4 nan4 = make_float4(qnan, qnan, qnan, qnan);
-                reinterpret_cast<float4 *>(a.O + nodeo)[0] = lost ? nan4 : o;
-                reinterpret_cast<float4 *>(a.U + nodeo)[0] = lost ? nan4 : u;
+                const float4 ow = make_float4(lost ? qnan : o.x, lost ? qnan : o.y, lost ? qnan : o.z, lost ? qnan : o.w);
+                const float4 uw = make_float4(lost ? qnan : u.x, lost ? qnan : u.y, lost ? qnan : u.z, lost ? qnan : u.w);
+                reinterpret_cast<float4 *>(a.O + nodeo)[0] = ow;
+                reinterpret_cast<float4 *>(a.U + nodeo)[0] = uw;
             }
             if (s_nch[node] >= 2) {  // a fork: light chains start from this state
                 float *dst = a.snap + ((static_cast<size_t>(b) * T + node) * H + h) * SS;
