@@ -183,6 +183,8 @@ def verify_kernel_name(T, solver, heads=0, waves=0, dtype="bf16"):
     if T > 64 and dtype == "bf16" and solver in ("auto", "fwdsub"):
         if waves in (1, 2) or (waves == 0 and heads <= 128):
             return "verify_wide_kernel"
+        if waves == 16 or (waves == 0 and heads > 256):
+            return "verify_dual_kernel"
     return "verify_kernel"
 
 

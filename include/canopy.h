@@ -74,6 +74,11 @@ typedef enum { CANOPY_FP32 = 0, CANOPY_BF16 = 1 } canopy_dtype;
  *  - 65 <= T <= 256 with bf16 inputs (AUTO, FWDSUB), for at most 128 (sequence, head) pairs:
  *    the same wave-per-sub-block forward substitution, with the Gram tiles formed as the
  *    solved tiles arrive (16, 32 or 64 value columns per workgroup).
+ *  - 65 <= T <= 256 with bf16 inputs (AUTO, FWDSUB), for more than 256 pairs: 64-node blocks
+ *    as below with FWDSUB on every diagonal block, in a kernel sized for two workgroups per CU
+ *    (at most 80 KiB of LDS and 128 registers per lane: K_c rows, S0 and the solved U_c are
+ *    read back from the caches instead of held), so that up to 512 pairs run in one pass. Its
+ *    products are bf16 hi + lo matrix-core passes (relative error about 2^-16 per product).
  *  - Otherwise, and for LEVEL: 64-node blocks staged in LDS, the couplings to earlier blocks
  *    applied as matrix-core products; a diagonal block is solved by
  *      FWDSUB   forward substitution over four 16-node sub-blocks on fp32 matrix-core
@@ -174,12 +179,16 @@ canopy_status canopy_tree_prep(const int32_t *parent, const int32_t *tree_len, c
  *               bf16 inputs and takes waves 0 or 8, else CANOPY_ERR_UNSUPPORTED); the matrix
  *               forms need a workspace and go through canopy_tree_verify_ws
  *               (CANOPY_ERR_UNSUPPORTED here).
- *   waves       workgroup width, 1, 2, 4 or 8, or 0 to let the library choose from B, H and T.
+ *   waves       workgroup width, 1, 2, 4, 8 or 16, or 0 to let the library choose from B, H
+ *               and T.
  *               T <= 16 (AUTO, NEUMANN): waves per workgroup, each owning 16 value columns.
  *               17 <= T <= 64 (AUTO, FWDSUB, NEUMANN): 16-column tiles per workgroup, whose
  *               waves each own 16 nodes (8 is taken as 4).
  *               T > 64, bf16, AUTO or FWDSUB: 1 or 2 picks the wave-per-sub-block kernel with
- *               that many 16-column tiles per workgroup, 4 or 8 the blocked kernel.
+ *               that many 16-column tiles per workgroup, 4 or 8 the blocked kernel, 16 the
+ *               blocked kernel sized for two workgroups per CU (8 waves each; 16 needs bf16,
+ *               T > 64, AUTO or FWDSUB and a head's rows of U and O within 2^31 bytes, else
+ *               CANOPY_ERR_UNSUPPORTED).
  *               Otherwise (the blocked kernel): waves per workgroup, each owning 16 value
  *               columns; fp32 inputs use at most 2.
  */

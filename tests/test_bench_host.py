@@ -82,6 +82,9 @@ def test_verify_flops_dense_tile():
     (128, "auto", 64, 0, "bf16", "verify_wide_kernel"),
     (128, "auto", 128, 0, "bf16", "verify_wide_kernel"),
     (128, "auto", 256, 0, "bf16", "verify_kernel"),
+    (128, "auto", 257, 0, "bf16", "verify_dual_kernel"),
+    (256, "fwdsub", 32, 16, "bf16", "verify_dual_kernel"),
+    (256, "auto", 512, 8, "bf16", "verify_kernel"),
     (100, "split", 512, 0, "bf16", "mat_apply_kernel"),
     (256, "fwdsub", 512, 2, "bf16", "verify_wide_kernel"),
     (256, "auto", 32, 0, "fp32", "verify_kernel"),

@@ -172,8 +172,8 @@ def test_malformed_tree(canopy):
 
 
 def test_agrees_with_blocked_solve(canopy):
-    """With more than 128 (sequence, head) pairs AUTO runs the blocked kernel's blocked solve:
-    the gather solve agrees with it to well inside the bf16 tolerance (both in fp32
+    """With more than 128 (sequence, head) pairs AUTO runs the blocked solve (forward
+    substitution over 16-node sub-blocks of 64-node blocks): the gather solve agrees with it to well inside the bf16 tolerance (both in fp32
     arithmetic from the same bf16 inputs)."""
     inp = synth.make_inputs(5, 32, 200, tree="random", dtype="bf16", seed=990)
     d = to_device(inp)

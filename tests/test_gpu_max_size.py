@@ -1,6 +1,7 @@
 """The largest arrays the ABI accepts in practice: B = 4096 sequences of 256 nodes and 32 heads,
 so that q, k, v, O and U hold 2^32 elements each and every index past 2^31 is taken by the
-64-bit address arithmetic of the blocked verify kernel and the commit. Inputs are drawn on the
+64-bit address arithmetic of the verify kernel AUTO picks there (the blocked solve for two
+workgroups per CU: 64-bit bases per (sequence, head), 32-bit offsets within one) and the commit. Inputs are drawn on the
 device from a seeded generator (the same distributions as the synthetic recipe: L2-normalized
 Gaussian q and k, Gaussian v, sigmoid beta, exp(-softplus) alpha, S0 ~ N(0, 0.1^2), random
 recursive trees); the oracle runs on sampled (sequence, head) pairs, the last one included.

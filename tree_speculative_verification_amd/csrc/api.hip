@@ -40,6 +40,13 @@ int pick_waves(canopy_dtype dt) { return dt == CANOPY_BF16 ? 8 : 2; }
 // 45.1 us with 4 column tiles against 55.6 us blocked, T = 128 23.8 against 26.9 us.
 constexpr long long kWideMaxHeads = 128;
 
+// Beyond this many (sequence, head) pairs (more workgroups than CUs, so the one-per-CU blocked
+// kernel would run a second pass) trees of 65 to 256 nodes run the blocked solve sized for two
+// workgroups per CU. Measured on MI355X at H = 32, T = 256: B = 16 103-108 us against 115 us
+// for the blocked kernel; at B = 8 (256 pairs) the blocked kernel's single pass wins, 60 us
+// against 73 us.
+constexpr long long kDualMinHeads = 257;
+
 }  // namespace
 
 extern "C" {
@@ -84,8 +91,12 @@ canopy_status canopy_tree_verify(const void *q, const void *k, const void *v,
     if (solver != CANOPY_SOLVE_AUTO && solver != CANOPY_SOLVE_FWDSUB &&
         solver != CANOPY_SOLVE_NEUMANN && solver != CANOPY_SOLVE_LEVEL && solver != CANOPY_SOLVE_LEVELSYNC)
         return CANOPY_ERR_UNSUPPORTED;
-    if (waves != 0 && waves != 1 && waves != 2 && waves != 4 && waves != 8) return CANOPY_ERR_UNSUPPORTED;
+    if (waves != 0 && waves != 1 && waves != 2 && waves != 4 && waves != 8 && waves != 16)
+        return CANOPY_ERR_UNSUPPORTED;
     if (solver == CANOPY_SOLVE_LEVELSYNC && (in_dtype != CANOPY_BF16 || (waves != 0 && waves != 8)))
+        return CANOPY_ERR_UNSUPPORTED;
+    if (waves == 16 && (in_dtype != CANOPY_BF16 || T <= 64 || !dual_fits(H, HV, T) ||
+                        (solver != CANOPY_SOLVE_AUTO && solver != CANOPY_SOLVE_FWDSUB)))
         return CANOPY_ERR_UNSUPPORTED;
     VerifyArgs a{};
     a.q = q; a.k = k; a.v = v;
@@ -106,16 +117,20 @@ canopy_status canopy_tree_verify(const void *q, const void *k, const void *v,
     if (T > 16 && T <= 64 && solver != CANOPY_SOLVE_LEVEL)
         return from_hip(launch_verify_mid(a, waves == 8 ? 4 : waves, stream));
     // Trees of 65 to 256 nodes with bf16 inputs, AUTO or FWDSUB: the wave-per-sub-block kernel
-    // (one workgroup per head and 16 or 32 value columns) while there are few heads, the
-    // blocked kernel (one workgroup per head and all columns, no repeated Gram work) beyond.
-    // An explicit width picks the kernel: 1 or 2 column tiles, or 4 or 8 blocked waves.
+    // (one workgroup per head and 16 to 64 value columns) while there are few heads, the
+    // blocked kernel (one workgroup per head and all columns, no repeated Gram work) beyond,
+    // and past one workgroup per CU the blocked solve sized for two workgroups per CU.
+    // An explicit width picks the kernel: 1 or 2 column tiles, 4 or 8 blocked waves, or 16
+    // for the two-per-CU blocked kernel.
     if (T > 64 && in_dtype == CANOPY_BF16 &&
         (solver == CANOPY_SOLVE_AUTO || solver == CANOPY_SOLVE_FWDSUB)) {
         if (waves == 1 || waves == 2) return from_hip(launch_verify_wide(a, waves, stream));
+        if (waves == 16) return from_hip(launch_verify_dual(a, stream));
         if (waves == 0) {
             const long long heads = static_cast<long long>(B) * HV;
             if (heads <= kWideMaxHeads)
                 return from_hip(launch_verify_wide(a, heads <= 32 ? 1 : (heads <= 64 ? 2 : 4), stream));
+            if (heads >= kDualMinHeads && dual_fits(H, HV, T)) return from_hip(launch_verify_dual(a, stream));
         }
     }
     return from_hip(launch_verify(a, waves ? waves : pick_waves(in_dtype), stream));
@@ -214,8 +229,12 @@ canopy_status canopy_commit_verify(const float *S0, const void *k_prev, const fl
     if (solver != CANOPY_SOLVE_AUTO && solver != CANOPY_SOLVE_FWDSUB &&
         solver != CANOPY_SOLVE_NEUMANN && solver != CANOPY_SOLVE_LEVEL && solver != CANOPY_SOLVE_LEVELSYNC)
         return CANOPY_ERR_UNSUPPORTED;
-    if (waves != 0 && waves != 1 && waves != 2 && waves != 4 && waves != 8) return CANOPY_ERR_UNSUPPORTED;
+    if (waves != 0 && waves != 1 && waves != 2 && waves != 4 && waves != 8 && waves != 16)
+        return CANOPY_ERR_UNSUPPORTED;
     if (solver == CANOPY_SOLVE_LEVELSYNC && (in_dtype != CANOPY_BF16 || (waves != 0 && waves != 8)))
+        return CANOPY_ERR_UNSUPPORTED;
+    if (waves == 16 && (in_dtype != CANOPY_BF16 || T <= 64 || !dual_fits(H, HV, T) ||
+                        (solver != CANOPY_SOLVE_AUTO && solver != CANOPY_SOLVE_FWDSUB)))
         return CANOPY_ERR_UNSUPPORTED;
     // After a previous tree of at most 64 nodes (one path position per lane): one launch, the
     // committed state kept in registers for the verify, for new trees of at most 16 nodes (AUTO,

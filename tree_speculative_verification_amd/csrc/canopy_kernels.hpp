@@ -147,6 +147,10 @@ bool commit_verify_mid_fits(const VerifyArgs &a, int col_tiles);
 hipError_t launch_commit_verify_mid(const VerifyArgs &a, const PrevCommitArgs &c, int col_tiles,
                                     hipStream_t stream);
 hipError_t launch_verify_wide(const VerifyArgs &a, int col_tiles, hipStream_t stream);
+// The blocked solve sized for two workgroups per CU (bf16, 65 <= T <= 256, FWDSUB on every
+// diagonal block); dual_fits: a head's rows span less than 2^31 bytes (32-bit offsets).
+hipError_t launch_verify_dual(const VerifyArgs &a, hipStream_t stream);
+bool dual_fits(int HK, int HV, int T);
 // Matrix-form solves (SERIES, SQUARING, SPLIT) with their operators in a workspace of
 // mat_workspace_bytes bytes.
 size_t mat_workspace_bytes(int B, int H, int T, int solver);
