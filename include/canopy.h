@@ -73,7 +73,8 @@ typedef enum { CANOPY_FP32 = 0, CANOPY_BF16 = 1 } canopy_dtype;
  *    sub-block's depth; NEUMANN sums the whole tree's series, one term per tree level.
  *  - 65 <= T <= 256 with bf16 inputs (AUTO, FWDSUB), for at most 128 (sequence, head) pairs:
  *    the same wave-per-sub-block forward substitution, with the Gram tiles formed as the
- *    solved tiles arrive (16, 32 or 64 value columns per workgroup).
+ *    solved tiles arrive (16, 32 or 64 value columns per workgroup); the products of its
+ *    sequential chain are bf16 hi + lo matrix-core passes (relative error about 2^-16).
  *  - 65 <= T <= 256 with bf16 inputs (AUTO, FWDSUB), for more than 256 pairs: 64-node blocks
  *    as below with FWDSUB on every diagonal block, in a kernel sized for two workgroups per CU
  *    (at most 80 KiB of LDS and 128 registers per lane: K_c rows, S0 and the solved U_c are

@@ -16,7 +16,9 @@
 //          needed. The Gram tiles G_pc, C_pc are formed one at a time as U_c arrives (K_c as
 //          the A operand, so each tile lands in the A placement of a 16-long reduction); the
 //          tile needed last, (p, p-1), is formed first so that the sequential part is two
-//          fp32-MFMA products per sub-block. Solved tiles pass between waves through LDS flags.
+//          products per sub-block. Solved tiles pass between waves through LDS flags, as bf16
+//          hi + lo parts; every 16-long product of the chain takes three bf16 matrix-core passes
+//          (hi hi + hi lo + lo hi, relative error about 2^-16).
 //   a5     O_p = diag(P) Q_p S0 + sum_{c<=p} C_pc U_c, accumulated as the U_c arrive
 // Node-by-column tiles (R, U) sit with rows 4g..4g+3 of column r in lane (g, r), the result
 // placement of an MFMA and the B placement of the 16-long reduction.
@@ -34,7 +36,7 @@ struct WideSmem {
     uint8_t k[WMAXT * Ops<true>::ROWB];
     union {
         uint8_t s0[16 * NCT * 512];  // S0 columns as bf16 hi rows, then lo rows
-        float4 x[WMAXT / 16][NCT][64];
+        float4 x[WMAXT / 16][NCT][64];  // solved U tiles as bf16 hi (8 bytes) + lo (8 bytes)
     } u;
     double lam[WMAXT];
     uint32_t mask[WMAXT][WMW];
@@ -76,6 +78,23 @@ __device__ __forceinline__ void wide_tile(const WideSmem<NCT> &sm, const Ops<tru
         g[e] = (onpath && i != j0 + e) ? -bi * gam * kk[e] : 0.f;
     }
     kk_out = kk;
+}
+
+// A solved U tile (rows 4 lg .. 4 lg + 3 of column lr in lane (lg, lr)) as bf16 hi and lo parts,
+// 16 bytes per lane in the tile's LDS slot.
+template <int NCT>
+__device__ __forceinline__ void wide_put_tile(WideSmem<NCT> &sm, int s, int ct, int lane, Ops<true>::Sp4 t) {
+    const uint2 h = __builtin_bit_cast(uint2, t.hi), l = __builtin_bit_cast(uint2, t.lo);
+    sm.u.x[s][ct][lane] = make_float4(__uint_as_float(h.x), __uint_as_float(h.y), __uint_as_float(l.x),
+                                      __uint_as_float(l.y));
+}
+template <int NCT>
+__device__ __forceinline__ Ops<true>::Sp4 wide_get_tile(const WideSmem<NCT> &sm, int s, int ct, int lane) {
+    const float4 x = sm.u.x[s][ct][lane];
+    Ops<true>::Sp4 t;
+    t.hi = __builtin_bit_cast(i16x4, make_uint2(__float_as_uint(x.x), __float_as_uint(x.y)));
+    t.lo = __builtin_bit_cast(i16x4, make_uint2(__float_as_uint(x.z), __float_as_uint(x.w)));
+    return t;
 }
 
 template <int NCT>
@@ -348,35 +367,39 @@ __global__ __launch_bounds__(1024) void verify_wide_kernel(VerifyArgs a) {
                 cm[e] = clast[e];
             }
         }
+        const Op::Sp4 gs = Op::split4(g), cs = Op::split4(cm);
         lost |= wait_flag(&sm.ready[s], a.wait_bound) != 1;
 #pragma unroll
         for (int ct = 0; ct < NCT; ++ct) {
-            const float4 t = sm.u.x[s][ct][lane];
-            const float tv[4] = {t.x, t.y, t.z, t.w};
-            const f32x4 r = mma16f(g, tv, f32x4{rhs[ct][0], rhs[ct][1], rhs[ct][2], rhs[ct][3]});
+            const Op::Sp4 tv = wide_get_tile(sm, s, ct, lane);
+            const f32x4 r = Op::mma16(gs, tv, f32x4{rhs[ct][0], rhs[ct][1], rhs[ct][2], rhs[ct][3]});
 #pragma unroll
             for (int e = 0; e < 4; ++e) rhs[ct][e] = r[e];
-            if (s + 1 < p) oacc[ct] = mma16f(cm, tv, oacc[ct]);
+            if (s + 1 < p) oacc[ct] = Op::mma16(cs, tv, oacc[ct]);
         }
     }
     float u[NCT][4];
+    Op::Sp4 us[NCT];
+    {
+        const Op::Sp4 ms = Op::split4(minv);
 #pragma unroll
-    for (int ct = 0; ct < NCT; ++ct) {
-        const f32x4 y = mma16f(minv, rhs[ct], f32x4{0.f, 0.f, 0.f, 0.f});
+        for (int ct = 0; ct < NCT; ++ct) {
+            const f32x4 y = Op::mma16(ms, Op::split4(rhs[ct]), f32x4{0.f, 0.f, 0.f, 0.f});
 #pragma unroll
-        for (int e = 0; e < 4; ++e) u[ct][e] = y[e];
-        sm.u.x[p][ct][lane] = make_float4(u[ct][0], u[ct][1], u[ct][2], u[ct][3]);
+            for (int e = 0; e < 4; ++e) u[ct][e] = y[e];
+            us[ct] = Op::split4(u[ct]);
+            wide_put_tile(sm, p, ct, lane, us[ct]);
+        }
     }
     __hip_atomic_store(&sm.ready[p], lost ? 2 : 1, __ATOMIC_RELEASE, __HIP_MEMORY_SCOPE_WORKGROUP);
     // ---- a5: the read-out terms left: the last incoming tile and the wave's own
+    {
+        const Op::Sp4 cl = Op::split4(clast), cd = Op::split4(cdiag);
 #pragma unroll
-    for (int ct = 0; ct < NCT; ++ct) {
-        if (p >= 1) {
-            const float4 t = sm.u.x[p - 1][ct][lane];
-            const float tv[4] = {t.x, t.y, t.z, t.w};
-            oacc[ct] = mma16f(clast, tv, oacc[ct]);
+        for (int ct = 0; ct < NCT; ++ct) {
+            if (p >= 1) oacc[ct] = Op::mma16(cl, wide_get_tile(sm, p - 1, ct, lane), oacc[ct]);
+            oacc[ct] = Op::mma16(cd, us[ct], oacc[ct]);
         }
-        oacc[ct] = mma16f(cdiag, u[ct], oacc[ct]);
     }
 
     // ---- a6: outputs (NaN for a malformed tree and for rows computed from a lost hand-off)
