@@ -104,6 +104,14 @@ def _mid_col_tiles(heads, waves):
     return 1 if heads <= 32 else (2 if heads <= 64 else 4)
 
 
+def _step_col_tiles(T, heads, waves):
+    """The column tiles canopy_commit_verify gives the 17-64-node kernel: as the verify alone,
+    except 2 (the one-launch form) at 49-64 nodes and 65-128 heads with waves 0."""
+    if waves == 0 and T > 48 and 64 < heads <= 128:
+        return 2
+    return _mid_col_tiles(heads, waves)
+
+
 def one_launch_step(T, solver, heads=32, waves=0):
     """Whether canopy_commit_verify runs the step as one launch (after previous trees of at most
     64 nodes): trees of at most 16 nodes (AUTO, NEUMANN), and trees of 17 to 64 nodes (not
@@ -113,7 +121,7 @@ def one_launch_step(T, solver, heads=32, waves=0):
     if T <= 16:
         return solver in ("auto", "neumann")
     if T <= 64 and solver != "level":
-        return 4 * _mid_col_tiles(heads, waves) <= 2 * ((T + 15) // 16)
+        return 4 * _step_col_tiles(T, heads, waves) <= 2 * ((T + 15) // 16)
     return False
 
 
@@ -122,7 +130,7 @@ def fused_kernel_name(T, dtype="bf16", heads=32, waves=0):
     bf = "true" if dtype == "bf16" else "false"
     if T <= 16:
         return "canopy::verify_small_kernel<%s, %d, true>" % (bf, waves if waves else 1)
-    return "canopy::verify_mid_kernel<%s, %d, %d, true>" % (bf, (T + 15) // 16, _mid_col_tiles(heads, waves))
+    return "canopy::verify_mid_kernel<%s, %d, %d, true>" % (bf, (T + 15) // 16, _step_col_tiles(T, heads, waves))
 
 
 def verify_flops_ragged(H, lens):

@@ -284,7 +284,7 @@ canopy_status canopy_commit(const float *S0, const void *k, canopy_dtype in_dtyp
  * previous tree of at most 64 nodes, both run in one launch and the committed state goes from
  * registers straight into the verify for new trees of at most 16 nodes (AUTO or NEUMANN) and
  * for 17 to 64 nodes (not LEVEL) when the 17-64 kernel's workgroups are narrow (B*HV <= 32, or
- * <= 64 at 49-64 nodes, with waves 0; or waves 1, or 2 at 49-64 nodes); otherwise the two
+ * <= 128 at 49-64 nodes, with waves 0; or waves 1, or 2 at 49-64 nodes); otherwise the two
  * kernels run one after the other on the stream.
  *   S0, k_prev, U_prev, alpha_prev, parent_prev, tree_len_prev, path, path_len: as S0, k, U,
  *               alpha, parent, tree_len, path and path_len of canopy_commit, for the previous

@@ -55,7 +55,9 @@ def test_fused_step_bytes_c2():
     (16, "auto", 32, 0, True), (7, "neumann", 512, 0, True), (16, "fwdsub", 32, 0, False),
     (16, "level", 32, 0, False), (17, "auto", 32, 0, True), (64, "auto", 32, 0, True),
     (64, "fwdsub", 64, 0, True), (64, "auto", 512, 0, False), (40, "auto", 64, 0, False),
-    (64, "level", 32, 0, False), (64, "auto", 32, 8, False), (256, "auto", 32, 0, False)])
+    (64, "level", 32, 0, False), (64, "auto", 32, 8, False), (256, "auto", 32, 0, False),
+    (64, "auto", 128, 0, True), (49, "auto", 96, 0, True), (48, "auto", 128, 0, False),
+    (64, "auto", 129, 0, False)])
 def test_one_launch_step_follows_the_dispatch(T, solver, heads, waves, one):
     assert bench.one_launch_step(T, solver, heads, waves) == one
 
@@ -65,6 +67,7 @@ def test_fused_kernel_name():
     assert bench.fused_kernel_name(7, "fp32", 2, 8) == "canopy::verify_small_kernel<false, 8, true>"
     assert bench.fused_kernel_name(64, "bf16", 32) == "canopy::verify_mid_kernel<true, 4, 1, true>"
     assert bench.fused_kernel_name(64, "bf16", 64) == "canopy::verify_mid_kernel<true, 4, 2, true>"
+    assert bench.fused_kernel_name(64, "bf16", 128) == "canopy::verify_mid_kernel<true, 4, 2, true>"
 
 
 def test_verify_flops_dense_tile():

@@ -198,7 +198,7 @@ def test_in_place_and_shared_U(canopy):
         assert np.array_equal(a[name], b[name], equal_nan=True), name
 
 
-@pytest.mark.parametrize("B,H,Tp,T", [(2, 4, 100, 16), (2, 4, 64, 130), (3, 16, 16, 40), (2, 48, 30, 64),
+@pytest.mark.parametrize("B,H,Tp,T", [(2, 4, 100, 16), (2, 4, 64, 130), (3, 16, 16, 40), (3, 48, 30, 64),
                                      (2, 4, 100, 40)])
 def test_two_launch_form(canopy, B, H, Tp, T):
     """Shapes outside the one-launch forms (a previous tree past 64 nodes, a new tree past 64,
@@ -225,6 +225,20 @@ def test_mid_one_launch(canopy, T, Tp, plen, dtype):
     _check(r, prev, new, dtype)
     if plen == 0:
         assert np.array_equal(r["S"], prev["S0"].astype(np.float32)), "an empty path must keep S0"
+    s = _separate(canopy, r)
+    for name in ("S", "O", "U"):
+        err = np.max(np.abs(r[name] - s[name])) / max(1e-30, np.max(np.abs(s[name])))
+        assert err < 1e-5, f"{name}: fused and separate differ by {err:.2e}"
+
+
+@pytest.mark.parametrize("B,H,T,Tp", [(2, 48, 64, 30), (4, 32, 64, 64), (2, 64, 49, 20)])
+def test_mid_one_launch_two_tiles(canopy, B, H, T, Tp):
+    """The one-launch form at two column tiles per workgroup (65-128 heads, 49-64 nodes): against
+    the oracle and the two separate calls."""
+    prev, new = _pair(B, H, Tp, T, "bf16", 6750 + B * H + T)
+    _say("17-64 one launch, two tiles", B, H, T, Tp)
+    r = _run(canopy, prev, new)
+    _check(r, prev, new, "bf16")
     s = _separate(canopy, r)
     for name in ("S", "O", "U"):
         err = np.max(np.abs(r[name] - s[name])) / max(1e-30, np.max(np.abs(s[name])))

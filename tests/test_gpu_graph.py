@@ -8,8 +8,8 @@ replays it four times. Before each replay the static inputs are overwritten with
 seeded input sets and the outputs with NaN, and unrelated eager work runs between replays;
 after each replay the outputs must equal those of eager calls on the same input set. The first
 replay is also checked against the oracle. One case per verify kernel (at most 16 nodes, 17 to
-64 nodes, 65 to 256 nodes with few heads, the blocked kernel in bf16 and fp32), plus a ragged
-batch."""
+64 nodes, 65 to 256 nodes with few heads, the blocked kernel in bf16 and fp32, the blocked solve
+sized for two workgroups per CU), plus a ragged batch."""
 from __future__ import annotations
 
 import numpy as np
@@ -66,6 +66,7 @@ CASES = [
     (2, 8, 40, "random", "bf16", "auto", 0, None, None),
     (1, 8, 130, "random", "bf16", "auto", 0, None, None),
     (2, 8, 130, "random", "bf16", "auto", 8, 4, None),
+    (2, 8, 200, "random", "bf16", "fwdsub", 16, 4, None),
     (2, 4, 100, "skewed", "fp32", "level", 0, None, None),
     (3, 4, 90, "random", "bf16", "auto", 0, 2, [90, 17, 1]),
 ]

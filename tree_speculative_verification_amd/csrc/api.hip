@@ -239,7 +239,7 @@ canopy_status canopy_commit_verify(const float *S0, const void *k_prev, const fl
     // After a previous tree of at most 64 nodes (one path position per lane): one launch, the
     // committed state kept in registers for the verify, for new trees of at most 16 nodes (AUTO,
     // NEUMANN) and for 17 to 64 nodes where the 17-64 kernel's threads hold at most 2 state
-    // pairs (narrow workgroups: up to 32 heads, or 64 at 49-64 nodes). Otherwise the commit
+    // pairs (narrow workgroups: up to 32 heads, or 128 at 49-64 nodes). Otherwise the commit
     // kernel, then the verify kernel on the committed state.
     const bool small = T <= 16 && (solver == CANOPY_SOLVE_AUTO || solver == CANOPY_SOLVE_NEUMANN);
     const bool mid = T > 16 && T <= 64 && solver != CANOPY_SOLVE_LEVEL && solver != CANOPY_SOLVE_LEVELSYNC;
@@ -256,7 +256,12 @@ canopy_status canopy_commit_verify(const float *S0, const void *k_prev, const fl
         const PrevCommitArgs c{k_prev, U_prev, alpha_prev, parent_prev, tree_len_prev, path,
                                path_len, T_prev, S_new, path_status};
         if (small) return from_hip(launch_commit_verify_small(a, c, waves, stream));
-        const int col_tiles = waves == 8 ? 4 : waves;
+        int col_tiles = waves == 8 ? 4 : waves;
+        // 65 to 128 heads at 49-64 nodes: the one launch at 2 column tiles per workgroup beats
+        // the two launches at the 4 the verify alone would take (measured at B = 4, H = 32,
+        // T = 64: 18.6 against 20.0 us per step).
+        const long long heads = static_cast<long long>(B) * HV;
+        if (waves == 0 && T > 48 && heads > 64 && heads <= 128) col_tiles = 2;
         if (commit_verify_mid_fits(a, col_tiles))
             return from_hip(launch_commit_verify_mid(a, c, col_tiles, stream));
     }
