@@ -12,7 +12,9 @@
 //   registers RHS_r and the read-out O_r of the current block (the wave's columns)
 //   re-read   the wave's S0 columns once per block, K_c rows of the wave's Gram tiles for an
 //             earlier block c, and the solved U_c of its columns (its own stores, for the
-//             couplings), all from the caches
+//             couplings): 576 KiB per (sequence, head) at T = 256, which miss the L2 and about
+//             double the bytes the kernel moves; it still runs faster than the one-workgroup-
+//             per-CU kernel that holds them
 // Per block r: a2 projections R_r = beta (V_r - P K_r S0), O_r = P Q_r S0; for each c < r the
 // Gram pair (r, c) staged, then RHS_r -= G_rc U_c and O_r += C_rc U_c; the diagonal pair (r, r)
 // staged, its 16 x 16 diagonal sub-blocks inverted (squaring form), forward substitution over
@@ -72,8 +74,6 @@ __device__ __forceinline__ void dual_lane(int lr0, int lg0, int &lr, int &lg) {
     asm volatile("" : "+v"(lr), "+v"(lg));
 }
 
-}  // namespace
-
 // The staged -G (or its diagonal inverses) at row r, columns c0 .. c0 + 3 as the hi and lo bf16
 // parts of a 16-long reduction's A operand.
 __device__ __forceinline__ Ops<true>::Sp4 dual_stage4(const Stage<true> &st, int r, int c0) {
@@ -83,6 +83,8 @@ __device__ __forceinline__ Ops<true>::Sp4 dual_stage4(const Stage<true> &st, int
     s.lo = __builtin_bit_cast(i16x4, *reinterpret_cast<const uint2 *>(st.gl + o));
     return s;
 }
+
+}  // namespace
 
 template <int NB>
 __global__ __launch_bounds__(kDualNT) __attribute__((amdgpu_waves_per_eu(4)))
@@ -233,17 +235,7 @@ void verify_dual_kernel(VerifyArgs a) {
             const bool diag = c == r;
             int lr, lg;
             dual_lane(lr0, lg0, lr, lg);
-            // U_c of the wave's columns as the couplings' B operands (node rows 32 ks + 8 lg + e;
-            // every row of an earlier block lies below Tb)
-            float ucr[2][8];
-            if (!diag) {
-#pragma unroll
-                for (int ks = 0; ks < 2; ++ks)
-#pragma unroll
-                    for (int e = 0; e < 8; ++e)
-                        ucr[ks][e] = __uint_as_float(
-                            __builtin_amdgcn_raw_buffer_load_b32(ru, vo_uc, (64 * c + 32 * ks + e) * vrow, 0));
-            }
+            float ucr[2][8];  // U_c for the couplings, requested once the Gram products are issued
             In kf[4];
             if (diag) {
 #pragma unroll
@@ -291,6 +283,18 @@ void verify_dual_kernel(VerifyArgs a) {
                     gv[e] = (on && i != jb + e) ? -bi * gam * kk[e] : 0.f;
                 }
                 st.store4(16 * ti + lr, 16 * tj + 4 * lg, gv, cv);
+            }
+            // U_c of the wave's columns as the couplings' B operands (node rows 32 ks + 8 lg + e;
+            // every row of an earlier block lies below Tb). Requested here rather than with the
+            // key rows, they do not hold 16 registers through the Gram products (2% faster at
+            // B = 16, T = 256).
+            if (!diag) {
+#pragma unroll
+                for (int ks = 0; ks < 2; ++ks)
+#pragma unroll
+                    for (int e = 0; e < 8; ++e)
+                        ucr[ks][e] = __uint_as_float(
+                            __builtin_amdgcn_raw_buffer_load_b32(ru, vo_uc, (64 * c + 32 * ks + e) * vrow, 0));
             }
             lds_barrier();
 
