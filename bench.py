@@ -12,7 +12,8 @@ it, and so is the serial fork baseline. Inputs are resident in HBM before the ti
 timed region holds exactly --steps steps between two stream synchronisations, timed with HIP
 events on the launch stream. The steps are captured once into a HIP graph and the timed region
 is one replay of it (the kernels are short enough at B=1 that launching them one by one from
-Python would time the host); --eager launches them one by one instead.
+Python would time the host), after untimed replays of at least 30 ms of GPU time that let the
+clocks settle; --eager launches them one by one instead.
 
 Prints one JSON line. The default workload is the 9B-shaped layer: B=1, H=32, d=128, T=16
 top-k tree (root, 3 children, 4 children each), bf16 q/k/v, fp32 state.
@@ -24,6 +25,7 @@ import csv
 import hashlib
 import json
 import os
+import re
 import sys
 import time
 
@@ -125,11 +127,22 @@ def one_launch_step(T, solver, heads=32, waves=0):
     return False
 
 
+def small_width(heads, waves, fuse, dtype="bf16"):
+    """(waves per workgroup, column tiles per wave) of the T <= 16 kernel, as the library picks
+    them: waves 16 is single-wave workgroups on two column tiles; waves 0 takes two tiles for
+    bf16 inputs once single-tile waves fill one pass or more (3 per SIMD for the one-launch
+    step, 4 for the verify alone, on 1024 SIMDs)."""
+    if waves == 0:
+        waves = 16 if dtype == "bf16" and heads * 8 >= 1024 * (3 if fuse else 4) else 1
+    return (1, 2) if waves == 16 else (waves, 1)
+
+
 def fused_kernel_name(T, dtype="bf16", heads=32, waves=0):
     """The one-launch step's kernel as the profiler names it."""
     bf = "true" if dtype == "bf16" else "false"
     if T <= 16:
-        return "canopy::verify_small_kernel<%s, %d, true>" % (bf, waves if waves else 1)
+        nwv, nct = small_width(heads, waves, True, dtype)
+        return "canopy::verify_small_kernel<%s, %d, true, %d>" % (bf, nwv, nct)
     return "canopy::verify_mid_kernel<%s, %d, %d, true>" % (bf, (T + 15) // 16, _step_col_tiles(T, heads, waves))
 
 
@@ -259,7 +272,10 @@ def pmc_summary(run_dir, out_path):
         wscale = probe / 1024.0 / max(w["__amd_rocclr_copyBuffer"])
         ent = {"config": rec["config"], "fetch_scale": round(fscale, 4), "write_scale": round(wscale, 4)}
         def is_fused(k):
-            return k.startswith("void canopy::verify") and ", true>(" in k
+            # the FUSE argument: third of verify_small_kernel<BF, NWV, FUSE, NCT>, last of
+            # verify_mid_kernel<BF, NSB, NCT, FUSE>
+            return re.match(r"void canopy::(verify_small_kernel<\w+, \d+, true[,>]|"
+                            r"verify_mid_kernel<\w+, \d+, \d+, true>)", k) is not None
         roles = (("verify", lambda k: k.startswith("void canopy::verify") and not is_fused(k), True),
                  ("commit", lambda k: k.startswith("void canopy::commit_kernel<"), True),
                  ("fused", is_fused, False))
@@ -466,14 +482,27 @@ def graph_of(fn, n):
     return g
 
 
-def time_graph(g, n):
-    """Average µs per call of a graph of n calls: one replay between two events on the stream
-    the replay runs on, synchronised on both sides."""
+SETTLE_MS = 30.0  # untimed GPU time before a timed replay
+
+
+def time_graph(g, n, settle_ms=SETTLE_MS):
+    """Average µs per call of a graph of n calls: untimed replays until ``settle_ms`` of GPU time
+    has run (at least one), then one replay between two events on the stream the replay runs
+    on, synchronised on both sides. The GPU's clocks take about 15 ms of sustained work to
+    settle: successive replays of a 3.3 ms graph (200 decode steps at B=16, T=16) ran 18.7,
+    17.0, 16.6 and then 16.3 µs per step, and of a 2 ms graph of B=16, T=256 verifies 119 down to
+    99 µs per call; a single warm replay left the timed one on a partly ramped GPU."""
     import torch
-    g.replay()  # warm replay
-    torch.cuda.synchronize()
     e0 = torch.cuda.Event(enable_timing=True)
     e1 = torch.cuda.Event(enable_timing=True)
+    spent, reps = 0.0, 0
+    while reps < 1 or (spent < settle_ms and reps < 1000):
+        e0.record()
+        g.replay()
+        e1.record()
+        torch.cuda.synchronize()
+        spent += e0.elapsed_time(e1)
+        reps += 1
     e0.record()
     g.replay()
     e1.record()
@@ -1242,7 +1271,9 @@ def measure(key, args, baselines=True):
                    "step": ("commit of the previous round's accepted path (a random root-to-leaf "
                             "path) into the carried state, then verify of the tree from it "
                             "(canopy_commit_verify, %s)" % ("one launch" if one else "two launches")),
-                   "launch": "eager" if args.eager else "hip graph of all timed steps",
+                   "launch": "eager" if args.eager else (
+                       "hip graph of all timed steps, replayed untimed for at least %g ms of GPU "
+                       "time before the one timed replay" % SETTLE_MS),
                    "copy_probe_bytes": args.copy_probe},
         "step_us": round(us_step, 3),
         "nodes_per_s": round(nodes / (us_step * 1e-6), 1),

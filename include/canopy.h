@@ -182,7 +182,11 @@ canopy_status canopy_tree_prep(const int32_t *parent, const int32_t *tree_len, c
  *               (CANOPY_ERR_UNSUPPORTED here).
  *   waves       workgroup width, 1, 2, 4, 8 or 16, or 0 to let the library choose from B, H
  *               and T.
- *               T <= 16 (AUTO, NEUMANN): waves per workgroup, each owning 16 value columns.
+ *               T <= 16 (AUTO, NEUMANN): 1, 2, 4 or 8 waves per workgroup, each owning 16
+ *               value columns; 16 single-wave workgroups each owning 32 value columns (two
+ *               16-column tiles). Waves 0 takes 16 with bf16 inputs when B*HV*8 single-tile
+ *               waves would fill one pass of the GPU or more (3 per SIMD in
+ *               canopy_commit_verify's one launch, 4 for the verify alone), else 1.
  *               17 <= T <= 64 (AUTO, FWDSUB, NEUMANN): 16-column tiles per workgroup, whose
  *               waves each own 16 nodes (8 is taken as 4).
  *               T > 64, bf16, AUTO or FWDSUB: 1 or 2 picks the wave-per-sub-block kernel with

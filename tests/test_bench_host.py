@@ -63,8 +63,14 @@ def test_one_launch_step_follows_the_dispatch(T, solver, heads, waves, one):
 
 
 def test_fused_kernel_name():
-    assert bench.fused_kernel_name(16, "bf16") == "canopy::verify_small_kernel<true, 1, true>"
-    assert bench.fused_kernel_name(7, "fp32", 2, 8) == "canopy::verify_small_kernel<false, 8, true>"
+    assert bench.fused_kernel_name(16, "bf16") == "canopy::verify_small_kernel<true, 1, true, 1>"
+    assert bench.fused_kernel_name(7, "fp32", 2, 8) == "canopy::verify_small_kernel<false, 8, true, 1>"
+    # single-tile waves filling a pass (3 per SIMD on 1024 SIMDs) or more: two column tiles
+    assert bench.fused_kernel_name(16, "bf16", 376) == "canopy::verify_small_kernel<true, 1, true, 1>"
+    assert bench.fused_kernel_name(16, "bf16", 384) == "canopy::verify_small_kernel<true, 1, true, 2>"
+    assert bench.fused_kernel_name(16, "bf16", 512) == "canopy::verify_small_kernel<true, 1, true, 2>"
+    assert bench.fused_kernel_name(16, "fp32", 512) == "canopy::verify_small_kernel<false, 1, true, 1>"
+    assert bench.fused_kernel_name(16, "bf16", 32, 16) == "canopy::verify_small_kernel<true, 1, true, 2>"
     assert bench.fused_kernel_name(64, "bf16", 32) == "canopy::verify_mid_kernel<true, 4, 1, true>"
     assert bench.fused_kernel_name(64, "bf16", 64) == "canopy::verify_mid_kernel<true, 4, 2, true>"
     assert bench.fused_kernel_name(64, "bf16", 128) == "canopy::verify_mid_kernel<true, 4, 2, true>"

@@ -95,8 +95,11 @@ canopy_status canopy_tree_verify(const void *q, const void *k, const void *v,
         return CANOPY_ERR_UNSUPPORTED;
     if (solver == CANOPY_SOLVE_LEVELSYNC && (in_dtype != CANOPY_BF16 || (waves != 0 && waves != 8)))
         return CANOPY_ERR_UNSUPPORTED;
-    if (waves == 16 && (in_dtype != CANOPY_BF16 || T <= 64 || !dual_fits(H, HV, T) ||
-                        (solver != CANOPY_SOLVE_AUTO && solver != CANOPY_SOLVE_FWDSUB)))
+    // 16: two column tiles per wave for trees of at most 16 nodes (AUTO, NEUMANN); the
+    // two-per-CU blocked kernel for bf16 trees of 65 to 256 nodes (AUTO, FWDSUB).
+    if (waves == 16 && !(T <= 16 && (solver == CANOPY_SOLVE_AUTO || solver == CANOPY_SOLVE_NEUMANN)) &&
+        (in_dtype != CANOPY_BF16 || T <= 64 || !dual_fits(H, HV, T) ||
+         (solver != CANOPY_SOLVE_AUTO && solver != CANOPY_SOLVE_FWDSUB)))
         return CANOPY_ERR_UNSUPPORTED;
     VerifyArgs a{};
     a.q = q; a.k = k; a.v = v;
@@ -233,8 +236,11 @@ canopy_status canopy_commit_verify(const float *S0, const void *k_prev, const fl
         return CANOPY_ERR_UNSUPPORTED;
     if (solver == CANOPY_SOLVE_LEVELSYNC && (in_dtype != CANOPY_BF16 || (waves != 0 && waves != 8)))
         return CANOPY_ERR_UNSUPPORTED;
-    if (waves == 16 && (in_dtype != CANOPY_BF16 || T <= 64 || !dual_fits(H, HV, T) ||
-                        (solver != CANOPY_SOLVE_AUTO && solver != CANOPY_SOLVE_FWDSUB)))
+    // 16: two column tiles per wave for trees of at most 16 nodes (AUTO, NEUMANN); the
+    // two-per-CU blocked kernel for bf16 trees of 65 to 256 nodes (AUTO, FWDSUB).
+    if (waves == 16 && !(T <= 16 && (solver == CANOPY_SOLVE_AUTO || solver == CANOPY_SOLVE_NEUMANN)) &&
+        (in_dtype != CANOPY_BF16 || T <= 64 || !dual_fits(H, HV, T) ||
+         (solver != CANOPY_SOLVE_AUTO && solver != CANOPY_SOLVE_FWDSUB)))
         return CANOPY_ERR_UNSUPPORTED;
     // After a previous tree of at most 64 nodes (one path position per lane): one launch, the
     // committed state kept in registers for the verify, for new trees of at most 16 nodes (AUTO,

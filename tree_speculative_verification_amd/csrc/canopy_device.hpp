@@ -41,7 +41,9 @@ __device__ __forceinline__ void lds_barrier() {
 // Streaming store (the nt bit: the line is not kept in the caches for reuse), for outputs that
 // nothing on the path reads again: the read-out O and the committed state. Measured on MI355X,
 // it shortens verify by 4% at B = 16, T = 64 and T = 256 and the commit by 6%; U, which the
-// commit reads back, stays an ordinary store (streaming it cost 10% with a cold cache).
+// commit reads back, stays an ordinary store (streaming it cost 10% with a cold cache), and so
+// does the state of the one-launch step for trees of at most 16 nodes, whose lanes write it in
+// 64-byte row segments (streaming was slower there, warm and cold).
 __device__ __forceinline__ void store_nt(float *p, float v) { __builtin_nontemporal_store(v, p); }
 
 __device__ __forceinline__ int wave_max(int x) {
