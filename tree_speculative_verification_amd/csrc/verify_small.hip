@@ -354,7 +354,13 @@ __global__ __launch_bounds__(64 * NWV) void verify_small_kernel(VerifyArgs a, Pr
             if (i < Tb) {
                 const size_t o = base + static_cast<size_t>(i) * rs + col0 + 16 * ct + lr;
                 a.U[o] = bad ? qnan : u[ct][e];
-                store_nt(a.O + o, bad ? qnan : oc[e]);
+                // O streams past the caches for the verify alone (4% faster at B = 16); the
+                // one-launch step stores it like the state (equal with one layer, 1.3% faster
+                // with 16 layers run in turn)
+                if constexpr (FUSE)
+                    a.O[o] = bad ? qnan : oc[e];
+                else
+                    store_nt(a.O + o, bad ? qnan : oc[e]);
             }
         }
     }
