@@ -764,6 +764,28 @@ def protocol_summary(trace_csv, warmup=25):
     return {ph: {k: _stats(v) for k, v in ks.items()} for ph, ks in out.items()}
 
 
+def trace_summary(trace_csv):
+    """Device time per dispatch of each library kernel in a rocprofv3 kernel trace (end - start,
+    µs): calls, average, median and minimum, keyed by the kernel's name with its template
+    arguments (the profiles' kernel-trace tables)."""
+    acc = {}
+    with open(trace_csv) as fh:
+        for r in csv.DictReader(fh):
+            name = r["Kernel_Name"]
+            if "canopy::" not in name:
+                continue
+            short = name.split("canopy::", 1)[1].split("(")[0]
+            acc.setdefault(short, []).append((int(r["End_Timestamp"]) - int(r["Start_Timestamp"])) / 1000.0)
+    out = {}
+    for k, v in acc.items():
+        v = sorted(v)
+        n = len(v)
+        med = v[n // 2] if n % 2 else 0.5 * (v[n // 2 - 1] + v[n // 2])
+        out[k] = {"calls": n, "average_us": round(sum(v) / n, 3), "median_us": round(med, 3),
+                  "min_us": round(v[0], 3)}
+    return out
+
+
 def run_peaks(args):
     """Measured references for the roofline fractions: HBM bandwidth of a large device copy
     (read + write) and of a large reduction (read), dense MFMA throughput of a large bf16 and
@@ -994,6 +1016,8 @@ def main(argv=None):
     ap.add_argument("--protocol-workloads", nargs="+", default=None, choices=sorted(WORKLOADS))
     ap.add_argument("--peaks", action="store_true",
                     help="measured HBM, GEMM and launch references for the roofline fractions")
+    ap.add_argument("--trace-summary", default="", metavar="CSV",
+                    help="per-kernel device time per dispatch from a rocprofv3 kernel trace CSV")
     ap.add_argument("--protocol-summary", default="", metavar="CSV",
                     help="device-time distributions from the rocprofv3 kernel trace CSV of a "
                          "--protocol run (no GPU work)")
@@ -1013,6 +1037,9 @@ def main(argv=None):
         return pmc_summary(args.pmc_summary, args.out or TRAFFIC_FILE)
     if args.protocol_summary:
         print(json.dumps(protocol_summary(args.protocol_summary)), flush=True)
+        return 0
+    if args.trace_summary:
+        print(json.dumps(trace_summary(args.trace_summary), indent=1, sort_keys=True), flush=True)
         return 0
 
     if args.gpus != 1 or int(os.environ.get("WORLD_SIZE", "1")) != 1:

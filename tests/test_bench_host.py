@@ -178,3 +178,23 @@ def test_method_flops_from_ancestor_pairs():
     assert 9.0e9 < f < 9.6e9, f
     assert f < bench.verify_flops(16, 32, 256) / 2.5
     assert bench.commit_flops(32, 3) == 32 * 2 * 128 * 128 * 3
+
+
+def test_trace_summary_per_kernel(tmp_path):
+    rows = [("void at::native::fill<float>(x)", 0, 1000),
+            ("void canopy::verify_small_kernel<true, 1, true, 2>(canopy::VerifyArgs, canopy::PrevCommitArgs)", 0, 3000),
+            ("void canopy::verify_small_kernel<true, 1, true, 2>(canopy::VerifyArgs, canopy::PrevCommitArgs)", 5000, 9000),
+            ("void canopy::verify_small_kernel<true, 1, true, 2>(canopy::VerifyArgs, canopy::PrevCommitArgs)", 10000, 12500),
+            ("void canopy::commit_kernel<true, 4>(canopy::CommitArgs)", 20000, 21500)]
+    path = tmp_path / "trace.csv"
+    with open(path, "w", newline="") as fh:
+        w = csv.DictWriter(fh, fieldnames=["Kernel_Name", "Start_Timestamp", "End_Timestamp"])
+        w.writeheader()
+        for n, a, b in rows:
+            w.writerow({"Kernel_Name": n, "Start_Timestamp": a, "End_Timestamp": b})
+    res = bench.trace_summary(str(path))
+    assert set(res) == {"verify_small_kernel<true, 1, true, 2>", "commit_kernel<true, 4>"}
+    v = res["verify_small_kernel<true, 1, true, 2>"]
+    assert v["calls"] == 3 and v["median_us"] == 3.0 and v["min_us"] == 2.5
+    assert v["average_us"] == pytest.approx(3.167, abs=1e-3)
+    assert res["commit_kernel<true, 4>"]["median_us"] == 1.5
