@@ -209,15 +209,23 @@ def verify_kernel_name(T, solver, heads=0, waves=0, dtype="bf16"):
     return "verify_kernel"
 
 
+def _code_only(text):
+    """C++ source with comments removed and whitespace runs collapsed (string literals, which the
+    kernels do not use, are not special-cased)."""
+    text = re.sub(r"/\*.*?\*/", " ", text, flags=re.S)
+    text = re.sub(r"//[^\n]*", " ", text)
+    return " ".join(text.split())
+
+
 def kernel_digest():
-    """Digest of the device code (every HIP source and header but the host-side C ABI file):
-    identifies the kernels a profile was taken on."""
+    """Digest of the device code (every HIP source and header but the host-side C ABI file, with
+    comments and whitespace left out): identifies the kernels a profile was taken on."""
     h = hashlib.sha256()
     for f in sorted(os.listdir(KERNEL_SOURCE_DIR)):
         if f.endswith((".hip", ".hpp")) and f != "api.hip":
             h.update(f.encode())
-            with open(os.path.join(KERNEL_SOURCE_DIR, f), "rb") as fh:
-                h.update(fh.read())
+            with open(os.path.join(KERNEL_SOURCE_DIR, f), encoding="utf-8") as fh:
+                h.update(_code_only(fh.read()).encode())
     return h.hexdigest()[:16]
 
 

@@ -127,6 +127,16 @@ def test_digest_follows_the_kernel_sources(tmp_path, monkeypatch):
     assert bench.kernel_digest() != d0
 
 
+def test_digest_ignores_comments_and_whitespace(tmp_path, monkeypatch):
+    monkeypatch.setattr(bench, "KERNEL_SOURCE_DIR", str(tmp_path))
+    (tmp_path / "k.hip").write_text("int f(int x) { return x + 1; }\n")
+    d0 = bench.kernel_digest()
+    (tmp_path / "k.hip").write_text("// what f does\nint f(int x) {\n    return x + 1;  /* one */\n}\n")
+    assert bench.kernel_digest() == d0
+    (tmp_path / "k.hip").write_text("int f(int x) { return x + 2; }\n")
+    assert bench.kernel_digest() != d0
+
+
 def test_protocol_summary_splits_warm_and_cold(tmp_path):
     fill = "void at::native::vectorized_elementwise_kernel<4, at::native::FillFunctor<float>, x>"
     other_fill = "void at::native::vectorized_elementwise_kernel<4, at::native::FillFunctor<long>, x>"

@@ -1,5 +1,5 @@
-// Tree verification for trees of at most 16 nodes: one wave per (sequence, head, 16 value
-// columns), everything in registers, no LDS and no barrier. The same closed form as the
+// Tree verification for trees of at most 16 nodes: one wave per (sequence, head, NCT 16-column
+// tiles of the value columns), everything in registers, no LDS and no barrier. The same closed form as the
 // general kernel (the canopy project page, "The tree closed form"), specialised to a single
 // 16-node tile:
 //   prep   pointer jumping over lanes (lane i = node i) with shuffles: ancestor mask, depth,
@@ -13,9 +13,11 @@
 // The Gram tiles come out with row r, columns 4g..4g+3 in lane (g, r), and the node-by-column
 // tiles (R, the series terms, U) with rows 4g..4g+3 of column r in lane (g, r): exactly the A
 // and B placements of a 16-long MFMA reduction, so the series and the read-out move no data
-// between lanes. A workgroup holds NWV waves, each on its own 16 value columns of one head.
+// between lanes. A workgroup holds NWV waves, each on its own NCT tiles of one head; with two
+// tiles a wave computes the tree prep, the key and query fragments, the Gram tile and the path
+// operands once for both, and the tiles' series chains interleave.
 //
-// The fused variant first commits the previous tree's accepted path into the wave's 128 x 16
+// The fused variant first commits the previous tree's accepted path into the wave's 128 x 16 NCT
 // slice of the state ("Design decisions / What the commit kernel stores"): S = P_a S0 +
 // sum_t w_t k_t u_t^T as fp32 MFMA products, four path positions per instruction, the key
 // rows permuted so that the result lands in the B-operand placement of S0 that the
@@ -107,9 +109,9 @@ __global__ __launch_bounds__(64 * NWV) void verify_small_kernel(VerifyArgs a, Pr
         qf[ks] = Op::template load_frag<In>(a.q, erow + 32 * ks, true);
     }
     // s0t[ct][t][ks] = S0[32ks + 8lg + t][col0 + 16ct + lr]: row t of the B fragment of reduction
-    // slice ks,
-    // grouped by t so that each f32x4 is also the accumulator of the fused commit's rank update
-    // for its 16 x 16 tile t (the key rows of that update are permuted to land there)
+    // slice ks for column tile ct, grouped by t so that each f32x4 is also the accumulator of the
+    // fused commit's rank update for its 16 x 16 tile t (the key rows of that update are permuted
+    // to land there)
     f32x4 s0t[NCT][8];  // per column tile ct: columns col0 + 16 ct + lr
 #pragma unroll
     for (int ct = 0; ct < NCT; ++ct) {
