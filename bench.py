@@ -845,6 +845,20 @@ def run_peaks(args):
     return 0
 
 
+def crossover_cpu_baseline(B, H, T, W, L, budget_s):
+    """The oracle for one crossover round of a cell: one layer of the cell's shape (seeded
+    synthetic inputs on its level tree) timed by cpu_baseline, scaled to the round's L layers
+    (the layers are independent and cost the same) and to 100 rounds."""
+    import synth
+    inp = synth.make_inputs(B, H, T, dtype="bf16", seed=1000 * B + T * 17 + W, parents=synth.level_tree(T, W))
+    cb = cpu_baseline(inp, budget_s)
+    per_layer = cb["value"]
+    return dict(value=round(per_layer * L, 1), unit=f"us per round ({L} layers, verify + commit)",
+                per_layer_us=round(per_layer, 1), extrapolated_100_rounds_s=round(per_layer * L * 100 / 1e6, 2),
+                cores=cb["cores"], kind="oracle",
+                sample=f"one layer timed ({cb['sample']}), scaled to {L} layers and to 100 rounds")
+
+
 def crossover_cells():
     """Depth x width level trees: root, then levels of W nodes (the last one partial);
     W = 1 is a chain; shapes that coincide (stars) are kept once; depth 1..64."""
@@ -981,6 +995,12 @@ def run_crossover(args):
                    "speedup_parallel_over_hybrid": round(us_hyb / us_par, 3),
                    "speedup_hybrid_over_serial": round(us_ser / us_hyb, 3),
                    "final_state_rel_err_parallel_vs_hybrid": err_h}
+            smallest = B == min(args.batches) and (W, T) == crossover_cells()[0][:2]
+            largest = B == max(args.batches) and (W, T) == (16, 256)
+            if not args.no_cpu and (smallest or largest):
+                cb = crossover_cpu_baseline(B, H, T, W, L, args.cpu_budget)
+                cb["speedup_parallel_over_oracle"] = round(cb["value"] / us_par, 1)
+                rec["cpu_baseline"] = cb
             line = json.dumps(rec)
             print(line, flush=True)
             if out:
