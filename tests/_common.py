@@ -48,3 +48,23 @@ def per_head_rel_err(x, y):
 def state_rel_err(x, y):
     """Relative error per (batch, head) slice of a [B,H,dk,dv] state."""
     return max_rel_err(x, y, axes=(2, 3))
+
+
+def fro_rel_err(x, y):
+    """Relative Frobenius error ||x - y||_F / ||y||_F over the whole tensor."""
+    x = np.asarray(x, dtype=np.float64)
+    y = np.asarray(y, dtype=np.float64)
+    den = np.linalg.norm(y.ravel())
+    num = np.linalg.norm((x - y).ravel())
+    return float(num / den) if den > 0 else float(num)
+
+
+def elem_rel_err(x, y, floor=1e-3):
+    """Worst element-wise relative error |x - y| / |y| over the entries with |y| above
+    ``floor`` times max|y| (smaller entries carry no relative precision)."""
+    x = np.asarray(x, dtype=np.float64)
+    y = np.asarray(y, dtype=np.float64)
+    keep = np.abs(y) > floor * np.max(np.abs(y))
+    if not keep.any():
+        return 0.0
+    return float(np.max(np.abs(x[keep] - y[keep]) / np.abs(y[keep])))

@@ -1,10 +1,13 @@
 """Helpers for GPU tests: upload synth inputs, run the oracle on the same values, compare."""
 from __future__ import annotations
 
+import json
+import os
+
 import numpy as np
 
 import oracle
-from _common import per_head_rel_err, state_rel_err
+from _common import elem_rel_err, fro_rel_err, per_head_rel_err, state_rel_err
 
 TOL = {"bf16": 2e-3, "fp32": 1e-5}
 
@@ -74,3 +77,19 @@ def assert_ell(ell_gpu, ell_ref):
     bound = 1e-5 * np.maximum(1.0, np.abs(ell_ref))
     bad = np.abs(ell_gpu - ell_ref) > bound
     assert not bad.any(), f"ell differs at {np.argwhere(bad)[:5]}"
+
+
+def report_metrics(config, name, x, y, state=False):
+    """The parity metrics of one output against the oracle: the gated one (per-(batch, head)
+    infinity-norm relative error), the relative Frobenius error and the worst element-wise
+    relative error over entries above 1e-3 of the largest. Printed, and appended as a JSON line
+    to the file named by CANOPY_PARITY_METRICS when that is set."""
+    rec = {"config": config, "output": name,
+           "inf_per_head": (state_rel_err if state else per_head_rel_err)(x, y),
+           "frobenius": fro_rel_err(x, y), "elementwise_above_1e-3": elem_rel_err(x, y)}
+    print("[metrics]", json.dumps(rec), flush=True)
+    path = os.environ.get("CANOPY_PARITY_METRICS")
+    if path:
+        with open(path, "a") as fh:
+            fh.write(json.dumps(rec) + "\n")
+    return rec

@@ -13,7 +13,7 @@ import pytest
 import oracle
 import synth
 from gpu_util import (TOL, assert_close_heads, assert_close_state, assert_ell, oracle_commit,
-                      run_oracle, slice_inputs, to_device)
+                      report_metrics, run_oracle, slice_inputs, to_device)
 
 pytestmark = pytest.mark.gpu
 
@@ -73,6 +73,9 @@ def test_config_binary7_fp32(canopy):
     assert_close_state("S_new", Sn.cpu().numpy(), ref["S_accept"], TOL["fp32"])
     S_or, _ = oracle_commit(inp)
     assert_close_state("S_new vs path recurrence", Sn.cpu().numpy(), S_or, TOL["fp32"])
+    report_metrics("C1", "O", O.cpu().numpy(), ref["O"])
+    report_metrics("C1", "U", U.cpu().numpy(), ref["U"])
+    report_metrics("C1", "S_new", Sn.cpu().numpy(), S_or, state=True)
 
 
 @pytest.mark.parametrize("solver", ["fwdsub", "neumann", "level", "auto"])
@@ -95,6 +98,10 @@ def test_config_topk16_bf16(canopy, solver):
     S_or, st_or = oracle_commit(inp)
     assert np.array_equal(pst.cpu().numpy(), st_or)
     assert_close_state("S_new", Sn.cpu().numpy(), S_or, TOL["bf16"])
+    if solver == "auto":
+        report_metrics("C2", "O", O, ref["O"])
+        report_metrics("C2", "U", U, ref["U"])
+        report_metrics("C2", "S_new", Sn.cpu().numpy(), S_or, state=True)
 
 
 EDGE_T = [1, 2, 7, 15, 16, 17, 31, 32, 33, 63, 64, 65, 127, 128, 129, 191, 192, 193, 255, 256]
@@ -140,6 +147,8 @@ def test_config_skewed64_batch_sweep(canopy, B):
         assert_close_heads("U", U, ref["U"], TOL["bf16"])
         assert_ell(ell, ref["ell"])
         _check_structure(inp, mask, depth, st)
+    report_metrics(f"C3 B={B}", "O", O, ref["O"])
+    report_metrics(f"C3 B={B}", "U", U, ref["U"])
     _say("skewed64 serial B", B)
     O, U, snap, st = canopy.serial_verify(d["q"], d["k"], d["v"], d["alpha"], d["beta"], d["S0"], d["parent"])
     torch.cuda.synchronize()
@@ -180,6 +189,9 @@ def test_config_random256_b16(canopy):
     _say("random256 B16 oracle commit over the full grid: %.2f s" % (time.perf_counter() - t0))
     assert np.array_equal(pst.cpu().numpy(), st_or)
     assert_close_state("S_new", Sn.cpu().numpy(), S_or, TOL["bf16"])
+    report_metrics("C4", "O", O, ref["O"])
+    report_metrics("C4", "U", U, ref["U"])
+    report_metrics("C4", "S_new", Sn.cpu().numpy(), S_or, state=True)
 
 
 def test_serial_snapshots_match_oracle_states(canopy):

@@ -9,7 +9,7 @@ import pytest
 
 import oracle
 import synth
-from _common import max_rel_err, read_golden, per_head_rel_err, state_rel_err
+from _common import elem_rel_err, fro_rel_err, max_rel_err, read_golden, per_head_rel_err, state_rel_err
 import closed_form as cf
 
 
@@ -163,6 +163,34 @@ def test_chain_equals_product_form():
         S = a[t] * (I - b[t] * np.outer(k[t], k[t])) @ S + b[t] * np.outer(k[t], v[t])
         np.testing.assert_allclose(r["S_all"][0, t, 0], S, rtol=0, atol=1e-12)
         np.testing.assert_allclose(r["O"][0, t, 0], S.T @ q[t], rtol=0, atol=1e-12)
+
+
+def test_rounds_equal_concatenated_recurrence():
+    """Rounds of verify + commit, each on its own tree from the state the previous round
+    committed, equal one sequential recurrence over the rounds' accepted tokens in order: the
+    final state, and every accepted node's output (the token loop in product form, as above)."""
+    rng = np.random.default_rng(17)
+    S_chain = 0.1 * rng.standard_normal((128, 128))
+    S_rounds = S_chain.copy()
+    I = np.eye(128)
+    trees = [synth.make_tree("random", 12, rng), synth.topk_tree((3, 4)), synth.chain(5),
+             synth.make_tree("skewed", 20, rng)]
+    for r, par in enumerate(trees):
+        T = len(par)
+        _, q, k, v, a, b, _ = _rand_head(rng, T, parent=par)
+        d = _one_head(par, q, k, v, a, b, S_rounds)
+        out = _run(d)
+        path = synth.random_leaf_path(par, rng)
+        plen = np.array([len(path)], np.int32)
+        pth = np.full((1, T), -1, np.int32)
+        pth[0, :len(path)] = path
+        S_new, st = oracle.commit(d["parent"], pth, plen, d["k"], d["v"], d["alpha"], d["beta"], d["S0"])
+        assert st.tolist() == [0]
+        for t in path:  # the round's accepted tokens, root first, through the plain loop
+            S_chain = a[t] * (I - b[t] * np.outer(k[t], k[t])) @ S_chain + b[t] * np.outer(k[t], v[t])
+            np.testing.assert_allclose(out["O"][0, t, 0], S_chain.T @ q[t], rtol=0, atol=1e-11)
+        S_rounds = S_new[0, 0]
+        np.testing.assert_allclose(S_rounds, S_chain, rtol=0, atol=1e-11)
 
 
 def test_beta_zero_decay_only():
@@ -390,6 +418,12 @@ def test_error_metric_self_check():
     assert per_head_rel_err(x, y) == 1.0
     assert state_rel_err(np.ones((1, 1, 2, 2)), np.ones((1, 1, 2, 2))) == 0.0
     assert max_rel_err([1.0, 2.0], [1.0, 4.0]) == 0.5
+    y = np.array([3.0, -4.0, 1e-6])
+    assert fro_rel_err(1.001 * y, y) == pytest.approx(1e-3)
+    assert fro_rel_err(np.array([3.0, 0.0, 0.0]), np.array([3.0, 4.0, 0.0])) == pytest.approx(0.8)
+    # the tiny third entry is below 1e-3 of the largest and is left out of the element-wise error
+    assert elem_rel_err(np.array([3.003, -4.0, 5e-6]), y) == pytest.approx(1e-3)
+    assert elem_rel_err(np.array([3.0, -4.4, 1e-6]), y) == pytest.approx(0.1)
 
 
 # --------------------------------------------------------------------------- grouped heads, ragged
